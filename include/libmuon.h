@@ -1,0 +1,244 @@
+/*
+ * libmuon — the Muon / Aurora-Muon matrix-optimizer step on AMD Instinct
+ * MI355X (gfx950), as a C-ABI shared library.
+ *
+ * The operations follow two web pages:
+ *   [Aurora page]  "modded-nanogpt Track 3 优化实录：Aurora 行均衡 polar +
+ *                  Contra-Muon + u/w-floor 将 3.28 验证损失推进到 3175 步"
+ *                  (www.xxmr.cn/news/295280);
+ *   [Track-1 page] "Modded-NanoGPT 纪录解读：U-Net 式跳跃连接与学习率翻倍如何将
+ *                  124M GPT 训练压到 7.23 分钟" (www.trdm.cn/news/788905).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Matrices are row-major, in device memory the caller owns. A descriptor
+ *    names one matrix: element (i, j) lives at ptr + i * ld + j (elements).
+ *    ld >= cols. ptr must be aligned to the element size. A matrix with
+ *    rows == 0 or cols == 0 is skipped (its ptr may be NULL).
+ *  - Batches: every call takes n descriptors of mixed shapes and types; each
+ *    matrix is processed on its own (its own norms, preconditioner and power
+ *    iteration) and the batch is fused into shared kernel launches.
+ *  - Limits: rows, cols <= 65536, min(rows, cols) <= 16384 and
+ *    rows * cols < 2^31 per matrix.
+ *  - Precision: a matrix whose input is MUON_BF16 runs Newton-Schulz on bf16
+ *    matrix cores with fp32 accumulation; a MUON_F32 input runs it with fp32
+ *    matrix-core arithmetic throughout. Norms, the preconditioner, the power
+ *    iteration and every scalar are fp32.
+ *  - Errors: no exception crosses the ABI. Calls return a muon_status; a
+ *    negative value is an error. All arguments are validated on the host
+ *    before anything is enqueued: on any error nothing is enqueued and no
+ *    caller buffer is touched. muon_last_error() gives a message.
+ *  - Asynchrony: compute calls enqueue on the handle's stream and return.
+ *    Inputs must stay valid and unmodified until that stream reaches the
+ *    work. Device faults surface as MUON_ERR_HIP on a later call or on the
+ *    caller's synchronisation.
+ *  - Determinism: reductions run in a fixed order with no floating-point
+ *    atomics; two calls on the same inputs give bitwise-equal results.
+ *  - Threads: a handle is not thread-safe; use one handle per thread.
+ */
+#ifndef LIBMUON_H
+#define LIBMUON_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+  MUON_F32 = 0,
+  MUON_BF16 = 1
+} muon_dtype;
+
+/* Status codes. */
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = -1,      /* NULL pointer, bad count, bad config value */
+  MUON_ERR_UNSUPPORTED_DTYPE = -2,/* dtype not in muon_dtype, or momentum not F32 */
+  MUON_ERR_SHAPE_MISMATCH = -3,   /* grad/momentum/weight/out shapes differ, ld < cols, limits */
+  MUON_ERR_ALLOC = -4,            /* device workspace allocation failed */
+  MUON_ERR_HIP = -5,              /* a HIP runtime call failed */
+  MUON_ERR_NO_DEVICE = -6         /* no usable gfx950 device */
+} muon_status_code;
+typedef int muon_status;
+
+/* One row-major device matrix (see conventions above). */
+typedef struct {
+  void*   ptr;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;
+  int32_t dtype; /* muon_dtype */
+} muon_matrix;
+
+/*
+ * Step hyper-parameters. muon_config_default() fills the values the Aurora
+ * page locks (§"完整的超参配置表" and the signature defaults in §"源码实现" and
+ * §"组合优化栈"): ns_steps 12, (ns_a, ns_b, ns_c) = (2, -1.5, 0.5),
+ * ns_eps 1e-7, pp_iterations 2, pp_beta 0.5, pp_eps 1e-7, mu 0.95,
+ * nesterov 1, power_steps 5, contra 0.4, target_uw 0.35, lr 0.0375, flags 0.
+ *
+ *   ns_steps, ns_a/b/c  Newton-Schulz iteration count and polynomial
+ *                       X <- a X + (b A + c A^2) X, A = X X^T (1..64 steps).
+ *   ns_eps              added to the Frobenius norm before normalising.
+ *   pp_iterations       Aurora passes (0 = plain NS, no preconditioner; 1 =
+ *                       row-normalise then polar; 0..8).
+ *   pp_beta, pp_eps     damping exponent of the D update; clamp of row norms
+ *                       (pp_eps) and squared row norms (pp_eps^2).
+ *   mu, nesterov        momentum coefficient in [0, 1]; Nesterov blend flag.
+ *   power_steps         power iterations for the operator-norm estimate (1..64).
+ *   contra              Contra-Muon coefficient; the step subtracts contra/2
+ *                       times the unit-operator-norm direction (0 = off).
+ *   target_uw           u/w-floor target ratio (0 = off).
+ *   lr                  learning rate of the parameter add.
+ *   flags               reserved, must be 0.
+ */
+typedef struct {
+  int32_t  ns_steps;
+  float    ns_a, ns_b, ns_c, ns_eps;
+  int32_t  pp_iterations;
+  float    pp_beta, pp_eps;
+  float    mu;
+  int32_t  nesterov;
+  int32_t  power_steps;
+  float    contra;
+  float    target_uw;
+  float    lr;
+  uint32_t flags;
+} muon_config;
+
+/* Per-kernel-class timing gathered when profiling is on (see muon_profile_*). */
+typedef struct {
+  int64_t gemm_launches;      /* Newton-Schulz matrix-core launches */
+  double  gemm_ms;            /* summed event time of those launches */
+  double  gemm_counted_flop;  /* 4 s^2 L + 2 s^3 per iteration per matrix (s <= L) */
+  double  gemm_executed_flop; /* flops the tiles actually issue (symmetric tiles skipped) */
+  int64_t stream_launches;    /* bandwidth-bound launches (momentum, power, tail, ...) */
+  double  stream_ms;
+  double  stream_bytes;       /* algorithmic HBM bytes of those launches */
+} muon_profile;
+
+typedef struct muon_handle muon_handle;
+
+/* Fill *cfg with the page's locked values (listed above). cfg must not be NULL. */
+void muon_config_default(muon_config* cfg);
+
+/* Static text for a status code. Never NULL. */
+const char* muon_status_string(muon_status s);
+
+/* Library version string ("major.minor.patch"). */
+const char* muon_version(void);
+
+/*
+ * Create a handle bound to the current HIP device and to `stream`
+ * (a hipStream_t; NULL = the default stream). The stream is borrowed, not
+ * owned. The handle owns its device workspace and plan cache; both grow on
+ * demand and are freed by muon_destroy. Returns MUON_ERR_NO_DEVICE when no
+ * gfx950 device is current.
+ */
+muon_status muon_create(muon_handle** handle, void* stream);
+
+/* Free the handle and its workspace (waits for the stream first). NULL is a no-op. */
+muon_status muon_destroy(muon_handle* handle);
+
+/* Rebind the handle to another stream of the same device. */
+muon_status muon_set_stream(muon_handle* handle, void* stream);
+
+/* Message of the handle's last error ("" if none). Valid until the next call. */
+const char* muon_last_error(const muon_handle* handle);
+
+/*
+ * Host-only validation of a muon_update batch with the same rules as
+ * muon_update; enqueues nothing and needs no device. weight and update_out
+ * may be NULL. msg (may be NULL) receives a message of up to msg_len bytes.
+ */
+muon_status muon_check_update_args(int n, const muon_matrix* grad,
+                                   const muon_matrix* momentum,
+                                   const muon_matrix* weight,
+                                   const muon_matrix* update_out,
+                                   const muon_config* cfg,
+                                   char* msg, int msg_len);
+
+/* Host-only validation of an ns_polar / aurora_orthogonalize batch. */
+muon_status muon_check_polar_args(int n, const muon_matrix* in,
+                                  const muon_matrix* out,
+                                  const muon_config* cfg,
+                                  char* msg, int msg_len);
+
+/*
+ * Grow the workspace so that batches with these shapes and types run without
+ * any further device allocation (so a timed or captured region allocates
+ * nothing). Only rows, cols and dtype of `shapes` are read.
+ */
+muon_status muon_reserve(muon_handle* handle, int n, const muon_matrix* shapes);
+
+/*
+ * ns_polar — out_i = NS(in_i): the Newton-Schulz approximation of the polar
+ * factor, [Aurora page] §"源码实现" (the shared NS primitive): divide by the
+ * Frobenius norm + ns_eps, then ns_steps times X <- a X + (b A + c A^2) X with
+ * A = X X^T formed on the short side.
+ *   in[i]   input, any shape, F32 or BF16; read only.
+ *   out[i]  output, same shape as in[i], F32 or BF16 (rounded to nearest
+ *           even); may alias in[i] exactly.
+ *   cfg     ns_* fields are used; NULL = defaults.
+ */
+muon_status ns_polar(muon_handle* handle, int n, const muon_matrix* in,
+                     const muon_matrix* out, const muon_config* cfg);
+
+/*
+ * aurora_orthogonalize — leverage-equilibrated polar, [Aurora page]
+ * §"Aurora 是什么", §"Aurora 的迭代伪代码" and §"源码实现": square inputs get
+ * plain NS; otherwise, in the tall orientation (m > n), D = 1/max(row norm,
+ * pp_eps) and pp_iterations passes of U = NS(D * G), multiplying D by
+ * (n/m / max(row_sq, pp_eps^2))^pp_beta between passes. Wide inputs are
+ * handled as their transpose without materialising it.
+ *   in, out, cfg as for ns_polar (pp_* and ns_* fields used).
+ */
+muon_status aurora_orthogonalize(muon_handle* handle, int n,
+                                 const muon_matrix* in, const muon_matrix* out,
+                                 const muon_config* cfg);
+
+/*
+ * muon_update — one Aurora + Contra-Muon + u/w-floor optimizer step,
+ * [Aurora page] §"组合优化栈" (muon_update, the Contra-Muon and u/w-floor
+ * parts) and §"完整的超参配置表":
+ *   M <- M + (1 - mu)(G - M); X = G + mu (M - G) (X = M without Nesterov);
+ *   N = X / max(sigma, 1e-7), sigma from power_steps power iterations on
+ *   X^T X started from ones/sqrt(cols) (restart from the first largest-norm
+ *   column if that start is annihilated);
+ *   U = aurora_orthogonalize(X); V = U - (contra/2) N, rescaled to ||U||_F
+ *   (clamp 1e-10); V *= sqrt(max(1, rows/cols));
+ *   if ||V||/||W|| < target_uw (both clamped at 1e-8): V *= target_uw ||W||/||V||;
+ *   W <- W - lr V.
+ *   grad[i]       G, F32 or BF16; read only (unlike the page's in-place
+ *                 lerp, the blended update goes to workspace).
+ *   momentum[i]   M, F32, same shape; updated in place.
+ *   weight        NULL, or weight[i] = W (F32 or BF16, same shape) updated in
+ *                 place (bf16 rounded to nearest even); weight[i].ptr NULL
+ *                 means no weight (and no floor) for matrix i.
+ *   update_out    NULL, or update_out[i] receives V after the floor and
+ *                 before lr (F32 or BF16; ptr NULL = not wanted).
+ *   cfg           NULL = defaults.
+ * update_out must not overlap grad, momentum or weight.
+ */
+muon_status muon_update(muon_handle* handle, int n, const muon_matrix* grad,
+                        const muon_matrix* momentum, const muon_matrix* weight,
+                        const muon_matrix* update_out, const muon_config* cfg);
+
+/*
+ * Profiling of the library's own launches (for roofline reporting): when
+ * enabled, each kernel launch is bracketed by HIP events on the handle's
+ * stream and its time, its algorithmic flops or bytes are added to totals.
+ * muon_profile_read synchronises those events and returns the totals since
+ * the last reset.
+ */
+muon_status muon_profile_enable(muon_handle* handle, int enable);
+muon_status muon_profile_reset(muon_handle* handle);
+muon_status muon_profile_read(muon_handle* handle, muon_profile* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMUON_H */

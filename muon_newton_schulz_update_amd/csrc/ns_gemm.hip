@@ -1,0 +1,323 @@
+// Newton-Schulz matrix-core engine for gfx950.
+//
+// One iteration of the quintic Newton-Schulz map (Aurora record page,
+// www.xxmr.cn/news/295280, section 源码实现: X <- a X + (b A + c A^2) X with
+// A = X X^T, X normalised first) is three products, each a launch over every
+// matrix of a batch:
+//   GM_GRAM  A = X X^T                (s x s, K = L)  upper tiles only, mirrored
+//   GM_SQ    B = b A + c A A^T         (s x s, K = s)  upper tiles only, mirrored
+//   GM_BX    X' = a X + B X            (s x L, K = s)  writes X' and X'^T
+// X^T is kept beside X (written by the GM_BX epilogue), so all three read
+// both operands with the reduction index contiguous: C[m][n] = sum_k P[m][k] Q[n][k].
+//
+// Tiling: 256 x 256 output tile per 512-thread workgroup (8 waves in 4 x 2,
+// each wave 64 x 128 = 2 x 4 MFMA 32x32 blocks, accumulators in AGPRs; two
+// waves share a SIMD).
+// K advances 128 bytes per row per stage (64 bf16 or 32 fp32); two LDS stages
+// of 64 KB are filled by direct global->LDS 16-byte loads, so the next stage
+// streams in while the current one feeds the matrix cores. LDS rows are
+// XOR-swizzled in 16-byte chunks to spread the fragment reads over the banks.
+// bf16 runs v_mfma_f32_32x32x16_bf16 (fp32 accumulation); fp32 runs
+// v_mfma_f32_32x32x2f32 on the same tiles.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon_device.hpp"
+
+namespace muon {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+namespace {
+
+constexpr int kRowBytes = 128;                 // bytes of K per tile row per stage
+constexpr int kStageA = kTile * kRowBytes;     // 32 KB
+constexpr int kStageBytes = 2 * kStageA;       // A + B operand = 64 KB
+constexpr int kPitch = 132;                    // floats per staged epilogue row (128 + 4 spreads banks)
+constexpr int kSlabBytes = 32 * kPitch * 4;    // one wave's 32 x 128 staging slab
+constexpr int kLdsBytes = 8 * kSlabBytes > 2 * kStageBytes ? 8 * kSlabBytes : 2 * kStageBytes;
+
+// 16-byte chunk position of logical chunk c of tile row r.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Read one accumulator through an explicit AGPR->VGPR move. The "a"
+// constraint keeps the accumulators allocated in AGPRs for their whole live
+// range (plain uses in the epilogue would pull them into VGPRs).
+__device__ __forceinline__ float agpr_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+__device__ __forceinline__ void wait_vm_all() {
+  // s_waitcnt vmcnt(0): every direct-to-LDS load of this wave has landed.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  // round to nearest even (inputs here are finite)
+  unsigned int u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(unsigned short h) {
+  return __uint_as_float(((unsigned int)h) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> {
+  static constexpr int kPerChunk = 8;          // bf16 per 16-byte chunk
+  __device__ static void ld8(const void* p, size_t i, float v[8]) {
+    const u16x8_t q = *(const u16x8_t*)((const unsigned short*)p + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf2f(q[e]);
+  }
+  __device__ static void st8(void* p, size_t i, const float v[8]) {
+    u16x8_t q;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = f2bf(v[e]);
+    *(u16x8_t*)((unsigned short*)p + i) = q;
+  }
+};
+template <> struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  __device__ static void ld8(const void* p, size_t i, float v[8]) {
+    const f32x4_t a = *(const f32x4_t*)((const float*)p + i), b = *(const f32x4_t*)((const float*)p + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[e + 4] = b[e]; }
+  }
+  __device__ static void st8(void* p, size_t i, const float v[8]) {
+    *(f32x4_t*)((float*)p + i) = (f32x4_t){v[0], v[1], v[2], v[3]};
+    *(f32x4_t*)((float*)p + i + 4) = (f32x4_t){v[4], v[5], v[6], v[7]};
+  }
+};
+
+// Issue the direct-to-LDS loads of one stage: rows [0, 256) of P and of Q,
+// 128 bytes of K per row. Wave w, instruction i fills the 8 tile rows of group
+// g = 8 i + w; lane p fetches the logical chunk that belongs at LDS position p
+// of that 1 KB group. The swizzle of row g*8 + p/8 does not depend on i, so a
+// lane needs one 32-bit byte offset (`lane_off`); the per-instruction row step
+// (`row64`, 64 rows) and the K position (`kb`) are uniform.
+__device__ __forceinline__ void issue_stage(uint8_t* sm, const uint8_t* P, const uint8_t* Q,
+                                            int64_t row64, int64_t kb, uint32_t lane_off, int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = i * 8 + wave;
+    const int64_t u = kb + i * row64;
+    __builtin_amdgcn_global_load_lds((const void*)(P + u + lane_off), LDS_PTR(sm + g * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(Q + u + lane_off), LDS_PTR(sm + kStageA + g * 1024), 16, 0, 0);
+  }
+}
+
+// Fragment reads: lane l reads tile row (base + l%32), logical chunk
+// 2j + l/32. Bases are multiples of 32 rows, so the swizzle term depends on
+// l only and the per-block part is an immediate offset.
+template <typename T>
+__device__ __forceinline__ void compute_stage(const uint8_t* sm, f32x16_t (&acc)[2][4],
+                                              int lane, int wm, int wn) {
+  const int lr = lane & 31;
+  const int sw = (lr >> 1) & 7;
+  const uint8_t* pa_base = sm + (wm * 64 + lr) * kRowBytes;
+  const uint8_t* qa_base = sm + kStageA + (wn * 128 + lr) * kRowBytes;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ph = ((2 * j + (lane >> 5)) ^ sw) * 16;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t pa[2], qa[4];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) pa[mi] = *(const bf16x8_t*)(pa_base + mi * 32 * kRowBytes + ph);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) qa[ni] = *(const bf16x8_t*)(qa_base + ni * 32 * kRowBytes + ph);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[mi], qa[ni], acc[mi][ni], 0, 0, 0);
+    } else {
+      f32x4_t pa[2], qa[4];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) pa[mi] = *(const f32x4_t*)(pa_base + mi * 32 * kRowBytes + ph);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) qa[ni] = *(const f32x4_t*)(qa_base + ni * 32 * kRowBytes + ph);
+      // the 4 floats of a chunk are 4 consecutive k; lanes 0-31 and 32-63
+      // supply the two k slots of each 32x32x2 step from chunks 2j and 2j+1
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[mi][e], qa[ni][e], acc[mi][ni], 0, 0, 0);
+    }
+  }
+}
+
+}  // namespace
+
+// Launch geometry: grid.x = 8 * per_xcd blocks; the hardware deals
+// consecutive workgroups round-robin to the 8 XCDs, so block b runs on XCD
+// b % 8. Items are dealt to XCDs in runs of `group` consecutive items (which
+// share an operand panel), keeping each run inside one XCD's L2.
+template <typename T, int mode>
+__global__ __launch_bounds__(512, 1) void k_ns_gemm(const DevMat* __restrict__ mats,
+                                                    const TileItem* __restrict__ items,
+                                                    int n_items, int group, int cur,
+                                                    float ca, float cb, float cc) {
+  // two 64 KB operand stages; after the K loop the same memory stages the
+  // epilogue (8 waves x 32 x 132 floats = 132 KB)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  uint8_t* const sm0 = smem;
+  uint8_t* const sm1 = smem + kStageBytes;
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, j = b >> 3;
+  const int item_idx = ((j / group) * 8 + xcd) * group + (j % group);
+  if (item_idx >= n_items) return;
+  const TileItem it = items[item_idx];
+  const DevMat& M = mats[it.mat];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS bases stay in SGPRs
+  const int wm = wave >> 1, wn = wave & 1;
+  const int sp = M.s_pad, Lp = M.L_pad;
+
+  const T *P, *Q;
+  int ld, K;
+  if constexpr (mode == GM_GRAM) {
+    const T* x = (const T*)M.x[cur];
+    P = x + (size_t)it.tm * kTile * Lp;
+    Q = x + (size_t)it.tn * kTile * Lp;
+    ld = Lp; K = Lp;
+  } else if constexpr (mode == GM_SQ) {
+    const T* a = (const T*)M.a;
+    P = a + (size_t)it.tm * kTile * sp;
+    Q = a + (size_t)it.tn * kTile * sp;
+    ld = sp; K = sp;
+  } else {
+    P = (const T*)M.b + (size_t)it.tm * kTile * sp;
+    Q = (const T*)M.xt[cur] + (size_t)it.tn * kTile * sp;
+    ld = sp; K = sp;
+  }
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = (f32x16_t){};
+
+  constexpr int KE = kRowBytes / sizeof(T);   // K elements per stage
+  const int nk = K / KE;
+  const int64_t row64 = (int64_t)64 * ld * sizeof(T);
+  const int lrow = wave * 8 + (lane >> 3);
+  const uint32_t lane_off = (uint32_t)(((int64_t)lrow * ld + swz(lrow, lane & 7) * Elem<T>::kPerChunk) * sizeof(T));
+  const uint8_t* Pb = (const uint8_t*)P;
+  const uint8_t* Qb = (const uint8_t*)Q;
+  issue_stage(sm0, Pb, Qb, row64, 0, lane_off, wave);
+  // K is a multiple of 256 elements, so the stage count is even.
+  for (int kt = 0; kt < nk; kt += 2) {
+    wait_vm_all();
+    __syncthreads();
+    issue_stage(sm1, Pb, Qb, row64, (int64_t)(kt + 1) * kRowBytes, lane_off, wave);
+    compute_stage<T>(sm0, acc, lane, wm, wn);
+    wait_vm_all();
+    __syncthreads();
+    if (kt + 2 < nk) issue_stage(sm0, Pb, Qb, row64, (int64_t)(kt + 2) * kRowBytes, lane_off, wave);
+    compute_stage<T>(sm1, acc, lane, wm, wn);
+  }
+
+  // Epilogue. Accumulator register r of 32x32 block (mi, ni) holds
+  // row 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of that block. Each wave
+  // stages one 32 x 128 slab of its 64 x 128 tile at a time in the now idle
+  // LDS, then writes it row-major (8 consecutive columns per lane) and, for
+  // mirrored and X^T outputs, transposed (8 consecutive rows per lane).
+  const int row0 = it.tm * kTile + wm * 64;
+  const int col0 = it.tn * kTile + wn * 128;
+  void* out;
+  void* outT;
+  const void* add;
+  float add_coef, acc_coef;
+  int ldo, ldt;
+  if constexpr (mode == GM_GRAM) {
+    out = M.a; outT = M.a; add = nullptr; add_coef = 0.f; acc_coef = 1.f; ldo = sp; ldt = sp;
+  } else if constexpr (mode == GM_SQ) {
+    out = M.b; outT = M.b; add = M.a; add_coef = cb; acc_coef = cc; ldo = sp; ldt = sp;
+  } else {
+    out = M.x[cur ^ 1]; outT = M.xt[cur ^ 1]; add = M.x[cur]; add_coef = ca; acc_coef = 1.f;
+    ldo = Lp; ldt = sp;
+  }
+  const bool write_t = (mode == GM_BX) || (it.tm != it.tn);
+  float* buf = (float*)(smem + wave * kSlabBytes);
+  __syncthreads();   // every wave is done reading the operand stages
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        buf[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + ni * 32 + (lane & 31)] = agpr_read(acc[mi][ni][r]);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = k * 64 + lane;
+      const int rr = q >> 4, c8 = (q & 15) * 8;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = acc_coef * buf[rr * kPitch + c8 + e];
+      const size_t idx = (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8;
+      if constexpr (mode != GM_GRAM) {
+        float av[8];
+        Elem<T>::ld8(add, idx, av);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += add_coef * av[e];
+      }
+      Elem<T>::st8(out, idx, v);
+      if (write_t) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) buf[rr * kPitch + c8 + e] = v[e];
+      }
+    }
+    __syncthreads();
+    if (write_t) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int q = k * 64 + lane;
+        const int c1 = q >> 2, rc = (q & 3) * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = buf[(rc + e) * kPitch + c1];
+        Elem<T>::st8(outT, (size_t)(col0 + c1) * ldt + row0 + mi * 32 + rc, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launcher.
+// ---------------------------------------------------------------------------
+hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items,
+                          int mode, int cur, float ca, float cb, float cc, hipStream_t st) {
+  if (n_items <= 0) return hipSuccess;
+  const int group = 8;
+  const int per_xcd_groups = (n_items + 8 * group - 1) / (8 * group);
+  const dim3 grid(per_xcd_groups * group * 8), block(512);
+#define NS_LAUNCH(T, MODE) \
+  hipLaunchKernelGGL((k_ns_gemm<T, MODE>), grid, block, 0, st, mats, items, n_items, group, cur, ca, cb, cc)
+  if (ns_t == DT_BF16) {
+    if (mode == GM_GRAM) NS_LAUNCH(__bf16, GM_GRAM);
+    else if (mode == GM_SQ) NS_LAUNCH(__bf16, GM_SQ);
+    else NS_LAUNCH(__bf16, GM_BX);
+  } else {
+    if (mode == GM_GRAM) NS_LAUNCH(float, GM_GRAM);
+    else if (mode == GM_SQ) NS_LAUNCH(float, GM_SQ);
+    else NS_LAUNCH(float, GM_BX);
+  }
+#undef NS_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,177 @@
+// Host-only argument validation for the libmuon entry points. Pure C++ (no
+// HIP): it runs before anything is enqueued, so an invalid call touches no
+// device memory. Rules are the ones stated in include/libmuon.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/libmuon.h"
+#include "validate.hpp"
+
+namespace muon {
+
+namespace {
+
+int fail(char* msg, int len, int code, const char* fmt, ...) {
+  if (msg && len > 0) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, (size_t)len, fmt, ap);
+    va_end(ap);
+  }
+  return code;
+}
+
+bool finitef(float x) { return isfinite(x) != 0; }
+
+int elem_size(int32_t dt) { return dt == MUON_BF16 ? 2 : 4; }
+
+// One descriptor. `need_ptr`: a non-empty matrix must have a pointer.
+int check_matrix(const muon_matrix& m, const char* what, int i, char* msg, int len) {
+  if (m.dtype != MUON_F32 && m.dtype != MUON_BF16)
+    return fail(msg, len, MUON_ERR_UNSUPPORTED_DTYPE, "%s[%d]: dtype %d is not MUON_F32 or MUON_BF16", what, i,
+                (int)m.dtype);
+  if (m.rows < 0 || m.cols < 0)
+    return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: negative shape %lld x %lld", what, i,
+                (long long)m.rows, (long long)m.cols);
+  if (m.rows == 0 || m.cols == 0) return MUON_OK;
+  if (!m.ptr) return fail(msg, len, MUON_ERR_INVALID_ARG, "%s[%d]: NULL pointer for a non-empty matrix", what, i);
+  if (m.ld < m.cols)
+    return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: ld %lld < cols %lld", what, i, (long long)m.ld,
+                (long long)m.cols);
+  if (m.rows > kMaxDim || m.cols > kMaxDim)
+    return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: %lld x %lld exceeds the %d per-dimension limit", what, i,
+                (long long)m.rows, (long long)m.cols, kMaxDim);
+  const int64_t s = m.rows < m.cols ? m.rows : m.cols;
+  if (s > kMaxShort)
+    return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: short side %lld exceeds %d", what, i, (long long)s,
+                kMaxShort);
+  if (m.rows * m.cols >= kMaxElems)
+    return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: %lld elements exceed the 2^31 limit", what, i,
+                (long long)(m.rows * m.cols));
+  if (((uintptr_t)m.ptr) % (uintptr_t)elem_size(m.dtype) != 0)
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "%s[%d]: pointer not aligned to its element size", what, i);
+  return MUON_OK;
+}
+
+int same_shape(const muon_matrix& a, const muon_matrix& b, const char* wa, const char* wb, int i, char* msg,
+               int len) {
+  if (a.rows != b.rows || a.cols != b.cols)
+    return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d] is %lld x %lld but %s[%d] is %lld x %lld", wb, i,
+                (long long)b.rows, (long long)b.cols, wa, i, (long long)a.rows, (long long)a.cols);
+  return MUON_OK;
+}
+
+}  // namespace
+
+int check_config(const muon_config* c, char* msg, int len) {
+  if (!c) return MUON_OK;
+  if (c->ns_steps < 1 || c->ns_steps > 64)
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "ns_steps %d outside [1, 64]", (int)c->ns_steps);
+  if (!finitef(c->ns_a) || !finitef(c->ns_b) || !finitef(c->ns_c))
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "ns coefficients must be finite");
+  if (!finitef(c->ns_eps) || c->ns_eps < 0.f) return fail(msg, len, MUON_ERR_INVALID_ARG, "ns_eps must be >= 0");
+  if (c->pp_iterations < 0 || c->pp_iterations > 8)
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "pp_iterations %d outside [0, 8]", (int)c->pp_iterations);
+  if (!finitef(c->pp_beta)) return fail(msg, len, MUON_ERR_INVALID_ARG, "pp_beta must be finite");
+  if (!finitef(c->pp_eps) || !(c->pp_eps > 0.f)) return fail(msg, len, MUON_ERR_INVALID_ARG, "pp_eps must be > 0");
+  if (!finitef(c->mu) || c->mu < 0.f || c->mu > 1.f)
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "mu must lie in [0, 1]");
+  if (c->nesterov != 0 && c->nesterov != 1) return fail(msg, len, MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
+  if (c->power_steps < 1 || c->power_steps > 64)
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "power_steps %d outside [1, 64]", (int)c->power_steps);
+  if (!finitef(c->contra)) return fail(msg, len, MUON_ERR_INVALID_ARG, "contra must be finite");
+  if (!finitef(c->target_uw) || c->target_uw < 0.f)
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "target_uw must be >= 0");
+  if (!finitef(c->lr)) return fail(msg, len, MUON_ERR_INVALID_ARG, "lr must be finite");
+  if (c->flags != 0) return fail(msg, len, MUON_ERR_INVALID_ARG, "flags must be 0");
+  return MUON_OK;
+}
+
+int check_polar(int n, const muon_matrix* in, const muon_matrix* out, const muon_config* cfg, char* msg, int len) {
+  if (msg && len > 0) msg[0] = 0;
+  if (n < 0 || n > kMaxBatch) return fail(msg, len, MUON_ERR_INVALID_ARG, "batch size %d outside [0, %d]", n, kMaxBatch);
+  if (n > 0 && (!in || !out)) return fail(msg, len, MUON_ERR_INVALID_ARG, "NULL descriptor array");
+  int rc = check_config(cfg, msg, len);
+  if (rc) return rc;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_matrix(in[i], "in", i, msg, len))) return rc;
+    if ((rc = check_matrix(out[i], "out", i, msg, len))) return rc;
+    if ((rc = same_shape(in[i], out[i], "in", "out", i, msg, len))) return rc;
+  }
+  return MUON_OK;
+}
+
+int check_update(int n, const muon_matrix* g, const muon_matrix* m, const muon_matrix* w, const muon_matrix* uo,
+                 const muon_config* cfg, char* msg, int len) {
+  if (msg && len > 0) msg[0] = 0;
+  if (n < 0 || n > kMaxBatch) return fail(msg, len, MUON_ERR_INVALID_ARG, "batch size %d outside [0, %d]", n, kMaxBatch);
+  if (n > 0 && (!g || !m)) return fail(msg, len, MUON_ERR_INVALID_ARG, "NULL grad or momentum array");
+  int rc = check_config(cfg, msg, len);
+  if (rc) return rc;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_matrix(g[i], "grad", i, msg, len))) return rc;
+    if ((rc = check_matrix(m[i], "momentum", i, msg, len))) return rc;
+    if (m[i].dtype != MUON_F32)
+      return fail(msg, len, MUON_ERR_UNSUPPORTED_DTYPE, "momentum[%d] must be MUON_F32", i);
+    if ((rc = same_shape(g[i], m[i], "grad", "momentum", i, msg, len))) return rc;
+    if (w && w[i].ptr) {
+      if ((rc = check_matrix(w[i], "weight", i, msg, len))) return rc;
+      if ((rc = same_shape(g[i], w[i], "grad", "weight", i, msg, len))) return rc;
+    }
+    if (uo && uo[i].ptr) {
+      if ((rc = check_matrix(uo[i], "update_out", i, msg, len))) return rc;
+      if ((rc = same_shape(g[i], uo[i], "grad", "update_out", i, msg, len))) return rc;
+    }
+  }
+  return MUON_OK;
+}
+
+}  // namespace muon
+
+extern "C" muon_status muon_check_update_args(int n, const muon_matrix* grad, const muon_matrix* momentum,
+                                              const muon_matrix* weight, const muon_matrix* update_out,
+                                              const muon_config* cfg, char* msg, int msg_len) {
+  return muon::check_update(n, grad, momentum, weight, update_out, cfg, msg, msg_len);
+}
+
+extern "C" muon_status muon_check_polar_args(int n, const muon_matrix* in, const muon_matrix* out,
+                                             const muon_config* cfg, char* msg, int msg_len) {
+  return muon::check_polar(n, in, out, cfg, msg, msg_len);
+}
+
+extern "C" void muon_config_default(muon_config* c) {
+  if (!c) return;
+  c->ns_steps = 12;
+  c->ns_a = 2.0f;
+  c->ns_b = -1.5f;
+  c->ns_c = 0.5f;
+  c->ns_eps = 1e-7f;
+  c->pp_iterations = 2;
+  c->pp_beta = 0.5f;
+  c->pp_eps = 1e-7f;
+  c->mu = 0.95f;
+  c->nesterov = 1;
+  c->power_steps = 5;
+  c->contra = 0.4f;
+  c->target_uw = 0.35f;
+  c->lr = 0.0375f;
+  c->flags = 0;
+}
+
+extern "C" const char* muon_status_string(muon_status s) {
+  switch (s) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG";
+    case MUON_ERR_UNSUPPORTED_DTYPE: return "MUON_ERR_UNSUPPORTED_DTYPE";
+    case MUON_ERR_SHAPE_MISMATCH: return "MUON_ERR_SHAPE_MISMATCH";
+    case MUON_ERR_ALLOC: return "MUON_ERR_ALLOC";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+    case MUON_ERR_NO_DEVICE: return "MUON_ERR_NO_DEVICE";
+    default: return "MUON_ERR_UNKNOWN";
+  }
+}
+
+extern "C" const char* muon_version(void) { return "0.1.0"; }

@@ -50,7 +50,7 @@ import numpy as np
 
 __all__ = [
     "OracleConfig", "ns_poly", "newton_schulz", "aurora_orthogonalize",
-    "power_sigma", "muon_update", "ns5_classic",
+    "power_sigma", "momentum_nesterov", "muon_update", "ns5_classic",
 ]
 
 
@@ -185,6 +185,20 @@ def power_sigma(X, steps=5):
 # u/w-floor, and the lr / weight-decay rows of §"完整的超参配置表")
 # ---------------------------------------------------------------------------
 
+def momentum_nesterov(G, M, mu=0.95, nesterov=True):
+    """Elementwise first two steps of muon_update: returns (M', X).
+
+    momentum.lerp_(grad, 1 - mu) gives M' = M + (1 - mu)(G - M); the Nesterov
+    blend grad.lerp_(momentum, mu) gives X = G + mu (M' - G); without Nesterov
+    X = M' ([Aurora page] §"组合优化栈", muon_update).
+    """
+    G = np.asarray(G, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    M_new = M + (1.0 - mu) * (G - M)
+    X = G + mu * (M_new - G) if nesterov else M_new
+    return M_new, X
+
+
 def muon_update(G, M, W=None, cfg: OracleConfig = OracleConfig()):
     """One Aurora + Contra-Muon + u/w-floor step on one matrix.
 
@@ -208,8 +222,7 @@ def muon_update(G, M, W=None, cfg: OracleConfig = OracleConfig()):
         raise ValueError("G and M must be matrices of one shape")
     rows, cols = G.shape
 
-    M_new = M + (1.0 - cfg.mu) * (G - M)
-    X = G + cfg.mu * (M_new - G) if cfg.nesterov else M_new
+    M_new, X = momentum_nesterov(G, M, cfg.mu, cfg.nesterov)
 
     U = aurora_orthogonalize(X, cfg.pp_iterations, cfg.pp_beta, cfg.pp_eps,
                              cfg.ns_steps, cfg.ns_a, cfg.ns_b, cfg.ns_c,

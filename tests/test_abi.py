@@ -1,0 +1,143 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+function include/libmuon.h declares, its defaults equal the page's locked
+values, and host-side validation rejects bad batches with the documented
+status codes (nothing is enqueued; no device is touched)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import muon_newton_schulz_update_amd as mu
+from muon_newton_schulz_update_amd import MuonMatrix
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmuon.h")
+PAGE = json.load(open(os.path.join(ROOT, "tests", "golden", "page_constants.json")))
+
+OK, INVALID, DTYPE, SHAPE = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mu.library_path()):
+        pytest.skip("libmuon.so not built")
+    return mu.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"ns_polar", "aurora_orthogonalize", "muon_update", "muon_create"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libmuon.so does not export {n}"
+
+
+def test_defaults_equal_page_values(lib):
+    c = mu.default_config()
+    assert c.ns_steps == PAGE["ns"]["steps"]
+    assert (c.ns_a, c.ns_b, c.ns_c) == (PAGE["ns"]["a"], PAGE["ns"]["b"], PAGE["ns"]["c"])
+    assert c.ns_eps == pytest.approx(PAGE["ns"]["norm_eps"], rel=1e-6)
+    assert c.pp_iterations == PAGE["table"]["pp_iterations"]
+    assert c.pp_beta == PAGE["table"]["pp_beta"]
+    assert c.pp_eps == pytest.approx(PAGE["aurora_signature"]["eps"], rel=1e-6)
+    assert c.mu == pytest.approx(PAGE["muon_update_signature"]["mu"], rel=1e-7)
+    assert c.nesterov == 1
+    assert c.power_steps == PAGE["power_steps"]
+    assert c.contra == pytest.approx(PAGE["contra"], rel=1e-7)
+    assert c.target_uw == pytest.approx(PAGE["target_uw"], rel=1e-7)
+    assert c.lr == pytest.approx(PAGE["table"]["lr"], rel=1e-7)
+    assert c.flags == 0
+
+
+def test_status_strings(lib):
+    for code, name in mu.STATUS.items():
+        assert lib.muon_status_string(code).decode() == name
+    assert lib.muon_version().decode().count(".") == 2
+
+
+FAKE = 0x10000  # never dereferenced: validation is host-only
+
+
+def m(rows, cols, dtype=1, ld=None, ptr=FAKE):
+    return MuonMatrix(ptr, rows, cols, cols if ld is None else ld, dtype)
+
+
+def test_valid_batch_passes(lib):
+    g = [m(4, 8), m(16, 3, 0), m(0, 5)]
+    mom = [m(4, 8, 0), m(16, 3, 0), m(0, 5, 0)]
+    rc, msg = mu.check_update_args(g, mom, [m(4, 8), MuonMatrix(None, 0, 0, 0, 0), m(0, 5)], None)
+    assert rc == OK, msg
+    assert mu.check_update_args([], [], None, None)[0] == OK
+
+
+@pytest.mark.parametrize("case,code", [
+    ("null_ptr", INVALID), ("ld_lt_cols", SHAPE), ("bad_dtype", DTYPE), ("mom_bf16", DTYPE),
+    ("shape_mismatch", SHAPE), ("weight_mismatch", SHAPE), ("out_mismatch", SHAPE),
+    ("negative", SHAPE), ("too_big", SHAPE), ("short_too_big", SHAPE), ("misaligned", INVALID),
+])
+def test_update_validation(lib, case, code):
+    g, mom, w, uo = [m(4, 8)], [m(4, 8, 0)], None, None
+    if case == "null_ptr":
+        g = [m(4, 8, ptr=None)]
+    elif case == "ld_lt_cols":
+        g = [m(4, 8, ld=7)]
+    elif case == "bad_dtype":
+        g = [m(4, 8, dtype=7)]
+    elif case == "mom_bf16":
+        mom = [m(4, 8, 1)]
+    elif case == "shape_mismatch":
+        mom = [m(4, 9, 0)]
+    elif case == "weight_mismatch":
+        w = [m(8, 4)]
+    elif case == "out_mismatch":
+        uo = [m(4, 7, 0)]
+    elif case == "negative":
+        g, mom = [m(-1, 8)], [m(-1, 8, 0)]
+    elif case == "too_big":
+        g, mom = [m(4, 70000)], [m(4, 70000, 0)]
+    elif case == "short_too_big":
+        g, mom = [m(20000, 20000)], [m(20000, 20000, 0)]
+    elif case == "misaligned":
+        g = [m(4, 8, ptr=FAKE + 1)]
+    rc, msg = mu.check_update_args(g, mom, w, uo)
+    assert rc == code, (case, rc, msg)
+    assert msg
+
+
+@pytest.mark.parametrize("field,value", [
+    ("ns_steps", 0), ("ns_steps", 65), ("pp_iterations", -1), ("pp_iterations", 9),
+    ("mu", 1.5), ("mu", -0.1), ("nesterov", 2), ("power_steps", 0), ("pp_eps", 0.0),
+    ("target_uw", -1.0), ("flags", 1), ("lr", float("nan")), ("ns_a", float("inf")),
+])
+def test_config_validation(lib, field, value):
+    cfg = mu.default_config()
+    setattr(cfg, field, value)
+    rc, msg = mu.check_update_args([m(4, 8)], [m(4, 8, 0)], None, None, cfg)
+    assert rc == INVALID, (field, value, rc, msg)
+
+
+def test_polar_validation(lib):
+    assert mu.check_polar_args([m(5, 3)], [m(5, 3, 0)])[0] == OK
+    assert mu.check_polar_args([m(5, 3)], [m(3, 5)])[0] == SHAPE
+    assert mu.check_polar_args([m(5, 3)], [m(5, 3, 9)])[0] == DTYPE
+    assert mu.check_polar_args([m(5, 3, ptr=None)], [m(5, 3)])[0] == INVALID
+
+
+def test_batch_count_limits(lib):
+    buf = ctypes.create_string_buffer(64)
+    assert lib.muon_check_polar_args(-1, None, None, None, buf, 64) == INVALID
+    assert lib.muon_check_update_args(2, None, None, None, None, None, buf, 64) == INVALID
+
+
+def test_null_handle_is_rejected(lib):
+    assert lib.ns_polar(None, 0, None, None, None) == INVALID
+    assert lib.muon_update(None, 0, None, None, None, None, None) == INVALID
+    assert lib.muon_destroy(None) == OK

@@ -1,0 +1,336 @@
+"""GPU parity of libmuon (through its C ABI) against the float64 oracle.
+
+Tolerances (relative Frobenius error of the update / polar output):
+  fp32 path  <= 1e-4;  bf16 matrix-core path <= 3e-2;
+  long-side row norms agree within 1e-2 (bf16);  momentum <= 1e-6 (relative).
+Weights are checked exactly against the update the same call returned
+(W' == round(W - lr V)); V itself is checked against the oracle.
+Inputs come from the seeded generators; the oracle reads the stored tensors.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import muon_newton_schulz_update_amd as mu
+from muon_newton_schulz_update_amd import inputs as gen
+from oracle import muon_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL, BF16_TOL, ROW_TOL, MOM_TOL = 1e-4, 3e-2, 1e-2, 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def row_agree(a, b):
+    """max relative difference of long-side row norms."""
+    if a.shape[0] < a.shape[1]:
+        a, b = a.T, b.T
+    na, nb = np.linalg.norm(a, axis=1), np.linalg.norm(b, axis=1)
+    mask = nb > 1e-6 * nb.max()
+    return float(np.max(np.abs(na[mask] / nb[mask] - 1))) if mask.any() else 0.0
+
+
+def ocfg(cfg: mu.MuonConfig) -> O.OracleConfig:
+    return O.OracleConfig(ns_steps=cfg.ns_steps, ns_a=cfg.ns_a, ns_b=cfg.ns_b, ns_c=cfg.ns_c,
+                          ns_eps=float(np.float32(cfg.ns_eps)), pp_iterations=cfg.pp_iterations,
+                          pp_beta=cfg.pp_beta, pp_eps=float(np.float32(cfg.pp_eps)),
+                          mu=float(np.float32(cfg.mu)), nesterov=bool(cfg.nesterov),
+                          power_steps=cfg.power_steps, contra=float(np.float32(cfg.contra)),
+                          target_uw=float(np.float32(cfg.target_uw)), lr=float(np.float32(cfg.lr)))
+
+
+def weight_add_ok(W0, V, W1, cfg):
+    """W1 == round(W0 - lr V): within one ulp of the stored type (the kernel
+    may fuse the multiply-add, so fp32 is allowed the product's rounding too)."""
+    lr = np.float32(cfg.lr)
+    want = (W0.float() - lr * V.float()).to(W0.dtype).float()
+    diff = (W1.float() - want).abs()
+    # fp32 rounding of the two terms (fused or not), plus one ulp of the stored type
+    tol = (W0.float().abs() + lr * V.float().abs()) * 2.0 ** -22
+    if W0.dtype == torch.bfloat16:
+        tol = tol + want.abs() * 2.0 ** -7
+    return bool((diff <= tol + 1e-30).all())
+
+
+def rne_bf16(x64):
+    return torch.from_numpy(np.asarray(x64, dtype=np.float32)).to(torch.bfloat16)
+
+
+def check_update(case, G, M0, W0, M1, V, W1, cfg, tol, rows_tol=None):
+    """Compare one matrix's outputs with the oracle."""
+    oc = ocfg(cfg)
+    Mo, Vo, Wo = O.muon_update(f64(G), f64(M0), None if W0 is None else f64(W0), oc)
+    e_v = rel(f64(V), Vo)
+    e_m = rel(f64(M1), Mo)
+    say(f"  {case}: {tuple(G.shape)} {G.dtype} rel(V)={e_v:.2e} rel(M)={e_m:.2e}")
+    assert e_v <= tol, (case, e_v)
+    assert e_m <= MOM_TOL, (case, e_m)
+    if rows_tol is not None:
+        assert row_agree(f64(V), Vo) <= rows_tol, case
+    if W0 is not None:
+        # the parameter add is exact given the returned update: W' = round(W - lr V)
+        assert weight_add_ok(W0, V, W1, cfg), case
+    return e_v
+
+
+def run_update(dev, mats, cfg=None, out_dtype=torch.float32):
+    """mats: list of (G, M, W-or-None) on the device. Returns (M1, V, W1) lists and the originals."""
+    cfg = cfg or mu.default_config()
+    G = [g for g, _, _ in mats]
+    M0 = [m.clone() for _, m, _ in mats]
+    W0 = [None if w is None else w.clone() for _, _, w in mats]
+    M = [m.clone() for _, m, _ in mats]
+    W = [None if w is None else w.clone() for _, _, w in mats]
+    V = [torch.empty(g.shape, device=dev, dtype=out_dtype) for g in G]
+    have_w = any(w is not None for w in W)
+    mu.muon_update(G, M, W if have_w else None, cfg, update_out=V)
+    torch.cuda.synchronize()
+    return G, M0, W0, M, V, W
+
+
+# ---------------------------------------------------------------------------
+# ns_polar
+# ---------------------------------------------------------------------------
+ODD = [(1, 1), (1, 7), (7, 1), (5, 5), (33, 517), (517, 33), (255, 257), (300, 700)]
+
+
+def test_ns_polar_fp32_odd_shapes(dev):
+    say("ns_polar fp32 odd shapes (one batched call)")
+    xs = [gen.custom_matrix(s, 100 + i, dev)[0] for i, s in enumerate(ODD)]
+    outs = mu.ns_polar(xs)
+    torch.cuda.synchronize()
+    for x, u in zip(xs, outs):
+        e = rel(f64(u), O.newton_schulz(f64(x)))
+        say(f"  {tuple(x.shape)} rel={e:.2e}")
+        assert e <= FP32_TOL
+
+
+def test_ns_polar_bf16(dev):
+    say("ns_polar bf16")
+    shapes = [(300, 700), (768, 768), (700, 300), (40, 1000)]
+    xs = [gen.custom_matrix(s, 200 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3)[0]
+          for i, s in enumerate(shapes)]
+    outs = mu.ns_polar(xs, [torch.empty(x.shape, device=dev, dtype=torch.float32) for x in xs])
+    torch.cuda.synchronize()
+    for x, u in zip(xs, outs):
+        want = O.newton_schulz(f64(x))
+        e = rel(f64(u), want)
+        say(f"  {tuple(x.shape)} rel={e:.2e} rows={row_agree(f64(u), want):.2e}")
+        assert e <= BF16_TOL
+        assert row_agree(f64(u), want) <= ROW_TOL
+
+
+def test_ns_polar_aliasing_and_ld(dev):
+    say("ns_polar in-place and ld > cols")
+    x = gen.custom_matrix((130, 300), 300, dev)[0]
+    want = O.newton_schulz(f64(x))
+    y = x.clone()
+    mu.ns_polar([y], [y])                                   # out aliases in
+    big = torch.zeros((130, 512), device=dev)
+    big[:, 100:400] = x
+    view = big[:, 100:400]                                  # ld = 512
+    out_big = torch.full((130, 320), 7.0, device=dev)
+    mu.ns_polar([view], [out_big[:, :300]])
+    torch.cuda.synchronize()
+    assert rel(f64(y), want) <= FP32_TOL
+    assert rel(f64(out_big[:, :300]), want) <= FP32_TOL
+    assert bool((out_big[:, 300:] == 7.0).all())            # nothing outside the view written
+
+
+# ---------------------------------------------------------------------------
+# aurora_orthogonalize
+# ---------------------------------------------------------------------------
+def test_aurora_fp32(dev):
+    say("aurora fp32 pp=2 beta=0.5")
+    shapes = [(33, 517), (517, 33), (256, 1024), (600, 200), (96, 96)]
+    xs = [gen.custom_matrix(s, 400 + i, dev)[0] for i, s in enumerate(shapes)]
+    outs = mu.aurora_orthogonalize(xs)
+    torch.cuda.synchronize()
+    for x, u in zip(xs, outs):
+        e = rel(f64(u), O.aurora_orthogonalize(f64(x)))
+        say(f"  {tuple(x.shape)} rel={e:.2e}")
+        assert e <= FP32_TOL
+
+
+@pytest.mark.parametrize("pp,beta", [(1, 0.5), (3, 0.5), (2, 0.25), (2, 1.0), (0, 0.5)])
+def test_aurora_fp32_options(dev, pp, beta):
+    say(f"aurora fp32 pp={pp} beta={beta}")
+    x = gen.custom_matrix((384, 160), 500 + pp * 10 + int(beta * 4), dev)[0]
+    cfg = mu.make_config(pp_iterations=pp, pp_beta=beta)
+    u = mu.aurora_orthogonalize([x], cfg=cfg)[0]
+    torch.cuda.synchronize()
+    e = rel(f64(u), O.aurora_orthogonalize(f64(x), pp, beta))
+    say(f"  rel={e:.2e}")
+    assert e <= FP32_TOL
+
+
+def test_aurora_bf16(dev):
+    say("aurora bf16")
+    shapes = [(256, 1024), (1024, 256), (512, 512), (768, 3072)]
+    xs = [gen.custom_matrix(s, 600 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3)[0]
+          for i, s in enumerate(shapes)]
+    outs = mu.aurora_orthogonalize(xs, [torch.empty(x.shape, device=dev) for x in xs])
+    torch.cuda.synchronize()
+    for x, u in zip(xs, outs):
+        want = O.aurora_orthogonalize(f64(x))
+        e, r = rel(f64(u), want), row_agree(f64(u), want)
+        say(f"  {tuple(x.shape)} rel={e:.2e} rows={r:.2e}")
+        assert e <= BF16_TOL and r <= ROW_TOL
+
+
+# ---------------------------------------------------------------------------
+# muon_update
+# ---------------------------------------------------------------------------
+def test_update_single_fp32_256x1024(dev):
+    say("muon_update single_fp32_256x1024")
+    g, m, w = gen.make_matrix(gen.WORKLOADS["single_fp32_256x1024"], 0, dev)
+    G, M0, W0, M, V, W = run_update(dev, [(g, m, w)])
+    check_update("single_fp32", G[0], M0[0], W0[0], M[0], V[0], W[0], mu.default_config(), FP32_TOL)
+
+
+def test_update_mixed_batch_bf16(dev):
+    say("muon_update mixed bf16 batch with ragged shapes")
+    shapes = [(512, 256), (256, 512), (384, 384), (300, 129), (129, 300)]
+    mats = [gen.custom_matrix(s, 700 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3, mom_sd=1e-3,
+                              weight_dtype=torch.bfloat16) for i, s in enumerate(shapes)]
+    G, M0, W0, M, V, W = run_update(dev, mats)
+    for i in range(len(shapes)):
+        check_update(f"mixed[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], mu.default_config(), BF16_TOL, ROW_TOL)
+
+
+def test_update_mixed_dtypes_in_one_call(dev):
+    say("muon_update fp32 and bf16 matrices in one call")
+    a = gen.custom_matrix((200, 90), 800, dev)
+    b = gen.custom_matrix((90, 200), 801, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16)
+    G, M0, W0, M, V, W = run_update(dev, [a, b])
+    check_update("fp32", G[0], M0[0], W0[0], M[0], V[0], W[0], mu.default_config(), FP32_TOL)
+    check_update("bf16", G[1], M0[1], W0[1], M[1], V[1], W[1], mu.default_config(), BF16_TOL)
+
+
+def test_update_floor_forced(dev):
+    say("muon_update with the u/w floor firing (W ~ N(0,1))")
+    g, m, w = gen.custom_matrix((160, 480), 900, dev, weight_sd=1.0)
+    G, M0, W0, M, V, W = run_update(dev, [(g, m, w)])
+    check_update("floor", G[0], M0[0], W0[0], M[0], V[0], W[0], mu.default_config(), FP32_TOL)
+    ratio = torch.linalg.norm(V[0].double()) / torch.linalg.norm(W0[0].double())
+    assert float(ratio) == pytest.approx(0.35, rel=1e-4)
+
+
+@pytest.mark.parametrize("opt", ["contra0", "nesterov0", "pp0", "pp3", "no_weight_floor"])
+def test_update_options(dev, opt):
+    say(f"muon_update option {opt}")
+    over = {"contra0": dict(contra=0.0), "nesterov0": dict(nesterov=0), "pp0": dict(pp_iterations=0),
+            "pp3": dict(pp_iterations=3), "no_weight_floor": dict(target_uw=0.0)}[opt]
+    cfg = mu.make_config(**over)
+    g, m, w = gen.custom_matrix((260, 140), 1000 + len(opt), dev, weight_sd=1.0)
+    G, M0, W0, M, V, W = run_update(dev, [(g, m, w)], cfg)
+    check_update(opt, G[0], M0[0], W0[0], M[0], V[0], W[0], cfg, FP32_TOL)
+
+
+def test_update_zero_and_empty(dev):
+    say("muon_update zero and empty matrices")
+    z = torch.zeros((64, 200), device=dev)
+    wz = torch.full((64, 200), 0.5, device=dev)
+    e = torch.zeros((0, 5), device=dev)
+    G, M0, W0, M, V, W = run_update(dev, [(z, z.clone(), wz), (e, e.clone(), e.clone())])
+    assert bool(torch.isfinite(V[0]).all()) and float(V[0].abs().max()) == 0.0
+    assert torch.equal(W[0], wz) and float(M[0].abs().max()) == 0.0
+
+
+def test_update_power_restart(dev):
+    """Rows summing to zero: the all-ones start vector is annihilated and the
+    power iteration restarts from the largest column."""
+    say("muon_update power-iteration restart")
+    base = torch.tensor([[1.0, -1.0, 0.0, 0.0], [2.0, 0.0, -2.0, 0.0], [0.0, 3.0, 0.0, -3.0],
+                         [1.0, 1.0, -1.0, -1.0], [0.0, 0.0, 4.0, -4.0], [2.0, -1.0, -1.0, 0.0]])
+    g = base.repeat(1, 16).to(dev)              # 6 x 64, every row sums to zero
+    m = torch.zeros_like(g)
+    w = 0.02 * torch.ones_like(g)
+    G, M0, W0, M, V, W = run_update(dev, [(g, m, w)])
+    check_update("restart", G[0], M0[0], W0[0], M[0], V[0], W[0], mu.default_config(), FP32_TOL)
+
+
+def test_update_deterministic(dev):
+    say("muon_update bitwise determinism")
+    mats = [gen.custom_matrix(s, 1100 + i, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16)
+            for i, s in enumerate([(300, 500), (512, 512)])]
+    r1 = run_update(dev, mats)
+    r2 = run_update(dev, mats)
+    for a, b in zip(r1[4] + r1[3] + r1[5], r2[4] + r2[3] + r2[5]):
+        assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# the named workloads, in the configuration the benchmark times
+# ---------------------------------------------------------------------------
+def _workload_run(dev, name, sample, big_oracle=()):
+    w = gen.WORKLOADS[name]
+    cfg = mu.make_config(**dict(w.config))
+    grads, moms, weights = gen.make_batch(name, dev)
+    say(f"workload {name}: {len(grads)} matrices")
+    mats = list(zip(grads, moms, weights if weights is not None else [None] * len(grads)))
+    G, M0, W0, M, V, W = run_update(dev, mats, cfg, out_dtype=torch.float32)
+    # elementwise outputs the oracle computes one by one: momentum on sampled
+    # rows of every matrix; every update finite; W' = round(W - lr V) exactly
+    for i in range(len(G)):
+        r = G[i].shape[0]
+        rows = sorted({0, r // 3, r // 2, r - 1})
+        mo, _ = O.momentum_nesterov(f64(G[i][rows]), f64(M0[i][rows]), float(np.float32(cfg.mu)),
+                                    bool(cfg.nesterov))
+        assert rel(f64(M[i][rows]), mo) <= MOM_TOL, i
+        assert bool(torch.isfinite(V[i]).all()), i
+        if W0[i] is not None:
+            assert weight_add_ok(W0[i], V[i], W[i], cfg), i
+    # whole-matrix oracle on a sample
+    for i in list(sample) + list(big_oracle):
+        check_update(f"{name}[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], cfg, BF16_TOL, ROW_TOL)
+    return cfg, grads, moms, weights, V
+
+
+def test_workload_ns_48x768sq(dev):
+    _workload_run(dev, "ns_48x768sq_bf16", sample=[0, 17, 47])
+
+
+def test_workload_gpt2_124m(dev):
+    _workload_run(dev, "gpt2_124m_matrices", sample=[0, 4, 5, 70, 71])
+
+
+def test_workload_llama3p8b_layer(dev):
+    # k (1024x3072), v and the 12288x3072 up-projection against the oracle
+    _workload_run(dev, "llama3p8b_layer", sample=[1, 2], big_oracle=[4])
+
+
+def test_workload_llama3p8b_all_layers(dev):
+    cfg, grads, moms, weights, V = _workload_run(dev, "llama3p8b_all_layers", sample=[1, 164])
+    # batching independence: a matrix run alone gives the same bits as inside the 168-matrix batch
+    w = gen.WORKLOADS["llama3p8b_all_layers"]
+    for i in (0, 101, 167):
+        g, m, wt = gen.make_matrix(w, i, dev)
+        v = torch.empty(g.shape, device=dev)
+        mu.muon_update([g], [m], [wt], cfg, update_out=[v])
+        torch.cuda.synchronize()
+        say(f"  batch independence [{i}] {tuple(g.shape)}")
+        assert torch.equal(v, V[i]), i
