@@ -85,6 +85,9 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3p8b_all_layers")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-launch event timing")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -112,6 +115,15 @@ def main() -> int:
 
     h = mu.get_handle(0)
     h.reserve([(r, c, w.grad_dtype) for r, c in shapes])
+    if a.copy_calibration_mib > 0:
+        n = a.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {a.copy_calibration_mib} MiB read + {a.copy_calibration_mib} MiB written")
+        del src, dst
 
     def step():
         mu.muon_update(grads, moms, weights, cfg, handle=h)

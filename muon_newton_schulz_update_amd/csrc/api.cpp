@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -32,7 +33,7 @@
 namespace muon {
 
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
-                          float ca, float cb, float cc, hipStream_t st);
+                          float ca, float cb, float cc, int variant, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  hipStream_t st);
 hipError_t launch_norms_finalize(DevMat* m, LaunchList L, int nblk, float pp_eps, float ns_eps, int init_power,
@@ -55,6 +56,7 @@ namespace {
 enum Kind { KIND_NS = 0, KIND_AURORA = 1, KIND_UPDATE = 2 };
 
 constexpr size_t kAlign = 256;
+constexpr int kSuperM = 4, kSuperN = 8;   // NS tile raster (one XCD's 32 CUs)
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 inline int esz(int dt) { return dt == DT_BF16 ? 2 : 4; }
@@ -127,6 +129,7 @@ struct ProfRec {
 
 struct muon_handle {
   int device = 0;
+  int ns_variant = 0;        // Newton-Schulz tile layout (MUON_NS_VARIANT; 0 = 8 waves, 1 = 4 waves)
   hipStream_t stream = nullptr;
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -256,7 +259,7 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
   add_list(meta, P->stream, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = 1;
   add_list(meta, P->permat, all, blocks);
-  for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].rows, 4);
+  for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].rows, 16);   // 4 waves x 4 rows
   add_list(meta, P->matvec, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = P->mats[i].n_rmv * P->mats[i].n_ct;
   add_list(meta, P->rmatvec, all, blocks);
@@ -308,14 +311,21 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
           const MatInfo& m = P->mats[i];
           const int ts = m.s_pad / kTile, tl = m.L_pad / kTile;
           const double s = m.s, L = m.L;
+          const int tcols = mode == GM_BX ? tl : ts;
+          // Super-tiles of kSuperM x kSuperN tiles, row-major inside and
+          // across: one super-tile is one XCD's wave of workgroups, so its
+          // tiles share kSuperM row panels and kSuperN column panels in L2.
+          for (int a0 = 0; a0 < ts; a0 += kSuperM)
+            for (int b0 = 0; b0 < tcols; b0 += kSuperN)
+              for (int a = a0; a < std::min(ts, a0 + kSuperM); ++a)
+                for (int b = b0; b < std::min(tcols, b0 + kSuperN); ++b) {
+                  if (mode != GM_BX && b < a) continue;   // symmetric: upper tiles only
+                  items.push_back(TileItem{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
+                }
           if (mode == GM_BX) {
-            for (int a = 0; a < ts; ++a)
-              for (int b = 0; b < tl; ++b) items.push_back(TileItem{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
             G.counted += 2.0 * s * s * L;
             G.executed += 2.0 * ts * tl * kTile * (double)kTile * m.s_pad;
           } else {
-            for (int a = 0; a < ts; ++a)
-              for (int b = a; b < ts; ++b) items.push_back(TileItem{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
             const double K = mode == GM_GRAM ? m.L_pad : m.s_pad;
             G.counted += mode == GM_GRAM ? 2.0 * s * s * L : 2.0 * s * s * s;
             G.executed += 2.0 * (ts * (ts + 1) / 2) * kTile * (double)kTile * K;
@@ -620,7 +630,7 @@ muon_status run(muon_handle* h, const Call& c) {
           if (G.n == 0) continue;
           ProfScope ps(h, 0, G.counted, G.executed);
           CHECK_LAUNCH(h, launch_ns_gemm(t, D, (const TileItem*)((uint8_t*)P->meta_dev + G.off), G.n, mode, cur,
-                                         cfg.ns_a, cfg.ns_b, cfg.ns_c, st));
+                                         cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, st));
         }
     }
     if (p + 1 < P->passes) {
@@ -677,6 +687,7 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
   if (!h) return MUON_ERR_ALLOC;
   h->device = dev;
   h->stream = (hipStream_t)stream;
+  if (const char* v = getenv("MUON_NS_VARIANT")) h->ns_variant = atoi(v) == 1 ? 1 : 0;
   if (hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming) != hipSuccess) {
     (void)hipGetLastError();
     delete h;

@@ -10,9 +10,10 @@
 // X^T is kept beside X (written by the GM_BX epilogue), so all three read
 // both operands with the reduction index contiguous: C[m][n] = sum_k P[m][k] Q[n][k].
 //
-// Tiling: 256 x 256 output tile per 512-thread workgroup (8 waves in 4 x 2,
-// each wave 64 x 128 = 2 x 4 MFMA 32x32 blocks, accumulators in AGPRs; two
-// waves share a SIMD).
+// Tiling: 256 x 256 output tile per workgroup; default 512 threads (8 waves
+// in 4 x 2, each wave 64 x 128 = 2 x 4 MFMA 32x32 blocks, accumulators in
+// AGPRs, two waves per SIMD); a 4-wave layout (2 x 2 waves of 128 x 128) is
+// kept for tuning.
 // K advances 128 bytes per row per stage (64 bf16 or 32 fp32); two LDS stages
 // of 64 KB are filled by direct global->LDS 16-byte loads, so the next stage
 // streams in while the current one feeds the matrix cores. LDS rows are
@@ -39,7 +40,7 @@ constexpr int kRowBytes = 128;                 // bytes of K per tile row per st
 constexpr int kStageA = kTile * kRowBytes;     // 32 KB
 constexpr int kStageBytes = 2 * kStageA;       // A + B operand = 64 KB
 constexpr int kPitch = 132;                    // floats per staged epilogue row (128 + 4 spreads banks)
-constexpr int kSlabBytes = 32 * kPitch * 4;    // one wave's 32 x 128 staging slab
+constexpr int kSlabBytes = 32 * kPitch * 4;    // one wave's 32 x 128 staging slab (NI*32 <= 128)
 constexpr int kLdsBytes = 8 * kSlabBytes > 2 * kStageBytes ? 8 * kSlabBytes : 2 * kStageBytes;
 
 // 16-byte chunk position of logical chunk c of tile row r.
@@ -98,17 +99,19 @@ template <> struct Elem<float> {
 };
 
 // Issue the direct-to-LDS loads of one stage: rows [0, 256) of P and of Q,
-// 128 bytes of K per row. Wave w, instruction i fills the 8 tile rows of group
-// g = 8 i + w; lane p fetches the logical chunk that belongs at LDS position p
-// of that 1 KB group. The swizzle of row g*8 + p/8 does not depend on i, so a
-// lane needs one 32-bit byte offset (`lane_off`); the per-instruction row step
-// (`row64`, 64 rows) and the K position (`kb`) are uniform.
+// 128 bytes of K per row. With NW waves, wave w's instruction i fills the 8
+// tile rows of group g = NW i + w; lane p fetches the logical chunk that
+// belongs at LDS position p of that 1 KB group. The swizzle of row g*8 + p/8
+// does not depend on i, so a lane needs one 32-bit byte offset (`lane_off`);
+// the per-instruction row step (`rstep` = NW*8 rows) and the K position (`kb`)
+// are uniform.
+template <int NW>
 __device__ __forceinline__ void issue_stage(uint8_t* sm, const uint8_t* P, const uint8_t* Q,
-                                            int64_t row64, int64_t kb, uint32_t lane_off, int wave) {
+                                            int64_t rstep, int64_t kb, uint32_t lane_off, int wave) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = i * 8 + wave;
-    const int64_t u = kb + i * row64;
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int g = i * NW + wave;
+    const int64_t u = kb + i * rstep;
     __builtin_amdgcn_global_load_lds((const void*)(P + u + lane_off), LDS_PTR(sm + g * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(Q + u + lane_off), LDS_PTR(sm + kStageA + g * 1024), 16, 0, 0);
   }
@@ -117,41 +120,41 @@ __device__ __forceinline__ void issue_stage(uint8_t* sm, const uint8_t* P, const
 // Fragment reads: lane l reads tile row (base + l%32), logical chunk
 // 2j + l/32. Bases are multiples of 32 rows, so the swizzle term depends on
 // l only and the per-block part is an immediate offset.
-template <typename T>
-__device__ __forceinline__ void compute_stage(const uint8_t* sm, f32x16_t (&acc)[2][4],
+template <typename T, int MI, int NI>
+__device__ __forceinline__ void compute_stage(const uint8_t* sm, f32x16_t (&acc)[MI][NI],
                                               int lane, int wm, int wn) {
   const int lr = lane & 31;
   const int sw = (lr >> 1) & 7;
-  const uint8_t* pa_base = sm + (wm * 64 + lr) * kRowBytes;
-  const uint8_t* qa_base = sm + kStageA + (wn * 128 + lr) * kRowBytes;
+  const uint8_t* pa_base = sm + (wm * MI * 32 + lr) * kRowBytes;
+  const uint8_t* qa_base = sm + kStageA + (wn * NI * 32 + lr) * kRowBytes;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int ph = ((2 * j + (lane >> 5)) ^ sw) * 16;
     if constexpr (sizeof(T) == 2) {
-      bf16x8_t pa[2], qa[4];
+      bf16x8_t pa[MI], qa[NI];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) pa[mi] = *(const bf16x8_t*)(pa_base + mi * 32 * kRowBytes + ph);
+      for (int mi = 0; mi < MI; ++mi) pa[mi] = *(const bf16x8_t*)(pa_base + mi * 32 * kRowBytes + ph);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) qa[ni] = *(const bf16x8_t*)(qa_base + ni * 32 * kRowBytes + ph);
+      for (int ni = 0; ni < NI; ++ni) qa[ni] = *(const bf16x8_t*)(qa_base + ni * 32 * kRowBytes + ph);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[mi], qa[ni], acc[mi][ni], 0, 0, 0);
     } else {
-      f32x4_t pa[2], qa[4];
+      f32x4_t pa[MI], qa[NI];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) pa[mi] = *(const f32x4_t*)(pa_base + mi * 32 * kRowBytes + ph);
+      for (int mi = 0; mi < MI; ++mi) pa[mi] = *(const f32x4_t*)(pa_base + mi * 32 * kRowBytes + ph);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) qa[ni] = *(const f32x4_t*)(qa_base + ni * 32 * kRowBytes + ph);
+      for (int ni = 0; ni < NI; ++ni) qa[ni] = *(const f32x4_t*)(qa_base + ni * 32 * kRowBytes + ph);
       // the 4 floats of a chunk are 4 consecutive k; lanes 0-31 and 32-63
       // supply the two k slots of each 32x32x2 step from chunks 2j and 2j+1
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
+          for (int ni = 0; ni < NI; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[mi][e], qa[ni][e], acc[mi][ni], 0, 0, 0);
     }
   }
@@ -161,15 +164,16 @@ __device__ __forceinline__ void compute_stage(const uint8_t* sm, f32x16_t (&acc)
 
 // Launch geometry: grid.x = 8 * per_xcd blocks; the hardware deals
 // consecutive workgroups round-robin to the 8 XCDs, so block b runs on XCD
-// b % 8. Items are dealt to XCDs in runs of `group` consecutive items (which
-// share an operand panel), keeping each run inside one XCD's L2.
-template <typename T, int mode>
-__global__ __launch_bounds__(512, 1) void k_ns_gemm(const DevMat* __restrict__ mats,
+// b % 8. Items are dealt to XCDs in runs of `group` consecutive items (one
+// super-tile of the planner's raster, whose tiles share operand panels), so a
+// run executes together on one XCD and reuses its L2.
+template <typename T, int mode, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __restrict__ mats,
                                                     const TileItem* __restrict__ items,
                                                     int n_items, int group, int cur,
                                                     float ca, float cb, float cc) {
   // two 64 KB operand stages; after the K loop the same memory stages the
-  // epilogue (8 waves x 32 x 132 floats = 132 KB)
+  // epilogue (one 32 x (NI*32) float slab per wave, at most 132 KB)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
   uint8_t* const sm0 = smem;
   uint8_t* const sm1 = smem + kStageBytes;
@@ -182,7 +186,10 @@ __global__ __launch_bounds__(512, 1) void k_ns_gemm(const DevMat* __restrict__ m
   const DevMat& M = mats[it.mat];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS bases stay in SGPRs
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int NW = WM * WN;                // waves per workgroup
+  constexpr int MI = kTile / WM / 32;        // 32x32 blocks per wave, down
+  constexpr int NI = kTile / WN / 32;        // 32x32 blocks per wave, across
+  const int wm = wave / WN, wn = wave % WN;
   const int sp = M.s_pad, Lp = M.L_pad;
 
   const T *P, *Q;
@@ -203,39 +210,39 @@ __global__ __launch_bounds__(512, 1) void k_ns_gemm(const DevMat* __restrict__ m
     ld = sp; K = sp;
   }
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[MI][NI];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = (f32x16_t){};
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = (f32x16_t){};
 
   constexpr int KE = kRowBytes / sizeof(T);   // K elements per stage
   const int nk = K / KE;
-  const int64_t row64 = (int64_t)64 * ld * sizeof(T);
+  const int64_t rstep = (int64_t)NW * 8 * ld * sizeof(T);
   const int lrow = wave * 8 + (lane >> 3);
   const uint32_t lane_off = (uint32_t)(((int64_t)lrow * ld + swz(lrow, lane & 7) * Elem<T>::kPerChunk) * sizeof(T));
   const uint8_t* Pb = (const uint8_t*)P;
   const uint8_t* Qb = (const uint8_t*)Q;
-  issue_stage(sm0, Pb, Qb, row64, 0, lane_off, wave);
+  issue_stage<NW>(sm0, Pb, Qb, rstep, 0, lane_off, wave);
   // K is a multiple of 256 elements, so the stage count is even.
   for (int kt = 0; kt < nk; kt += 2) {
     wait_vm_all();
     __syncthreads();
-    issue_stage(sm1, Pb, Qb, row64, (int64_t)(kt + 1) * kRowBytes, lane_off, wave);
-    compute_stage<T>(sm0, acc, lane, wm, wn);
+    issue_stage<NW>(sm1, Pb, Qb, rstep, (int64_t)(kt + 1) * kRowBytes, lane_off, wave);
+    compute_stage<T, MI, NI>(sm0, acc, lane, wm, wn);
     wait_vm_all();
     __syncthreads();
-    if (kt + 2 < nk) issue_stage(sm0, Pb, Qb, row64, (int64_t)(kt + 2) * kRowBytes, lane_off, wave);
-    compute_stage<T>(sm1, acc, lane, wm, wn);
+    if (kt + 2 < nk) issue_stage<NW>(sm0, Pb, Qb, rstep, (int64_t)(kt + 2) * kRowBytes, lane_off, wave);
+    compute_stage<T, MI, NI>(sm1, acc, lane, wm, wn);
   }
 
   // Epilogue. Accumulator register r of 32x32 block (mi, ni) holds
   // row 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of that block. Each wave
-  // stages one 32 x 128 slab of its 64 x 128 tile at a time in the now idle
+  // stages one 32-row slab of its tile at a time in the now idle
   // LDS, then writes it row-major (8 consecutive columns per lane) and, for
   // mirrored and X^T outputs, transposed (8 consecutive rows per lane).
-  const int row0 = it.tm * kTile + wm * 64;
-  const int col0 = it.tn * kTile + wn * 128;
+  const int row0 = it.tm * kTile + wm * MI * 32;
+  const int col0 = it.tn * kTile + wn * NI * 32;
   void* out;
   void* outT;
   const void* add;
@@ -252,18 +259,19 @@ __global__ __launch_bounds__(512, 1) void k_ns_gemm(const DevMat* __restrict__ m
   const bool write_t = (mode == GM_BX) || (it.tm != it.tn);
   float* buf = (float*)(smem + wave * kSlabBytes);
   __syncthreads();   // every wave is done reading the operand stages
+  constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         buf[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + ni * 32 + (lane & 31)] = agpr_read(acc[mi][ni][r]);
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < SC / 16; ++k) {
       const int q = k * 64 + lane;
-      const int rr = q >> 4, c8 = (q & 15) * 8;
+      const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = acc_coef * buf[rr * kPitch + c8 + e];
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(512, 1) void k_ns_gemm(const DevMat* __restrict__ m
     __syncthreads();
     if (write_t) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < SC / 16; ++k) {
         const int q = k * 64 + lane;
         const int c1 = q >> 2, rc = (q & 3) * 8;
         float v[8];
@@ -299,23 +307,31 @@ __global__ __launch_bounds__(512, 1) void k_ns_gemm(const DevMat* __restrict__ m
 // ---------------------------------------------------------------------------
 // Host-side launcher.
 // ---------------------------------------------------------------------------
+// variant 0: 8 waves in 4 x 2 (64 x 128 per wave, two waves per SIMD);
+// variant 1: 4 waves in 2 x 2 (128 x 128 per wave, one wave per SIMD).
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items,
-                          int mode, int cur, float ca, float cb, float cc, hipStream_t st) {
+                          int mode, int cur, float ca, float cb, float cc, int variant, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
-  const int group = 8;
+  const int group = 32;   // one super-tile of the planner's raster per XCD wave
   const int per_xcd_groups = (n_items + 8 * group - 1) / (8 * group);
-  const dim3 grid(per_xcd_groups * group * 8), block(512);
-#define NS_LAUNCH(T, MODE) \
-  hipLaunchKernelGGL((k_ns_gemm<T, MODE>), grid, block, 0, st, mats, items, n_items, group, cur, ca, cb, cc)
+  const dim3 grid(per_xcd_groups * group * 8);
+#define NS_LAUNCH(T, MODE, WM, WN) \
+  hipLaunchKernelGGL((k_ns_gemm<T, MODE, WM, WN>), grid, dim3(WM * WN * 64), 0, st, mats, items, n_items, group, \
+                     cur, ca, cb, cc)
+#define NS_MODES(T, WM, WN)                          \
+  do {                                               \
+    if (mode == GM_GRAM) NS_LAUNCH(T, GM_GRAM, WM, WN); \
+    else if (mode == GM_SQ) NS_LAUNCH(T, GM_SQ, WM, WN); \
+    else NS_LAUNCH(T, GM_BX, WM, WN);                \
+  } while (0)
   if (ns_t == DT_BF16) {
-    if (mode == GM_GRAM) NS_LAUNCH(__bf16, GM_GRAM);
-    else if (mode == GM_SQ) NS_LAUNCH(__bf16, GM_SQ);
-    else NS_LAUNCH(__bf16, GM_BX);
+    if (variant == 1) NS_MODES(__bf16, 2, 2);
+    else NS_MODES(__bf16, 4, 2);
   } else {
-    if (mode == GM_GRAM) NS_LAUNCH(float, GM_GRAM);
-    else if (mode == GM_SQ) NS_LAUNCH(float, GM_SQ);
-    else NS_LAUNCH(float, GM_BX);
+    if (variant == 1) NS_MODES(float, 2, 2);
+    else NS_MODES(float, 4, 2);
   }
+#undef NS_MODES
 #undef NS_LAUNCH
   return hipGetLastError();
 }

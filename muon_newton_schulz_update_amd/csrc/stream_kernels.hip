@@ -257,37 +257,45 @@ __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mat
   const void* src = use_xn ? (const void*)M.xn : M.g;
   const int64_t lds = use_xn ? (int64_t)M.cols : M.ld_g;
   const int sdt = use_xn ? M.ns_t : M.dt_g;
+  const bool vs = aligned16(src, lds, sdt);
   const float scale = M.scal[SC_SCALE];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   // direct frame: wide -> x[0] (ld L_pad); tall -> xt[0] (ld s_pad)
-  T* dir = (T*)(M.tall ? M.xt[0] : M.x[0]);
-  T* tra = (T*)(M.tall ? M.x[0] : M.xt[0]);
+  void* dir = M.tall ? M.xt[0] : M.x[0];
+  void* tra = M.tall ? M.x[0] : M.xt[0];
   const int ld_dir = M.tall ? M.s_pad : M.L_pad;
   const int ld_tra = M.tall ? M.L_pad : M.s_pad;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = br + i, c = bc + tx;
-    float v = 0.f;
-    if (r < M.rows && c < M.cols) {
-      const size_t idx = (size_t)r * lds + c;
-      v = (sdt == DT_BF16) ? bf2f(((const unsigned short*)src)[idx]) : ((const float*)src)[idx];
-      float d = scale;
-      if (M.aurora) d *= M.dvec[M.tall ? r : c];
-      v *= d;
+  const int odt = sizeof(T) == 2 ? DT_BF16 : DT_F32;
+  // 64 x 64 tile = 512 chunks of 8 columns; two chunks per thread
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = h * 256 + threadIdx.x;
+    const int i = q >> 3, j = (q & 7) * 8;
+    const int r = br + i, c = bc + j;
+    float v[8];
+    if (r < M.rows) {
+      load8(src, sdt, lds, r, c, M.cols, vs, v);   // zero past cols
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
     }
-    tile[i][tx] = v;
-    if constexpr (sizeof(T) == 2)
-      ((unsigned short*)dir)[(size_t)r * ld_dir + c] = f2bf(v);
-    else
-      ((float*)dir)[(size_t)r * ld_dir + c] = v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float d = scale;
+      if (M.aurora && r < M.rows && c + e < M.cols) d *= M.dvec[M.tall ? r : c + e];
+      v[e] *= d;
+      tile[i][j + e] = v[e];
+    }
+    store8(dir, odt, ld_dir, r, c, c + 8, true, v);
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int r = bc + i, c = br + tx;     // transposed frame
-    const float v = tile[tx][i];
-    if constexpr (sizeof(T) == 2)
-      ((unsigned short*)tra)[(size_t)r * ld_tra + c] = f2bf(v);
-    else
-      ((float*)tra)[(size_t)r * ld_tra + c] = v;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = h * 256 + threadIdx.x;
+    const int jc = q >> 3, i0 = (q & 7) * 8;   // transposed row = tile column jc
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[i0 + e][jc];
+    store8(tra, odt, ld_tra, bc + jc, br + i0, br + i0 + 8, true, v);
   }
 }
 
@@ -355,25 +363,40 @@ __device__ __forceinline__ float inv_fro(const DevMat& M) {
   return n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
 }
 
-// u = (X / ||X||) v : one wave per row, 4 rows per block.
+// u = (X / ||X||) v : each wave owns kMvRows rows (16 rows per block); a
+// lane loads 8 consecutive entries of v once and reuses them for every row.
+constexpr int kMvRows = 4;
 __global__ __launch_bounds__(256) void k_power_matvec(const DevMat* __restrict__ mats, LaunchList L,
                                                       int steps, int final_pass) {
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   if (!final_pass && M.ist[IS_PSTEPS] >= steps) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = local * 4 + w;
-  if (r >= M.rows) return;
+  const int r0 = (local * 4 + w) * kMvRows;
+  if (r0 >= M.rows) return;
   const bool vx = aligned16(M.xn, M.cols, M.ns_t);
-  float s = 0.f;
-  for (int c = lane * 8; c < M.cols; c += 512) {
-    float x[8];
-    load8(M.xn, M.ns_t, M.cols, r, c, M.cols, vx, x);
+  float s[kMvRows];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) if (c + e < M.cols) s += x[e] * M.pv[c + e];
+  for (int k = 0; k < kMvRows; ++k) s[k] = 0.f;
+  for (int c = lane * 8; c < M.cols; c += 512) {
+    float v[8];
+    load8(M.pv, DT_F32, 0, 0, c, M.cols, true, v);   // pv is 256-byte aligned workspace
+#pragma unroll
+    for (int k = 0; k < kMvRows; ++k) {
+      if (r0 + k < M.rows) {
+        float x[8];
+        load8(M.xn, M.ns_t, M.cols, r0 + k, c, M.cols, vx, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[k] += x[e] * v[e];
+      }
+    }
   }
-  s = wave_sum(s);
-  if (lane == 0) M.pu[r] = s * inv_fro(M);
+  const float inv = inv_fro(M);
+#pragma unroll
+  for (int k = 0; k < kMvRows; ++k) {
+    const float t = wave_sum(s[k]);
+    if (lane == 0 && r0 + k < M.rows) M.pu[r0 + k] = t * inv;
+  }
 }
 
 // partial w = (X / ||X||)^T u over kRmvRows rows x kStreamCols columns per block.
