@@ -35,6 +35,23 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per engine launch from the committed byte-counter record, or
+    None when there is none for this workload or the engine source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"ns_engine_{workload}_traffic.json")
+    src = os.path.join(ROOT, "muon_newton_schulz_update_amd", "csrc", "ns_gemm.hip")
+    try:
+        rec = json.load(open(path))
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != cur:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def step_flops(shapes, cfg) -> float:
     from muon_newton_schulz_update_amd.inputs import counted_ns_flops
     tot = 0.0
@@ -180,7 +197,7 @@ def main() -> int:
         peak = PEAK_BF16_TFLOPS if w.grad_dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
         out["roofline"] = {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(a.workload),
             "kernel": "k_ns_gemm (Gram, B = bA + cA^2, X = aX + BX launches together)",
             "launches": int(p["gemm_launches"]),
             "avg_launch_ms": round(p["gemm_ms"] / p["gemm_launches"], 4),

@@ -160,6 +160,21 @@ def test_ns_polar_aliasing_and_ld(dev):
     assert bool((out_big[:, 300:] == 7.0).all())            # nothing outside the view written
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, FP32_TOL), (torch.bfloat16, BF16_TOL)])
+def test_ns_polar_classic_five_step(dev, dtype, tol):
+    """The earlier 5-step recipe (Track-1 page) through the same engine."""
+    say(f"ns_polar classic 5-step recipe {dtype}")
+    cfg = mu.make_config(ns_steps=5, ns_a=3.4445, ns_b=-4.7750, ns_c=2.0315)
+    xs = [gen.custom_matrix(s, 250 + i, dev, grad_dtype=dtype, grad_sd=1e-3)[0]
+          for i, s in enumerate([(200, 600), (600, 200), (384, 384)])]
+    outs = mu.ns_polar(xs, [torch.empty(x.shape, device=dev) for x in xs], cfg=cfg)
+    torch.cuda.synchronize()
+    for x, u in zip(xs, outs):
+        e = rel(f64(u), O.ns5_classic(f64(x), 5, np.float32(3.4445), np.float32(-4.7750), np.float32(2.0315)))
+        say(f"  {tuple(x.shape)} rel={e:.2e}")
+        assert e <= tol
+
+
 # ---------------------------------------------------------------------------
 # aurora_orthogonalize
 # ---------------------------------------------------------------------------
