@@ -33,7 +33,7 @@
 namespace muon {
 
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
-                          float ca, float cb, float cc, int variant, hipStream_t st);
+                          int write_t, float ca, float cb, float cc, int variant, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  hipStream_t st);
 hipError_t launch_norms_finalize(DevMat* m, LaunchList L, int nblk, float pp_eps, float ns_eps, int init_power,
@@ -629,8 +629,10 @@ muon_status run(muon_handle* h, const Call& c) {
           const GemmList& G = P->gemm[g][t][mode];
           if (G.n == 0) continue;
           ProfScope ps(h, 0, G.counted, G.executed);
+          // X'^T is needed after a pass's last iteration (D update, output)
+          const int write_t = k + 1 == cfg.ns_steps;
           CHECK_LAUNCH(h, launch_ns_gemm(t, D, (const TileItem*)((uint8_t*)P->meta_dev + G.off), G.n, mode, cur,
-                                         cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, st));
+                                         write_t, cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, st));
         }
     }
     if (p + 1 < P->passes) {

@@ -287,6 +287,10 @@ __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mat
     }
     store8(dir, odt, ld_dir, r, c, c + 8, true, v);
   }
+  // bf16 iterates need only the wide orientation (the engine's BX reads X
+  // itself); fp32 iterates also keep X^T. A tall source's direct frame is
+  // X^T, so its transposed frame (X) is always written.
+  if (sizeof(T) == 2 && !M.tall) return;
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
