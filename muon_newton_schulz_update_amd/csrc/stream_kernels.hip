@@ -130,6 +130,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // Outputs per tile: rowpart[r][seg] (row sums over a wave segment) and, for
 // wide matrices, colpart[tile_row][c].
 // ---------------------------------------------------------------------------
+constexpr int kRB = 4;   // rows whose loads are issued together (memory-level parallelism)
+
 __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict__ mats, LaunchList L,
                                                         int nesterov_pass, float mu, int nesterov) {
   int local;
@@ -144,37 +146,49 @@ __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict
   const bool vg = aligned16(M.g, M.ld_g, M.dt_g);
   const bool vm = nesterov_pass ? aligned16(M.m, M.ld_m, DT_F32) : false;
   const bool vx = nesterov_pass ? aligned16(M.xn, M.cols, M.ns_t) : false;
-  float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const bool live = c < M.cols;
   const bool seg_live = seg < M.n_seg;
-  for (int r = r0; r < r1; ++r) {
-    float x[8];
-    if (c < M.cols) {
-      float g[8];
-      load8(M.g, M.dt_g, M.ld_g, r, c, M.cols, vg, g);
-      if (nesterov_pass) {
-        float m[8];
-        load8(M.m, DT_F32, M.ld_m, r, c, M.cols, vm, m);
+  float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r0; r < r1; r += kRB) {
+    // all loads of kRB rows first: the compiler cannot prove that the
+    // stores of one row do not alias the next row's inputs, so a per-row
+    // loop would serialise the memory traffic row by row
+    float x[kRB][8], m[kRB][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float mn = m[e] + (1.f - mu) * (g[e] - m[e]);
-          m[e] = mn;
-          x[e] = round_to(M.ns_t, nesterov ? g[e] + mu * (mn - g[e]) : mn);
-        }
-        store8(M.m, DT_F32, M.ld_m, r, c, M.cols, vm, m);
-        store8(M.xn, M.ns_t, M.cols, r, c, M.cols, vx, x);
+    for (int k = 0; k < kRB; ++k) {
+      const bool ok = live && r + k < r1;
+      if (ok) {
+        load8(M.g, M.dt_g, M.ld_g, r + k, c, M.cols, vg, x[k]);
+        if (nesterov_pass) load8(M.m, DT_F32, M.ld_m, r + k, c, M.cols, vm, m[k]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = g[e];
+        for (int e = 0; e < 8; ++e) x[k][e] = m[k][e] = 0.f;
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
     }
-    float rs = 0.f;
+    if (nesterov_pass) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { rs += x[e] * x[e]; col[e] += x[e] * x[e]; }
-    rs = wave_sum(rs);
-    if (lane == 0 && seg_live) M.rowpart[(size_t)r * M.n_seg + seg] = rs;
+      for (int k = 0; k < kRB; ++k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float g = x[k][e];
+          const float mn = m[k][e] + (1.f - mu) * (g - m[k][e]);
+          m[k][e] = mn;
+          x[k][e] = round_to(M.ns_t, nesterov ? g + mu * (mn - g) : mn);
+        }
+        if (live && r + k < r1) {
+          store8(M.m, DT_F32, M.ld_m, r + k, c, M.cols, vm, m[k]);
+          store8(M.xn, M.ns_t, M.cols, r + k, c, M.cols, vx, x[k]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kRB; ++k) {
+      float rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { rs += x[k][e] * x[k][e]; col[e] += x[k][e] * x[k][e]; }
+      rs = wave_sum(rs);
+      if (lane == 0 && seg_live && r + k < r1) M.rowpart[(size_t)(r + k) * M.n_seg + seg] = rs;
+    }
   }
   if (wide_cols) {
 #pragma unroll
@@ -241,10 +255,12 @@ __global__ __launch_bounds__(256) void k_norms_finalize(DevMat* __restrict__ mat
 }
 
 // ---------------------------------------------------------------------------
-// NS prologue: X0 = scale * D o T in the wide orientation, written to x[0]
-// (s_pad x L_pad) and its transpose to xt[0] (L_pad x s_pad), zero padded.
-// T is the source in storage orientation (rows x cols); for a tall source the
-// wide iterate is its transpose. 64 x 64 tiles over the padded storage frame.
+// NS prologue through an LDS transpose (tall sources, and fp32 sources):
+// X0 = scale * D o T in the wide orientation, written to x[0] (s_pad x L_pad)
+// and, for fp32 (whose BX reads it), its transpose to xt[0] (L_pad x s_pad),
+// zero padded. T is the source in storage orientation (rows x cols); for a
+// tall source the wide iterate is its transpose. 64 x 64 tiles over the
+// padded storage frame.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mats, LaunchList L, int use_xn) {
@@ -285,12 +301,8 @@ __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mat
       v[e] *= d;
       tile[i][j + e] = v[e];
     }
-    store8(dir, odt, ld_dir, r, c, c + 8, true, v);
+    if (sizeof(T) == 4) store8(dir, odt, ld_dir, r, c, c + 8, true, v);   // bf16 iterates keep no X^T
   }
-  // bf16 iterates need only the wide orientation (the engine's BX reads X
-  // itself); fp32 iterates also keep X^T. A tall source's direct frame is
-  // X^T, so its transposed frame (X) is always written.
-  if (sizeof(T) == 2 && !M.tall) return;
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -635,6 +647,48 @@ __global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ m
   }
 }
 
+// NS prologue without a transpose (bf16 wide or square sources, whose
+// iterate is the source itself): x[0] = scale * D o source over the padded
+// frame s_pad x L_pad, zero outside rows x cols. Tiles of kStreamRows x
+// kStreamCols; a lane owns 8 consecutive columns.
+__global__ __launch_bounds__(256) void k_prologue_direct(const DevMat* __restrict__ mats, LaunchList L, int use_xn) {
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  const int nct = (M.L_pad + kStreamCols - 1) / kStreamCols;
+  const int tr = local / nct, tc = local % nct;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = tc * kStreamCols + w * kSegCols + lane * 8;
+  if (c >= M.L_pad) return;
+  const int r0 = tr * kStreamRows, r1 = min(r0 + kStreamRows, M.s_pad);
+  const void* src = use_xn ? (const void*)M.xn : M.g;
+  const int64_t lds = use_xn ? (int64_t)M.cols : M.ld_g;
+  const int sdt = use_xn ? M.ns_t : M.dt_g;
+  const bool vs = aligned16(src, lds, sdt);
+  const float scale = M.scal[SC_SCALE];
+  float d[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) d[e] = (M.aurora && c + e < M.cols) ? scale * M.dvec[c + e] : scale;
+  for (int r = r0; r < r1; r += kRB) {
+    float v[kRB][8];
+#pragma unroll
+    for (int k = 0; k < kRB; ++k) {
+      if (r + k < M.rows) load8(src, sdt, lds, r + k, c, M.cols, vs, v[k]);   // zero past cols
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kRB; ++k) {
+      if (r + k < r1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[k][e] *= d[e];
+        store8(M.x[0], DT_BF16, M.L_pad, r + k, c, c + 8, true, v[k]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (grid sizes come from the planner's LaunchList).
 // ---------------------------------------------------------------------------
@@ -656,6 +710,10 @@ hipError_t launch_norms_finalize(DevMat* m, LaunchList L, int nblk, float pp_eps
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st) {
   if (ns_t == DT_BF16) LAUNCH(k_prologue<__bf16>, nblk, m, L, use_xn);
   else LAUNCH(k_prologue<float>, nblk, m, L, use_xn);
+  return hipGetLastError();
+}
+hipError_t launch_prologue_direct(const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st) {
+  LAUNCH(k_prologue_direct, nblk, m, L, use_xn);
   return hipGetLastError();
 }
 hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, int fin, float pp_eps,
