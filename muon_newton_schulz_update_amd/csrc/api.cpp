@@ -33,13 +33,12 @@
 namespace muon {
 
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
-                          int write_t, float ca, float cb, float cc, int variant, hipStream_t st);
+                          float ca, float cb, float cc, int variant, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  hipStream_t st);
 hipError_t launch_norms_finalize(DevMat* m, LaunchList L, int nblk, float pp_eps, float ns_eps, int init_power,
                                  hipStream_t st);
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st);
-hipError_t launch_prologue_direct(const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st);
 hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, int fin, float pp_eps, float pp_beta,
                                  hipStream_t st);
 hipError_t launch_aurora_scale(DevMat* m, LaunchList L, int nblk, float ns_eps, hipStream_t st);
@@ -94,8 +93,7 @@ struct Plan {
   bool any_aurora = false;
   // lists
   HostList stream, permat, matvec, rmatvec, ascale;
-  HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]: transposing prologue (tall or fp32)
-  HostList prologue_dir[2]; // [group]: bf16 wide/square sources, no transpose
+  HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
   HostList dupdate[2];      // [ns_t]
   GemmList gemm[2][2][3];   // [group][ns_t][mode]
   // device meta: DevMat array followed by the list arrays
@@ -267,27 +265,17 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
   add_list(meta, P->rmatvec, all, blocks);
   (void)bytes_stream;
 
-  auto direct_prologue = [](const MatInfo& m) { return m.ns_t == DT_BF16 && !m.tall; };
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < 2; ++g)
     for (int t = 0; t < 2; ++t) {
       std::vector<int> ms, bl;
       for (int i = 0; i < nm; ++i) {
         const MatInfo& m = P->mats[i];
-        if (m.ns_t != t || (g == 1 && !m.aurora) || direct_prologue(m)) continue;
+        if (m.ns_t != t || (g == 1 && !m.aurora)) continue;
         ms.push_back(i);
         bl.push_back((m.s_pad / 64) * (m.L_pad / 64));
       }
       add_list(meta, P->prologue[g][t], ms, bl);
     }
-    std::vector<int> ms, bl;
-    for (int i = 0; i < nm; ++i) {
-      const MatInfo& m = P->mats[i];
-      if ((g == 1 && !m.aurora) || !direct_prologue(m)) continue;
-      ms.push_back(i);
-      bl.push_back(cdiv(m.s_pad, kStreamRows) * cdiv(m.L_pad, kStreamCols));
-    }
-    add_list(meta, P->prologue_dir[g], ms, bl);
-  }
   for (int t = 0; t < 2; ++t) {
     std::vector<int> ms, bl;
     for (int i = 0; i < nm; ++i)
@@ -571,7 +559,7 @@ muon_status run(muon_handle* h, const Call& c) {
 
   // algorithmic byte counts for the profile
   double el_ns = 0, el_all = 0;
-  double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_pro_dir[2] = {0, 0};
+  double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}};
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
     const double el = (double)m.rows * m.cols;
@@ -581,16 +569,10 @@ muon_status run(muon_handle* h, const Call& c) {
     b_mom += upd ? el * (esz(d.dt_g) + 8 + esz(m.ns_t)) : el * esz(d.dt_g);
     b_tail_r += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? esz(d.dt_w) : 0));
     b_tail_a += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? 2 * esz(d.dt_w) : 0) + (d.uo ? esz(d.dt_uo) : 0));
-    // prologue bytes: read the source, write the iterate (and X^T for fp32)
-    const double wr = (m.ns_t == DT_BF16 ? 1.0 : 2.0) * m.s_pad * (double)m.L_pad * esz(m.ns_t);
-    const double pro = el * esz(m.ns_t) + wr;
-    if (m.ns_t == DT_BF16 && !m.tall) {
-      b_pro_dir[0] += pro;
-      if (m.aurora) b_pro_dir[1] += pro;
-    } else {
-      b_pro[0][m.ns_t] += pro;
-      if (m.aurora) b_pro[1][m.ns_t] += pro;
-    }
+    // prologue bytes: read the source, write the iterate and its transpose
+    const double pro = el * esz(m.ns_t) + 2.0 * m.s_pad * (double)m.L_pad * esz(m.ns_t);
+    b_pro[0][m.ns_t] += pro;
+    if (m.aurora) b_pro[1][m.ns_t] += pro;
   }
   (void)el_all;
 
@@ -640,11 +622,6 @@ muon_status run(muon_handle* h, const Call& c) {
       ProfScope ps(h, 1, b_pro[g][t]);
       CHECK_LAUNCH(h, launch_prologue(t, D, dev_list(*P, L), L.nblk, upd ? 1 : 0, st));
     }
-    if (P->prologue_dir[g].nblk > 0) {
-      ProfScope ps(h, 1, b_pro_dir[g]);
-      CHECK_LAUNCH(h, launch_prologue_direct(D, dev_list(*P, P->prologue_dir[g]), P->prologue_dir[g].nblk,
-                                             upd ? 1 : 0, st));
-    }
     for (int k = 0; k < cfg.ns_steps; ++k) {
       const int cur = k & 1;
       for (int mode = 0; mode < 3; ++mode)
@@ -652,10 +629,8 @@ muon_status run(muon_handle* h, const Call& c) {
           const GemmList& G = P->gemm[g][t][mode];
           if (G.n == 0) continue;
           ProfScope ps(h, 0, G.counted, G.executed);
-          // X'^T is needed after a pass's last iteration (D update, output)
-          const int write_t = k + 1 == cfg.ns_steps;
           CHECK_LAUNCH(h, launch_ns_gemm(t, D, (const TileItem*)((uint8_t*)P->meta_dev + G.off), G.n, mode, cur,
-                                         write_t, cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, st));
+                                         cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, st));
         }
     }
     if (p + 1 < P->passes) {

@@ -255,10 +255,9 @@ __global__ __launch_bounds__(256) void k_norms_finalize(DevMat* __restrict__ mat
 }
 
 // ---------------------------------------------------------------------------
-// NS prologue through an LDS transpose (tall sources, and fp32 sources):
-// X0 = scale * D o T in the wide orientation, written to x[0] (s_pad x L_pad)
-// and, for fp32 (whose BX reads it), its transpose to xt[0] (L_pad x s_pad),
-// zero padded. T is the source in storage orientation (rows x cols); for a
+// NS prologue through an LDS transpose: X0 = scale * D o T in the wide
+// orientation, written to x[0] (s_pad x L_pad) and its transpose to xt[0]
+// (L_pad x s_pad), zero padded (the first iteration's products read both). T is the source in storage orientation (rows x cols); for a
 // tall source the wide iterate is its transpose. 64 x 64 tiles over the
 // padded storage frame.
 // ---------------------------------------------------------------------------
@@ -301,7 +300,7 @@ __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mat
       v[e] *= d;
       tile[i][j + e] = v[e];
     }
-    if (sizeof(T) == 4) store8(dir, odt, ld_dir, r, c, c + 8, true, v);   // bf16 iterates keep no X^T
+    store8(dir, odt, ld_dir, r, c, c + 8, true, v);
   }
   __syncthreads();
 #pragma unroll
@@ -647,48 +646,6 @@ __global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ m
   }
 }
 
-// NS prologue without a transpose (bf16 wide or square sources, whose
-// iterate is the source itself): x[0] = scale * D o source over the padded
-// frame s_pad x L_pad, zero outside rows x cols. Tiles of kStreamRows x
-// kStreamCols; a lane owns 8 consecutive columns.
-__global__ __launch_bounds__(256) void k_prologue_direct(const DevMat* __restrict__ mats, LaunchList L, int use_xn) {
-  int local;
-  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  const int nct = (M.L_pad + kStreamCols - 1) / kStreamCols;
-  const int tr = local / nct, tc = local % nct;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = tc * kStreamCols + w * kSegCols + lane * 8;
-  if (c >= M.L_pad) return;
-  const int r0 = tr * kStreamRows, r1 = min(r0 + kStreamRows, M.s_pad);
-  const void* src = use_xn ? (const void*)M.xn : M.g;
-  const int64_t lds = use_xn ? (int64_t)M.cols : M.ld_g;
-  const int sdt = use_xn ? M.ns_t : M.dt_g;
-  const bool vs = aligned16(src, lds, sdt);
-  const float scale = M.scal[SC_SCALE];
-  float d[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) d[e] = (M.aurora && c + e < M.cols) ? scale * M.dvec[c + e] : scale;
-  for (int r = r0; r < r1; r += kRB) {
-    float v[kRB][8];
-#pragma unroll
-    for (int k = 0; k < kRB; ++k) {
-      if (r + k < M.rows) load8(src, sdt, lds, r + k, c, M.cols, vs, v[k]);   // zero past cols
-      else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kRB; ++k) {
-      if (r + k < r1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[k][e] *= d[e];
-        store8(M.x[0], DT_BF16, M.L_pad, r + k, c, c + 8, true, v[k]);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Host-side launchers (grid sizes come from the planner's LaunchList).
 // ---------------------------------------------------------------------------
@@ -710,10 +667,6 @@ hipError_t launch_norms_finalize(DevMat* m, LaunchList L, int nblk, float pp_eps
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st) {
   if (ns_t == DT_BF16) LAUNCH(k_prologue<__bf16>, nblk, m, L, use_xn);
   else LAUNCH(k_prologue<float>, nblk, m, L, use_xn);
-  return hipGetLastError();
-}
-hipError_t launch_prologue_direct(const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st) {
-  LAUNCH(k_prologue_direct, nblk, m, L, use_xn);
   return hipGetLastError();
 }
 hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, int fin, float pp_eps,
