@@ -1,6 +1,6 @@
 """Benchmark of one Muon optimizer step (Aurora + Contra-Muon + u/w-floor).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--recipe aurora|classic] [--gpus 1]
 
 A step is one libmuon `muon_update` over the whole matrix batch of the
 workload (default: every matrix of the 28-layer 3.8B-style decoder, 168
@@ -9,7 +9,8 @@ resident in HBM, momentum and weights updated in place. Prints one JSON line.
 
 value = counted Newton-Schulz TFLOP/s of the whole step (4 s^2 L + 2 s^3 per
 iteration per matrix, s <= L, 12 iterations, 2 passes for non-square
-matrices) = counted flops / step time. `roofline` reports the matrix-core
+matrices; 5 iterations and one pass with --recipe classic) = counted flops /
+step time. `roofline` reports the matrix-core
 kernels alone (summed HIP-event time of their launches on the library's
 stream, over the timed steps) against the bf16 dense peak; `cpu_baseline`
 times the float64 oracle on a bounded sample of the same workload.
@@ -27,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "Aurora-Muon optimizer-step ms & MFMA TFLOP/s (% peak), 3.8B bf16 matrix set"
+METRIC_CLASSIC = "Classic Muon (NS5) optimizer-step ms & MFMA TFLOP/s (% peak), 3.8B bf16 matrix set"
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 matrix-core peak
 PEAK_FP32_TFLOPS = 157.3
 
@@ -86,11 +88,13 @@ def cpu_baseline(name: str, grads, moms, weights, cfg, budget_s: float) -> dict:
         dt = time.perf_counter() - t0
         t_total += dt
         flops += step_flops([tuple(grads[i].shape)], cfg)
-        done.append(f"{tuple(grads[i].shape)}")
+        done.append(tuple(grads[i].shape))
         if t_total >= budget_s:
             break
+    from collections import Counter
+    kinds = ", ".join(f"{n} x {r}x{c}" for (r, c), n in Counter(done).items())
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(done)} matrices of {name} ({', '.join(done)}), float64 numpy, "
+            "sample": f"{len(done)} matrices of {name} ({kinds}), smallest first, float64 numpy, "
                       f"{t_total:.1f} s"}
 
 
@@ -100,6 +104,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3p8b_all_layers")
+    ap.add_argument("--recipe", default="aurora", choices=["aurora", "classic"],
+                    help="aurora: the Aurora + Contra + floor step (the headline metric); classic: the "
+                         "five-step Muon recipe (momentum after its warm-up, NS5, no Aurora/Contra/floor)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-launch event timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -122,7 +129,7 @@ def main() -> int:
         return 2
     dev = torch.device("cuda:0")
     w = gen.WORKLOADS[a.workload]
-    cfg = mu.make_config(**dict(w.config))
+    cfg = mu.make_config(a.recipe, **dict(w.config))
     log(f"[bench] generating {a.workload}: {len(w.shapes)} matrices")
     grads, moms, weights = gen.make_batch(a.workload, dev)
     torch.cuda.synchronize()
@@ -174,7 +181,7 @@ def main() -> int:
     ms_per_step = ms_ev / a.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     out = {
-        "metric": METRIC,
+        "metric": METRIC if a.recipe == "aurora" else METRIC_CLASSIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -186,7 +193,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.grad_dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": {"workload": a.workload, "matrices": len(shapes), "matrix_params": params,
+        "config": {"workload": a.workload, "recipe": a.recipe, "matrices": len(shapes), "matrix_params": params,
                    "counted_ns_tflop_per_step": round(flops / 1e12, 3),
                    "matrix_params_per_s": round(params / (ms_per_step * 1e-3), 1),
                    "pct_bf16_peak_whole_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -197,8 +204,10 @@ def main() -> int:
         peak = PEAK_BF16_TFLOPS if w.grad_dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
         out["roofline"] = {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": measured_traffic(a.workload),
-            "kernel": "k_ns_gemm (Gram, B = bA + cA^2, X = aX + BX launches together)",
+            "frac": round(achieved / peak, 4),
+            # the byte-counter record was taken on the Aurora step's launches
+            "traffic": measured_traffic(a.workload) if a.recipe == "aurora" else None,
+            "kernel": "k_ns_gemm (A = XX^T, B' = bA + cA^2 + aI, X' = B'X launches together)",
             "launches": int(p["gemm_launches"]),
             "avg_launch_ms": round(p["gemm_ms"] / p["gemm_launches"], 4),
             "executed_tflops": round(p["gemm_executed_flop"] / (p["gemm_ms"] * 1e-3) / 1e12, 2),

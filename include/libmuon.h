@@ -124,6 +124,26 @@ typedef struct muon_handle muon_handle;
 /* Fill *cfg with the page's locked values (listed above). cfg must not be NULL. */
 void muon_config_default(muon_config* cfg);
 
+/*
+ * Fill *cfg with the classic Muon recipe of the Track-1 record page
+ * (§"训练管线与系统实现"): Nesterov momentum 0.95, Newton-Schulz with
+ * (ns_a, ns_b, ns_c) = (3.4445, -4.7750, 2.0315) for ns_steps 5, no Aurora
+ * preconditioner (pp_iterations 0), no Contra term (contra 0), no u/w-floor
+ * (target_uw 0), the sqrt(max(1, rows/cols)) scale, lr 0.04. The remaining
+ * fields keep muon_config_default's values. cfg must not be NULL.
+ * That recipe's fixed point is deliberately not 1, so its update is not an
+ * exact orthogonalisation.
+ */
+void muon_config_classic(muon_config* cfg);
+
+/*
+ * Momentum warm-up of the same page: frac = min(step / warmup_steps, 1),
+ * mu = (1 - frac) * mu_start + frac * mu_end (the page uses 0.85 -> 0.95
+ * over 500 steps). A host-side scalar for muon_config.mu; step < 0 counts as
+ * 0, warmup_steps <= 0 returns mu_end. Computed in double, returned as float.
+ */
+float muon_momentum_warmup(int64_t step, float mu_start, float mu_end, int64_t warmup_steps);
+
 /* Static text for a status code. Never NULL. */
 const char* muon_status_string(muon_status s);
 

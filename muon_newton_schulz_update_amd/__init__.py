@@ -24,7 +24,7 @@ import torch  # loaded first so libmuon binds to the HIP runtime torch already m
 
 __all__ = [
     "MuonConfig", "MuonProfile", "LibMuonError", "Handle", "load_library",
-    "library_path", "default_config", "make_config", "ns_polar",
+    "library_path", "default_config", "classic_config", "momentum_warmup", "make_config", "ns_polar",
     "aurora_orthogonalize", "muon_update", "check_update_args",
     "check_polar_args", "get_handle", "STATUS",
 ]
@@ -99,6 +99,9 @@ def load_library() -> ctypes.CDLL:
         P = ctypes.POINTER
         sig = {
             "muon_config_default": (None, [P(MuonConfig)]),
+            "muon_config_classic": (None, [P(MuonConfig)]),
+            "muon_momentum_warmup": (ctypes.c_float, [ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                                      ctypes.c_int64]),
             "muon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "muon_version": (ctypes.c_char_p, []),
             "muon_create": (ctypes.c_int, [P(ctypes.c_void_p), ctypes.c_void_p]),
@@ -136,9 +139,28 @@ def default_config() -> MuonConfig:
     return cfg
 
 
-def make_config(**overrides) -> MuonConfig:
-    """Defaults (the page's locked values) with keyword overrides."""
-    cfg = default_config()
+def classic_config() -> MuonConfig:
+    """The classic five-step Muon recipe (muon_config_classic)."""
+    cfg = MuonConfig()
+    load_library().muon_config_classic(ctypes.byref(cfg))
+    return cfg
+
+
+def momentum_warmup(step: int, mu_start: float = 0.85, mu_end: float = 0.95, warmup_steps: int = 500) -> float:
+    """Host-side momentum warm-up of the classic recipe (muon_momentum_warmup)."""
+    return float(load_library().muon_momentum_warmup(int(step), float(mu_start), float(mu_end),
+                                                     int(warmup_steps)))
+
+
+def make_config(recipe: str = "aurora", **overrides) -> MuonConfig:
+    """A recipe's values ("aurora": the page's locked values, the default;
+    "classic": the five-step Muon recipe) with keyword overrides."""
+    if recipe == "aurora":
+        cfg = default_config()
+    elif recipe == "classic":
+        cfg = classic_config()
+    else:
+        raise ValueError(f"unknown recipe {recipe!r}")
     for k, v in overrides.items():
         if k not in dict(MuonConfig._fields_):
             raise KeyError(f"unknown config field {k!r}")

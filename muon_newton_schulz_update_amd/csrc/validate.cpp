@@ -161,6 +161,30 @@ extern "C" void muon_config_default(muon_config* c) {
   c->flags = 0;
 }
 
+// Classic recipe of the Track-1 record page, §"训练管线与系统实现".
+extern "C" void muon_config_classic(muon_config* c) {
+  if (!c) return;
+  muon_config_default(c);
+  c->ns_steps = 5;
+  c->ns_a = 3.4445f;
+  c->ns_b = -4.7750f;
+  c->ns_c = 2.0315f;
+  c->pp_iterations = 0;
+  c->contra = 0.0f;
+  c->target_uw = 0.0f;
+  c->mu = 0.95f;
+  c->nesterov = 1;
+  c->lr = 0.04f;
+}
+
+// Linear momentum warm-up of the same page: frac = min(step / n, 1).
+extern "C" float muon_momentum_warmup(int64_t step, float mu_start, float mu_end, int64_t warmup_steps) {
+  if (warmup_steps <= 0) return mu_end;
+  const double s = step < 0 ? 0.0 : (double)step;
+  const double frac = s >= (double)warmup_steps ? 1.0 : s / (double)warmup_steps;
+  return (float)((1.0 - frac) * (double)mu_start + frac * (double)mu_end);
+}
+
 extern "C" const char* muon_status_string(muon_status s) {
   switch (s) {
     case MUON_OK: return "MUON_OK";

@@ -51,6 +51,7 @@ import numpy as np
 __all__ = [
     "OracleConfig", "ns_poly", "newton_schulz", "aurora_orthogonalize",
     "power_sigma", "momentum_nesterov", "muon_update", "ns5_classic",
+    "classic_config", "momentum_warmup",
 ]
 
 
@@ -262,3 +263,27 @@ def ns5_classic(G, steps=5, a=3.4445, b=-4.7750, c=2.0315, eps=1e-7):
     Track-1 page; its fixed point is deliberately not 1 (p(1) != 1).
     """
     return newton_schulz(G, steps, a, b, c, eps)
+
+
+def classic_config() -> OracleConfig:
+    """The classic recipe as one OracleConfig ([Track-1 page]).
+
+    Muon on every 2-D matrix with lr 0.04, Nesterov momentum 0.95 (warmed up,
+    see `momentum_warmup`), five NS iterations with the page's (a, b, c), the
+    sqrt(max(1, rows / cols)) scale; none of Aurora's preconditioner, the
+    Contra term or the u/w-floor (pp_iterations 0, contra 0, target_uw 0;
+    reading R5).
+    """
+    return OracleConfig(ns_steps=5, ns_a=3.4445, ns_b=-4.7750, ns_c=2.0315,
+                        pp_iterations=0, mu=0.95, nesterov=True, contra=0.0,
+                        target_uw=0.0, lr=0.04)
+
+
+def momentum_warmup(step, mu_start=0.85, mu_end=0.95, warmup_steps=500):
+    """Momentum at a given step ([Track-1 page]): over the first 500 steps the
+    coefficient moves linearly from 0.85 to 0.95 (frac = min(step / 500, 1),
+    mu = (1 - frac) 0.85 + frac 0.95), then stays at 0.95."""
+    if warmup_steps <= 0:
+        return float(mu_end)
+    frac = min(max(step, 0) / warmup_steps, 1.0)
+    return (1.0 - frac) * mu_start + frac * mu_end

@@ -141,3 +141,29 @@ def test_null_handle_is_rejected(lib):
     assert lib.ns_polar(None, 0, None, None, None) == INVALID
     assert lib.muon_update(None, 0, None, None, None, None, None) == INVALID
     assert lib.muon_destroy(None) == OK
+
+
+def test_classic_config_equals_page_values(lib):
+    c = mu.classic_config()
+    k, n = PAGE["classic_recipe"], PAGE["ns5_classic"]
+    assert c.ns_steps == n["steps"]
+    assert (c.ns_a, c.ns_b, c.ns_c) == pytest.approx((n["a"], n["b"], n["c"]), rel=1e-7)
+    assert c.lr == pytest.approx(k["lr"], rel=1e-7)
+    assert c.mu == pytest.approx(k["mu"], rel=1e-7)
+    assert c.nesterov == 1
+    assert (c.pp_iterations, c.contra, c.target_uw) == (0, 0.0, 0.0)
+    # everything else keeps the default values
+    d = mu.default_config()
+    for f in ("ns_eps", "pp_beta", "pp_eps", "power_steps", "flags"):
+        assert getattr(c, f) == getattr(d, f), f
+    assert mu.make_config("classic", lr=0.02).lr == pytest.approx(0.02)
+
+
+def test_momentum_warmup_host_function(lib):
+    w = PAGE["classic_recipe"]["warmup"]
+    for s in (-3, 0, 1, 137, 250, 499, 500, 501, 10 ** 9):
+        frac = min(max(s, 0) / w["steps"], 1.0)
+        want = (1 - frac) * w["mu_start"] + frac * w["mu_end"]
+        got = lib.muon_momentum_warmup(s, w["mu_start"], w["mu_end"], w["steps"])
+        assert got == pytest.approx(want, abs=1e-7), s
+    assert lib.muon_momentum_warmup(5, 0.85, 0.95, 0) == pytest.approx(0.95)

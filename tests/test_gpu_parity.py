@@ -265,6 +265,21 @@ def test_update_options(dev, opt):
     check_update(opt, G[0], M0[0], W0[0], M[0], V[0], W[0], cfg, FP32_TOL)
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, FP32_TOL), (torch.bfloat16, BF16_TOL)])
+def test_update_classic_recipe(dev, dtype, tol):
+    """The classic five-step Muon recipe through muon_update: momentum from
+    the warm-up at step 123, NS5, sqrt(max(1, rows/cols)), lr 0.04, no
+    Aurora, Contra or floor."""
+    say(f"muon_update classic recipe {dtype}")
+    cfg = mu.make_config("classic", mu=mu.momentum_warmup(123))
+    shapes = [(384, 128), (128, 384), (256, 256), (300, 77)]
+    mats = [gen.custom_matrix(s, 1300 + i, dev, grad_dtype=dtype, grad_sd=1e-3, mom_sd=1e-3, weight_dtype=dtype)
+            for i, s in enumerate(shapes)]
+    G, M0, W0, M, V, W = run_update(dev, mats, cfg)
+    for i in range(len(shapes)):
+        check_update(f"classic[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], cfg, tol)
+
+
 def test_update_zero_and_empty(dev):
     say("muon_update zero and empty matrices")
     z = torch.zeros((64, 200), device=dev)

@@ -5,6 +5,7 @@ it with an independent route (an SVD closed form, a special case whose answer
 is known, an invariant, or a constant printed on the pages), chosen so that a
 wrong coefficient, sign, index, orientation or step order fails at least one.
 """
+import dataclasses
 import json
 import math
 import os
@@ -339,3 +340,48 @@ def test_zero_inputs():
     Mn, V, Wn = O.muon_update(Z, Z, W)
     assert not np.any(Mn) and not np.any(V) and np.array_equal(Wn, W)
     assert np.all(np.isfinite(V))
+
+
+# --------------------------------------------------------------------------
+# Classic five-step recipe (Track-1 page)
+# --------------------------------------------------------------------------
+
+def test_classic_config_matches_page():
+    k, n = PAGE["classic_recipe"], PAGE["ns5_classic"]
+    c = O.classic_config()
+    assert (c.ns_steps, c.ns_a, c.ns_b, c.ns_c) == (n["steps"], n["a"], n["b"], n["c"])
+    assert (c.lr, c.mu, c.nesterov) == (k["lr"], k["mu"], k["nesterov"])
+    # no Aurora preconditioner, no Contra term, no u/w-floor
+    assert (c.pp_iterations, c.contra, c.target_uw) == (0, 0.0, 0.0)
+
+
+def test_momentum_warmup_points_and_linearity():
+    w = PAGE["classic_recipe"]["warmup"]
+
+    def f(s):
+        return O.momentum_warmup(s, w["mu_start"], w["mu_end"], w["steps"])
+
+    assert f(0) == w["mu_start"] and f(-7) == w["mu_start"]
+    assert f(w["steps"]) == w["mu_end"] and f(10 ** 7) == w["mu_end"]
+    assert f(w["steps"] // 2) == pytest.approx(0.5 * (w["mu_start"] + w["mu_end"]), abs=1e-15)
+    ys = np.array([f(s) for s in range(0, w["steps"] + 1)])
+    assert np.all(np.diff(ys) > 0)                     # increasing over the warm-up
+    assert np.max(np.abs(np.diff(ys, 2))) < 1e-15      # and linear
+    assert O.momentum_warmup(3, 0.85, 0.95, 0) == 0.95
+
+
+@pytest.mark.parametrize("shape", [(96, 40), (40, 96), (64, 64)])
+def test_classic_update_closed_form(shape):
+    """Classic step = Nesterov blend -> NS5 (SVD closed form) -> sqrt(max(1,
+    rows/cols)) -> W - lr V, with no further rescaling."""
+    rng = np.random.default_rng(11)
+    G, M, W = (rng.standard_normal(shape) for _ in range(3))
+    cfg = dataclasses.replace(O.classic_config(), mu=O.momentum_warmup(123))
+    M1, V, W1 = O.muon_update(G, M, W, cfg)
+    Mw = M + (1.0 - cfg.mu) * (G - M)
+    X = G + cfg.mu * (Mw - G)
+    k = PAGE["ns5_classic"]
+    want = svd_ns(X, steps=k["steps"], coeffs=(k["a"], k["b"], k["c"])) * math.sqrt(max(1.0, shape[0] / shape[1]))
+    assert rel(M1, Mw) < 1e-14
+    assert rel(V, want) < 1e-10
+    assert rel(W1, W - PAGE["classic_recipe"]["lr"] * want) < 1e-12
