@@ -124,6 +124,17 @@ def test_config_validation(lib, field, value):
     assert rc == INVALID, (field, value, rc, msg)
 
 
+@pytest.mark.parametrize("rows,cols,code", [
+    (16384, 65536, OK), (65536, 16384, OK), (1, 65536, OK), (65536, 1, OK),
+    (16385, 65536, SHAPE), (16384, 65537, SHAPE), (65537, 1, SHAPE), (16385, 16385, SHAPE),
+])
+def test_size_limits_at_the_boundary(lib, rows, cols, code):
+    rc, msg = mu.check_update_args([m(rows, cols)], [m(rows, cols, 0)], None, None)
+    assert rc == code, (rows, cols, rc, msg)
+    rc, msg = mu.check_polar_args([m(rows, cols)], [m(rows, cols)])
+    assert rc == code, (rows, cols, rc, msg)
+
+
 def test_polar_validation(lib):
     assert mu.check_polar_args([m(5, 3)], [m(5, 3, 0)])[0] == OK
     assert mu.check_polar_args([m(5, 3)], [m(3, 5)])[0] == SHAPE

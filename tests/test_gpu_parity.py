@@ -280,6 +280,55 @@ def test_update_classic_recipe(dev, dtype, tol):
         check_update(f"classic[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], cfg, tol)
 
 
+# ---------------------------------------------------------------------------
+# size limits: long side 65536, short side 16384, 2^30 elements
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,dtype,tol", [((256, 65536), torch.bfloat16, BF16_TOL),
+                                             ((65536, 256), torch.float32, FP32_TOL)])
+def test_update_max_long_side(dev, shape, dtype, tol):
+    """The full step at the longest side the library accepts, dense random
+    inputs, every element checked against the oracle."""
+    say(f"muon_update at the long-side limit {shape} {dtype}")
+    mats = [gen.custom_matrix(shape, 1400, dev, grad_dtype=dtype, grad_sd=1e-3, mom_sd=1e-3, weight_dtype=dtype)]
+    G, M0, W0, M, V, W = run_update(dev, mats)
+    check_update("max_long", G[0], M0[0], W0[0], M[0], V[0], W[0], mu.default_config(), tol, ROW_TOL)
+
+
+def test_ns_polar_max_short_side_and_elements(dev):
+    """ns_polar on a 16384 x 65536 bf16 matrix (short-side limit, 2^30
+    elements) with one nonzero v_i per row in distinct columns: X = D P with
+    D diagonal and P a partial permutation, so every Gram is diagonal and the
+    exact result keeps the support, with values sign(v_i) p^12(|v_i| / (||v|| + 1e-7))."""
+    rows, cols = 16384, 65536
+    say(f"ns_polar at the short-side / element limit {rows}x{cols} bf16")
+    gcpu = torch.Generator().manual_seed(1500)
+    col = torch.randperm(cols, generator=gcpu)[:rows]
+    mag = torch.pow(10.0, -3.0 * torch.rand(rows, generator=gcpu, dtype=torch.float64))
+    sgn = torch.where(torch.rand(rows, generator=gcpu) < 0.5, -1.0, 1.0).double()
+    v = (sgn * mag).to(torch.bfloat16)                      # stored values are the ground truth
+    x = torch.zeros((rows, cols), device=dev, dtype=torch.bfloat16)
+    ridx = torch.arange(rows, device=dev)
+    x[ridx, col.to(dev)] = v.to(dev)
+    out = torch.empty_like(x)
+    mu.ns_polar([x], [out])
+    torch.cuda.synchronize()
+    del x
+    # support kept exactly
+    nz = int(torch.count_nonzero(out))
+    got = out[ridx, col.to(dev)].double().cpu().numpy()
+    assert nz == rows and bool((got != 0).all()), nz
+    # closed form on the support
+    vv = v.double().numpy()
+    t = np.abs(vv) / (np.linalg.norm(vv) + 1e-7)
+    for _ in range(12):
+        t = 2.0 * t - 1.5 * t ** 3 + 0.5 * t ** 5
+    want = np.sign(vv) * t
+    e_f = rel(got, want)
+    e_max = float(np.max(np.abs(got - want) / np.abs(want)))
+    say(f"  rel(Frobenius)={e_f:.2e} max elementwise rel={e_max:.2e}")
+    assert e_f <= BF16_TOL and e_max <= 5e-2
+
+
 def test_update_zero_and_empty(dev):
     say("muon_update zero and empty matrices")
     z = torch.zeros((64, 200), device=dev)
