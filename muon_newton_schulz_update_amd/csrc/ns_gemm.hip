@@ -186,10 +186,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
       (uint32_t)(((int64_t)(16 * wave + (lane >> 2)) * ld + ((lane & 3) ^ ((lane >> 4) & 3)) * CPR) * sizeof(T));
   const int rstep = (int)((int64_t)16 * NW * ld * sizeof(T));
   // Buffer resources over the two operand panels, range-checked: a read
-  // beyond the panel returns zeros instead of touching other memory.
+  // beyond the panel returns zeros instead of touching other memory. On a
+  // diagonal tile of the two symmetric products both operands are the same
+  // panel: the second resource gets no records, so its loads fetch nothing
+  // (the issue count, and with it every wait, stays the same), and both
+  // operands' fragments are read from the first panel's stage.
   const int ext = (int)((int64_t)kTile * ld * sizeof(T));
+  const bool same = (mode != GM_BX) && (it.tm == it.tn);
+  const uint32_t qsel = same ? 0u : (uint32_t)kOpBytes;   // LDS offset of the second operand
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void*)P, (short)0, ext, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Q, (short)0, ext, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Q, (short)0, same ? 0 : ext, 0x00020000);
 
   auto issue = [&](int slot, int ks) {
     uint8_t* sm = smem + slot * kStageBytes;
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
       fa[buf][mi] = *(const Frag*)(sm + (wm * MI * 32 + mi * 32 + lr) * kRowBytes + ph);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
-      fb[buf][ni] = *(const Frag*)(sm + kOpBytes + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
+      fb[buf][ni] = *(const Frag*)(sm + qsel + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
   };
   auto mfmas = [&](int buf) {
     if constexpr (sizeof(T) == 2) {
