@@ -25,8 +25,8 @@
 // for them); four stages stream in while one feeds the matrix cores. Inside a
 // stage the second half's fragments are read between the first half's MFMAs;
 // the workgroup barrier sits between the halves, so matrix-core work
-// continues across it, and the next stage's first fragments and the refill
-// of the freed slot are issued between the second half's MFMAs. LDS rows are
+// continues across it, and the refill of the freed slot and the next stage's
+// first fragments are issued between the second half's MFMAs. LDS rows are
 // XOR-swizzled in 16-byte chunks so fragment reads are conflict-free.
 // bf16 runs v_mfma_f32_32x32x16_bf16 (fp32 accumulation); fp32 runs
 // v_mfma_f32_32x32x2f32 on the same tiles.
@@ -270,16 +270,24 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
     wait_vm<(S - 2) * kLoads>();
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // second half: the next stage's first fragments and the refill of slot u
-    // with stage k+S are issued between the MFMAs
-    read_frags(un, 0, 0);
+    // second half: the refill of slot u with stage k+S (longest latency
+    // first), then the next stage's first fragments, spread evenly between
+    // the MFMAs in that order (the compiler cannot tell the refill and the
+    // reads apart, so the pattern keeps their program order)
     issue(u, min(k + S, nk - 1));
+    read_frags(un, 0, 0);
     mfmas(1);
+    {
+      constexpr int nmem = kLoads + kReadHalf;
 #pragma unroll
-    for (int q = 0; q < kMfmaHalf; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < kReadHalf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (q < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct load
+      for (int q = 0; q < kMfmaHalf; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+#pragma unroll
+        for (int t = q * nmem / kMfmaHalf; t < (q + 1) * nmem / kMfmaHalf; ++t) {
+          if (t < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct load
+          else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // one LDS read
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     u = un;
