@@ -19,15 +19,18 @@
 // wave's stalls on the in-order issue of memory instructions); a 4-wave
 // layout (2 x 2 waves of 128 x 128) is kept for tuning.
 //
-// K advances 64 bytes per tile row per stage (32 bf16 or 16 fp32). A ring of
-// five 32 KB LDS stages is filled by buffer-form direct global->LDS loads
-// (they count on vmcnt only, so waits on LDS fragment reads do not also wait
-// for them); four stages stream in while one feeds the matrix cores. Inside a
-// stage the second half's fragments are read between the first half's MFMAs;
-// the workgroup barrier sits between the halves, so matrix-core work
-// continues across it, and the refill of the freed slot and the next stage's
-// first fragments are issued between the second half's MFMAs. LDS rows are
-// XOR-swizzled in 16-byte chunks so fragment reads are conflict-free.
+// K advances 128 bytes per tile row per stage (64 bf16 or 32 fp32), so each
+// direct-load request covers whole 128-byte lines. The LDS holds five 32 KB
+// operand slots, filled by buffer-form direct global->LDS loads (they count
+// on vmcnt only, so waits on LDS fragment reads do not also wait for them);
+// stage k's two operands occupy slots 2k and 2k+1 (mod 5), so while one
+// stage feeds the matrix cores the next stage and half of the one after
+// stream in. A stage is four k-steps; each step's fragments are read between
+// the previous step's MFMAs. The workgroup barrier sits before the last step,
+// so matrix-core work continues across it, and the refill of the two freed
+// slots and the next stage's first fragments are issued between that last
+// step's MFMAs. LDS rows are XOR-swizzled in 16-byte chunks so fragment reads
+// are conflict-free.
 // bf16 runs v_mfma_f32_32x32x16_bf16 (fp32 accumulation); fp32 runs
 // v_mfma_f32_32x32x2f32 on the same tiles.
 #include <hip/hip_runtime.h>
@@ -46,9 +49,8 @@ typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 
 namespace {
 
-constexpr int kRowBytes = 64;                  // K bytes per tile row per stage
-constexpr int kOpBytes = kTile * kRowBytes;    // 16 KB per operand per stage
-constexpr int kStageBytes = 2 * kOpBytes;      // 32 KB
+constexpr int kRowBytes = 128;                 // K bytes per tile row per stage
+constexpr int kOpBytes = kTile * kRowBytes;    // 32 KB: one operand of one stage (one LDS slot)
 constexpr int kPitch = 132;                    // floats per staged epilogue row (128 + 4 spreads banks)
 constexpr int kSlabBytes = 32 * kPitch * 4;    // one wave's 32 x 128 staging slab
 
@@ -130,14 +132,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
   constexpr int NW = WM * WN;                // waves per workgroup
   constexpr int MI = kTile / WM / 32;        // 32x32 blocks per wave, down
   constexpr int NI = kTile / WN / 32;        // 32x32 blocks per wave, across
-  constexpr int LPW = 16 / NW;               // direct loads per wave per operand per stage
-  constexpr int kLoads = 2 * LPW;            // direct loads per wave per stage
-  constexpr int kMfmaHalf = MI * NI * (sizeof(T) == 2 ? 1 : 4);   // MFMAs per stage half
-  constexpr int kReadHalf = MI + NI;                              // LDS reads per stage half
-  // the ring; after the K loop the same memory stages the epilogue
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * kStageBytes];
-  static_assert(S * kStageBytes >= NW * kSlabBytes, "epilogue staging fits in the ring");
-  static_assert(S >= 3 && (S - 1) * kLoads < 64, "ring depth");
+  constexpr int LPO = 32 / NW;               // direct loads per wave per operand per stage
+  constexpr int kMfmaStep = MI * NI * (sizeof(T) == 2 ? 1 : 4);   // MFMAs per k-step
+  constexpr int kReadStep = MI + NI;                              // LDS reads per k-step
+  // S operand slots; after the K loop the same memory stages the epilogue
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * kOpBytes];
+  static_assert(S * kOpBytes >= NW * kSlabBytes, "epilogue staging fits in the slots");
+  static_assert(S >= 4 && (S - 2) * LPO < 64, "slot count");
 
   const int b = blockIdx.x;
   const int xcd = b & 7, j = b >> 3;
@@ -175,54 +176,55 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = (f32x16_t){};
 
   constexpr int KE = kRowBytes / sizeof(T);   // K elements per stage
-  const int nk = K / KE;                      // K is a multiple of 256: nk >= 8
+  const int nk = K / KE;                      // K is a multiple of 256: nk >= 4
   constexpr int CPR = Elem<T>::kPerChunk;
-  // Direct loads: one wave instruction fills one 1 KB group of 16 tile rows;
-  // wave w's load i fills group g = NW i + w, lane p fetching row 16 g + p/4,
-  // physical chunk p%4 of it. Physical chunk c' of row r holds logical chunk
-  // c' ^ ((r >> 2) & 3); for these rows that term is (p / 16) % 4, so a lane
-  // needs one 32-bit byte offset for the whole K loop.
-  const uint32_t lane_off =
-      (uint32_t)(((int64_t)(16 * wave + (lane >> 2)) * ld + ((lane & 3) ^ ((lane >> 4) & 3)) * CPR) * sizeof(T));
-  const int rstep = (int)((int64_t)16 * NW * ld * sizeof(T));
+  // Direct loads: one wave instruction fills one 1 KB group of 8 tile rows;
+  // wave w's load i fills group g = NW i + w, lane p fetching row 8 g + p/8,
+  // physical chunk p%8 of it. Physical chunk c' of row r holds logical chunk
+  // c' ^ ((r >> 1) & 7); for these rows that term is (4 w + p/16) % 8, so a
+  // lane needs one 32-bit byte offset for the whole K loop.
+  const int prow = 8 * wave + (lane >> 3);
+  const uint32_t lane_off = (uint32_t)(((int64_t)prow * ld + ((lane & 7) ^ ((prow >> 1) & 7)) * CPR) * sizeof(T));
+  const int rstep = (int)((int64_t)8 * NW * ld * sizeof(T));
   // Buffer resources over the two operand panels, range-checked: a read
   // beyond the panel returns zeros instead of touching other memory. On a
   // diagonal tile of the two symmetric products both operands are the same
   // panel: the second resource gets no records, so its loads fetch nothing
   // (the issue count, and with it every wait, stays the same), and both
-  // operands' fragments are read from the first panel's stage.
+  // operands' fragments are read from the first panel's slot.
   const int ext = (int)((int64_t)kTile * ld * sizeof(T));
   const bool same = (mode != GM_BX) && (it.tm == it.tn);
-  const uint32_t qsel = same ? 0u : (uint32_t)kOpBytes;   // LDS offset of the second operand
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void*)P, (short)0, ext, 0x00020000);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Q, (short)0, same ? 0 : ext, 0x00020000);
 
-  auto issue = [&](int slot, int ks) {
-    uint8_t* sm = smem + slot * kStageBytes;
+  // Operand stage o is P (o even) or Q (o odd) of stage o/2; it goes to
+  // slot o % S. Stages past the end of K are clamped to the last one: an
+  // L2-resident re-read into a slot nobody reads again, which keeps every
+  // wait below the same.
+  auto issue = [&](int slot, int o) {
+    const int ks = min(o >> 1, nk - 1);
+    uint8_t* sm = smem + slot * kOpBytes;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, LDS_PTR(sm + (NW * i + wave) * 1024), 16, lane_off,
-                                               ks * kRowBytes + i * rstep, 0, 0);
-#pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_PTR(sm + kOpBytes + (NW * i + wave) * 1024), 16, lane_off,
-                                               ks * kRowBytes + i * rstep, 0, 0);
+    for (int i = 0; i < LPO; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((o & 1) ? rq : rp, LDS_PTR(sm + (NW * i + wave) * 1024), 16,
+                                               lane_off, ks * kRowBytes + i * rstep, 0, 0);
   };
 
   // Fragments: lane l reads tile row (block base + l%32), logical chunk
-  // 2 h + l/32 of the stage (8 bf16 or 4 fp32 consecutive k) for half h.
+  // 2 s + l/32 of the stage (8 bf16 or 4 fp32 consecutive k) for k-step s.
   typedef typename Elem<T>::Frag Frag;
   Frag fa[2][MI], fb[2][NI];
   const int lr = lane & 31;
-  auto read_frags = [&](int slot, int h, int buf) {
-    const uint8_t* sm = smem + slot * kStageBytes;
-    const int ph = ((2 * h + (lane >> 5)) ^ ((lr >> 2) & 3)) * 16;
+  auto read_frags = [&](int pslot, int qslot, int s, int buf) {
+    const uint8_t* sa = smem + pslot * kOpBytes;
+    const uint8_t* sb = same ? sa : smem + qslot * kOpBytes;
+    const int ph = ((2 * s + (lane >> 5)) ^ ((lr >> 1) & 7)) * 16;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
-      fa[buf][mi] = *(const Frag*)(sm + (wm * MI * 32 + mi * 32 + lr) * kRowBytes + ph);
+      fa[buf][mi] = *(const Frag*)(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes + ph);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
-      fb[buf][ni] = *(const Frag*)(sm + qsel + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
+      fb[buf][ni] = *(const Frag*)(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
   };
   auto mfmas = [&](int buf) {
     if constexpr (sizeof(T) == 2) {
@@ -243,57 +245,62 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][mi][e], fb[buf][ni][e], acc[mi][ni], 0, 0, 0);
     }
   };
-
-  // Prologue: fill the whole ring, wait for stage 0, read its first half.
-  // Refills past the end of K are clamped to the last stage: an L2-resident
-  // re-read into a slot nobody reads again, which keeps every wait below the
-  // same.
+  // Spread nmem memory instructions evenly between one k-step's MFMAs, the
+  // first nloads of them direct loads, the rest LDS reads. The compiler
+  // cannot tell the refill and the reads apart, so the pattern keeps their
+  // program order.
+  auto spread = [&](int nmem, int nloads) {
 #pragma unroll
-  for (int s = 0; s < S; ++s) issue(s, min(s, nk - 1));
-  wait_vm<(S - 1) * kLoads>();
-  ring_barrier();
-  read_frags(0, 0, 0);
-  int u = 0;
-  for (int k = 0; k < nk - 1; ++k) {
-    const int un = (u + 1 == S) ? 0 : u + 1;
-    // first half: this stage's second fragments are read between the MFMAs
-    read_frags(u, 1, 1);
-    mfmas(0);
-#pragma unroll
-    for (int q = 0; q < kMfmaHalf; ++q) {
+    for (int q = 0; q < kMfmaStep; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      if (q < kReadHalf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // stage k+1 has landed for every wave; slot u (stage k) is free
-    wait_lgkm0();
-    wait_vm<(S - 2) * kLoads>();
-    ring_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // second half: the refill of slot u with stage k+S (longest latency
-    // first), then the next stage's first fragments, spread evenly between
-    // the MFMAs in that order (the compiler cannot tell the refill and the
-    // reads apart, so the pattern keeps their program order)
-    issue(u, min(k + S, nk - 1));
-    read_frags(un, 0, 0);
-    mfmas(1);
-    {
-      constexpr int nmem = kLoads + kReadHalf;
 #pragma unroll
-      for (int q = 0; q < kMfmaHalf; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-#pragma unroll
-        for (int t = q * nmem / kMfmaHalf; t < (q + 1) * nmem / kMfmaHalf; ++t) {
-          if (t < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct load
-          else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // one LDS read
-        }
+      for (int t = q * nmem / kMfmaStep; t < (q + 1) * nmem / kMfmaStep; ++t) {
+        if (t < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct load
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // one LDS read
       }
     }
+  };
+
+  // Prologue: fill every slot, wait for stage 0, read its first k-step.
+#pragma unroll
+  for (int o = 0; o < S; ++o) issue(o, o);
+  wait_vm<(S - 2) * LPO>();
+  ring_barrier();
+  read_frags(0, 1, 0, 0);
+  // slots of stage k (ps, qs) and of stage k+1 (pn, qn)
+  int ps = 0, qs = 1, pn = 2 % S, qn = 3 % S;
+  for (int k = 0; k < nk - 1; ++k) {
+    // k-steps 0-2, each with the next k-step's fragments read between its MFMAs
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      read_frags(ps, qs, s + 1, (s + 1) & 1);
+      mfmas(s & 1);
+      spread(kReadStep, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // stage k+1 has landed for every wave (only the S - 4 most recent
+    // operand stages may be in flight); stage k's slots are free
+    wait_lgkm0();
+    wait_vm<(S - 4) * LPO>();
+    ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    u = un;
+    // k-step 3: the refill of the freed slots with operand stages 2k+S and
+    // 2k+S+1 (longest latency first), then the next stage's first fragments
+    issue(ps, 2 * k + S);
+    issue(qs, 2 * k + S + 1);
+    read_frags(pn, qn, 0, 0);
+    mfmas(1);
+    spread(2 * LPO + kReadStep, 2 * LPO);
+    __builtin_amdgcn_sched_barrier(0);
+    ps = pn; qs = qn;
+    pn = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
+    qn = (qn + 2 >= S) ? qn + 2 - S : qn + 2;
   }
-  read_frags(u, 1, 1);
-  mfmas(0);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    read_frags(ps, qs, s + 1, (s + 1) & 1);
+    mfmas(s & 1);
+  }
   mfmas(1);
   wait_vm<0>();
   // Keep every MFMA above this point and give the last ones time to write
