@@ -36,14 +36,15 @@ hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, i
                           float ca, float cb, float cc, int variant, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  hipStream_t st);
-hipError_t launch_norms_finalize(DevMat* m, LaunchList L, int nblk, float pp_eps, float ns_eps, int init_power,
-                                 hipStream_t st);
+hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st);
+hipError_t launch_norms_scalars(DevMat* m, LaunchList L, int nblk, float ns_eps, int init_power, hipStream_t st);
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st);
 hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, int fin, float pp_eps, float pp_beta,
                                  hipStream_t st);
 hipError_t launch_aurora_scale(DevMat* m, LaunchList L, int nblk, float ns_eps, hipStream_t st);
 hipError_t launch_power_matvec(const DevMat* m, LaunchList L, int nblk, int steps, int final_pass, hipStream_t st);
 hipError_t launch_power_rmatvec(const DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
+hipError_t launch_power_wsum(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_normalize(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_sigma(DevMat* m, LaunchList L, int nblk, float contra, hipStream_t st);
 hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, int fin, hipStream_t st);
@@ -59,6 +60,9 @@ constexpr size_t kAlign = 256;
 constexpr int kSuperM = 4, kSuperN = 8;   // NS tile raster (one XCD's 32 CUs)
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+// Blocks of the norm-line kernel: one per 256 rows, plus one per 256 columns
+// of a wide matrix (its column norms are lines too).
+inline int line_blocks(int rows, int cols) { return cdiv(rows, 256) + (rows < cols ? cdiv(cols, 256) : 0); }
 inline int esz(int dt) { return dt == DT_BF16 ? 2 : 4; }
 
 struct MatInfo {
@@ -68,7 +72,7 @@ struct MatInfo {
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv;
   size_t o_xn, o_x[2], o_xt[2], o_a, o_b, o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
-      o_pwpart, o_tailpart, o_scal, o_ist;
+      o_pwpart, o_tailpart, o_linepart, o_scal, o_ist;
 };
 
 // Host copy of one LaunchList: offset of its int arrays in the meta buffer.
@@ -92,7 +96,7 @@ struct Plan {
   int passes = 1;
   bool any_aurora = false;
   // lists
-  HostList stream, permat, matvec, rmatvec, ascale;
+  HostList stream, permat, lines, colblk, matvec, rmatvec, ascale;
   HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
   HostList dupdate[2];      // [ns_t]
   GemmList gemm[2][2][3];   // [group][ns_t][mode]
@@ -234,7 +238,8 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
     m.o_pu = take((size_t)m.rows * 4);
     m.o_pv = take((size_t)m.cols * 4);
     m.o_pwpart = take(kind == KIND_UPDATE ? (size_t)m.n_rmv * m.cols * 4 : 4);
-    m.o_tailpart = take(std::max((size_t)m.n_rt * m.n_ct * 4, (size_t)cdiv(m.L, 4)) * 4);
+    m.o_tailpart = take(std::max((size_t)m.n_rt * m.n_seg * 4, (size_t)cdiv(m.L, 4)) * 4);
+    m.o_linepart = take((size_t)2 * line_blocks(m.rows, m.cols) * 4);
     m.o_scal = take(SC_COUNT * 4);
     m.o_ist = take(IS_COUNT * 4);
     if (m.aurora) P->any_aurora = true;
@@ -254,11 +259,15 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
   double bytes_stream = 0;
   for (int i = 0; i < nm; ++i) {
     const MatInfo& m = P->mats[i];
-    blocks[i] = m.n_rt * m.n_ct;
+    blocks[i] = m.n_rt * m.n_seg;   // kStreamRows x kSegCols tiles
   }
   add_list(meta, P->stream, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = 1;
   add_list(meta, P->permat, all, blocks);
+  for (int i = 0; i < nm; ++i) blocks[i] = line_blocks(P->mats[i].rows, P->mats[i].cols);
+  add_list(meta, P->lines, all, blocks);
+  for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].cols, 256);
+  add_list(meta, P->colblk, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].rows, 16);   // 4 waves x 4 rows
   add_list(meta, P->matvec, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = P->mats[i].n_rmv * P->mats[i].n_ct;
@@ -547,6 +556,7 @@ muon_status run(muon_handle* h, const Call& c) {
     d.rho = (float*)(ws + m.o_rho); d.dvec = (float*)(ws + m.o_dvec);
     d.pu = (float*)(ws + m.o_pu); d.pv = (float*)(ws + m.o_pv);
     d.pwpart = (float*)(ws + m.o_pwpart); d.tailpart = (float*)(ws + m.o_tailpart);
+    d.linepart = (float*)(ws + m.o_linepart);
     d.scal = (float*)(ws + m.o_scal); d.ist = (int32_t*)(ws + m.o_ist);
   }
   rc = upload_devmat(h, *P, dm);
@@ -584,8 +594,9 @@ muon_status run(muon_handle* h, const Call& c) {
   }
   {
     ProfScope ps(h, 1, 0);
-    CHECK_LAUNCH(h, launch_norms_finalize(D, dev_list(*P, P->permat), P->permat.nblk, cfg.pp_eps, cfg.ns_eps,
-                                          contra ? 1 : 0, st));
+    CHECK_LAUNCH(h, launch_norms_lines(D, dev_list(*P, P->lines), P->lines.nblk, cfg.pp_eps, st));
+    CHECK_LAUNCH(h, launch_norms_scalars(D, dev_list(*P, P->permat), P->permat.nblk, cfg.ns_eps, contra ? 1 : 0,
+                                         st));
   }
   // 2. power iteration
   if (contra) {
@@ -600,6 +611,7 @@ muon_status run(muon_handle* h, const Call& c) {
       }
       {
         ProfScope ps(h, 1, 0);
+        CHECK_LAUNCH(h, launch_power_wsum(D, dev_list(*P, P->colblk), P->colblk.nblk, cfg.power_steps, st));
         CHECK_LAUNCH(h, launch_power_normalize(D, dev_list(*P, P->permat), P->permat.nblk, cfg.power_steps, st));
       }
     }

@@ -18,9 +18,10 @@
 namespace muon {
 
 constexpr int kTile = 256;        // NS output tile edge (and padding unit)
-constexpr int kStreamRows = 32;   // rows per tile of the streaming kernels
-constexpr int kStreamCols = 2048; // columns per tile of the streaming kernels
-constexpr int kSegCols = 512;     // columns per wave segment (row partial sums)
+constexpr int kStreamRows = 32;   // rows per tile of the streaming kernels (4 waves x kWaveRows)
+constexpr int kWaveRows = 8;      // rows per wave of a streaming tile, loaded in one batch
+constexpr int kSegCols = 512;     // columns per streaming tile (a lane covers 8 of them)
+constexpr int kStreamCols = 2048; // columns per tile of the X^T u kernel
 constexpr int kRmvRows = 256;     // rows per tile of the X^T u kernel
 
 enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1 };
@@ -58,8 +59,8 @@ struct DevMat {
   int32_t square;
   int32_t aurora;   // diagonal preconditioner on the long side
   int32_t ns_t;     // DT_F32 or DT_BF16: type of xn, x, xt, a, b
-  int32_t n_rt, n_ct;   // streaming tiles (kStreamRows x kStreamCols)
-  int32_t n_seg;        // ceil(cols / kSegCols)
+  int32_t n_rt, n_ct;   // ceil(rows / kStreamRows), ceil(cols / kStreamCols)
+  int32_t n_seg;        // ceil(cols / kSegCols): streaming tiles are n_rt x n_seg
   int32_t n_rmv;        // ceil(rows / kRmvRows)
   // workspace
   void* xn;
@@ -67,7 +68,7 @@ struct DevMat {
   void* xt[2];
   void* a;
   void* b;
-  float* rowpart;   // rows x n_seg   : row sums of squares per wave segment
+  float* rowpart;   // rows x n_seg   : row sums of squares per tile segment
   float* colpart;   // n_rt x cols    : column sums of squares per row tile
   float* rowsq;     // rows
   float* colsq;     // cols
@@ -76,7 +77,9 @@ struct DevMat {
   float* pu;        // rows : u = X v
   float* pv;        // cols : v
   float* pwpart;    // n_rmv x cols : partial X^T u
-  float* tailpart;  // n_rt * n_ct * 4 : partial tail sums
+  float* tailpart;  // n_rt * n_seg * 4 : partial tail sums per streaming tile
+  float* linepart;  // 2 * (ceil(rows/256) + (rows < cols ? ceil(cols/256) : 0)): per-block norm
+                    // partials of the line sums; reused for the blocks of ||w||^2
   float* scal;      // SC_COUNT
   int32_t* ist;     // IS_COUNT
 };

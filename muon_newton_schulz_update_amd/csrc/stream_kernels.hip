@@ -6,10 +6,20 @@
 // Aurora 的迭代伪代码 / 源码实现 (the diagonal preconditioner D).
 //
 // Every launch covers a whole batch: a LaunchList maps block b to a matrix
-// and a local block index. Streaming tiles are kStreamRows x kStreamCols; a
-// wave owns a kSegCols-column segment, a lane 8 consecutive columns. All
-// reductions are two-stage (per-block partials, then a fixed-order sum in a
-// per-matrix block): no atomics, bitwise reproducible.
+// and a local block index. Streaming tiles are kStreamRows x kSegCols; each
+// of a block's four waves owns kWaveRows rows of one, a lane 8 consecutive
+// columns. All reductions are two-stage (per-block partials, then a
+// fixed-order sum): no atomics, bitwise reproducible.
+//
+// Memory-level parallelism: every HBM access goes through a global
+// address-space pointer (global_load/store: they count on vmcnt only, while
+// generic-pointer loads would also hold up every scalar-load wait), element
+// types are resolved once per block (a uniform branch at kernel entry into a
+// body templated on them), and a lane issues the loads of all its rows before
+// it converts or uses any of them (one batch per wave: short-lived waves keep
+// more requests in flight than looping ones). Lanes whose 8 columns are
+// ragged (the last chunk of a row) or whose buffers are not 16-byte aligned
+// take an element-wise path.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -31,6 +41,18 @@ __device__ __forceinline__ float bf2f(unsigned short h) { return __uint_as_float
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+#define GLOBAL_AS __attribute__((address_space(1)))
+// Loads and stores through global address-space pointers (all buffers here
+// are device memory).
+template <typename V>
+__device__ __forceinline__ V gld(const void* p) {
+  return *(const GLOBAL_AS V*)p;
+}
+template <typename V>
+__device__ __forceinline__ void gst(void* p, V v) {
+  *(GLOBAL_AS V*)p = v;
+}
+
 __device__ __forceinline__ int find_job(const LaunchList& L, int b, int* local) {
   int lo = 0, hi = L.n - 1;
   while (lo < hi) {
@@ -41,60 +63,73 @@ __device__ __forceinline__ int find_job(const LaunchList& L, int b, int* local) 
   return L.mat[lo];
 }
 
-// Load 8 consecutive elements of row r starting at column c (c % 8 == 0),
-// zero beyond `cols`. `vec` = row starts and ld are 16-byte aligned.
-__device__ __forceinline__ void load8(const void* base, int dt, int64_t ld, int r, int c, int cols,
-                                      bool vec, float v[8]) {
-  if (dt == DT_BF16) {
-    const unsigned short* p = (const unsigned short*)base + (size_t)r * ld + c;
-    if (vec && c + 8 <= cols) {
-      const u16x8_t q = *(const u16x8_t*)p;
+// Element types: 8 consecutive elements of a row as one raw vector (16 bytes
+// of bf16, 32 of fp32), converted to float after the loads of a batch.
+template <typename T> struct Ty;
+template <> struct Ty<__bf16> {
+  typedef u16x8_t Raw;
+  __device__ static Raw ld(const void* b, size_t i) { return gld<u16x8_t>((const unsigned short*)b + i); }
+  __device__ static void cvt(const Raw& q, float v[8]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = bf2f(q[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (c + e < cols) ? bf2f(p[e]) : 0.f;
-    }
-  } else {
-    const float* p = (const float*)base + (size_t)r * ld + c;
-    if (vec && c + 8 <= cols) {
-      const f32x4_t q0 = *(const f32x4_t*)p, q1 = *(const f32x4_t*)(p + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { v[e] = q0[e]; v[e + 4] = q1[e]; }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (c + e < cols) ? p[e] : 0.f;
-    }
+    for (int e = 0; e < 8; ++e) v[e] = bf2f(q[e]);
   }
-}
-
-__device__ __forceinline__ void store8(void* base, int dt, int64_t ld, int r, int c, int cols,
-                                       bool vec, const float v[8]) {
-  if (dt == DT_BF16) {
-    unsigned short* p = (unsigned short*)base + (size_t)r * ld + c;
-    if (vec && c + 8 <= cols) {
-      u16x8_t q;
+  __device__ static float ld1(const void* b, size_t i) { return bf2f(gld<unsigned short>((const unsigned short*)b + i)); }
+  __device__ static void st(void* b, size_t i, const float v[8]) {
+    u16x8_t q;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = f2bf(v[e]);
-      *(u16x8_t*)p = q;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) if (c + e < cols) p[e] = f2bf(v[e]);
-    }
-  } else {
-    float* p = (float*)base + (size_t)r * ld + c;
-    if (vec && c + 8 <= cols) {
-      *(f32x4_t*)p = (f32x4_t){v[0], v[1], v[2], v[3]};
-      *(f32x4_t*)(p + 4) = (f32x4_t){v[4], v[5], v[6], v[7]};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) if (c + e < cols) p[e] = v[e];
-    }
+    for (int e = 0; e < 8; ++e) q[e] = f2bf(v[e]);
+    gst<u16x8_t>((unsigned short*)b + i, q);
   }
-}
+  __device__ static void st1(void* b, size_t i, float x) { gst<unsigned short>((unsigned short*)b + i, f2bf(x)); }
+  __device__ static float round(float x) { return bf2f(f2bf(x)); }   // what a later read of a stored value sees
+};
+template <> struct Ty<float> {
+  struct Raw {
+    f32x4_t a, b;
+  };
+  __device__ static Raw ld(const void* b, size_t i) {
+    const float* p = (const float*)b + i;
+    Raw q;
+    q.a = gld<f32x4_t>(p);
+    q.b = gld<f32x4_t>(p + 4);
+    return q;
+  }
+  __device__ static void cvt(const Raw& q, float v[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = q.a[e]; v[e + 4] = q.b[e]; }
+  }
+  __device__ static float ld1(const void* b, size_t i) { return gld<float>((const float*)b + i); }
+  __device__ static void st(void* b, size_t i, const float v[8]) {
+    float* p = (float*)b + i;
+    gst<f32x4_t>(p, (f32x4_t){v[0], v[1], v[2], v[3]});
+    gst<f32x4_t>(p + 4, (f32x4_t){v[4], v[5], v[6], v[7]});
+  }
+  __device__ static void st1(void* b, size_t i, float x) { gst<float>((float*)b + i, x); }
+  __device__ static float round(float x) { return x; }
+};
 
-// Round to the storage type and back (what a later read of a stored value sees).
-__device__ __forceinline__ float round_to(int dt, float x) { return dt == DT_BF16 ? bf2f(f2bf(x)) : x; }
+// Element-wise forms: the first n (0..8) elements at index i, zero past them.
+template <typename T>
+__device__ __forceinline__ void ld_part(const void* b, size_t i, int n, float v[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = e < n ? Ty<T>::ld1(b, i + e) : 0.f;
+}
+template <typename T>
+__device__ __forceinline__ void st_part(void* b, size_t i, int n, const float v[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e < n) Ty<T>::st1(b, i + e, v[e]);
+}
+// Stores whose element type is only known at run time (caller outputs).
+__device__ __forceinline__ void st_vec_rt(void* b, int dt, size_t i, const float v[8]) {
+  if (dt == DT_BF16) Ty<__bf16>::st(b, i, v); else Ty<float>::st(b, i, v);
+}
+__device__ __forceinline__ void st_part_rt(void* b, int dt, size_t i, int n, const float v[8]) {
+  if (dt == DT_BF16) st_part<__bf16>(b, i, n, v); else st_part<float>(b, i, n, v);
+}
+__device__ __forceinline__ float ld1_rt(const void* b, int dt, size_t i) {
+  return dt == DT_BF16 ? Ty<__bf16>::ld1(b, i) : Ty<float>::ld1(b, i);
+}
 
 __device__ __forceinline__ bool aligned16(const void* p, int64_t ld, int dt) {
   const int esz = dt == DT_BF16 ? 2 : 4;
@@ -119,6 +154,21 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Sum of n floats p[0], p[stride], ..., in index order, eight loads at a time.
+__device__ __forceinline__ float strided_sum(const float* p, size_t stride, int n) {
+  float s = 0.f;
+  int k = 0;
+  for (; k + 8 <= n; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = gld<float>(p + (size_t)(k + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; k < n; ++k) s += gld<float>(p + (size_t)k * stride);
+  return s;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -127,122 +177,179 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // X is stored in the NS type (rounded), and the norms are taken of the stored
 // values. With `nesterov_pass` false this only gathers the norms of the
 // matrix given in `g` (the polar entry points).
-// Outputs per tile: rowpart[r][seg] (row sums over a wave segment) and, for
-// wide matrices, colpart[tile_row][c].
+// A block is a kStreamRows x kSegCols tile, a wave kWaveRows rows of it,
+// loaded in one batch. Outputs per tile: rowpart[r][seg] (row sums over the
+// tile's columns) and, for wide matrices, colpart[tile_row][c] (column sums
+// over the tile's rows, the four waves combined in LDS).
 // ---------------------------------------------------------------------------
-constexpr int kRB = 4;   // rows whose loads are issued together (memory-level parallelism)
+template <typename TG, typename TX, bool NP>
+__device__ __forceinline__ void momentum_body(const DevMat& M, int local, float mu, int nesterov, float* cp) {
+  typedef Ty<TG> G;
+  typedef Ty<float> F;
+  constexpr int R = kWaveRows;
+  const int tr = local / M.n_seg, sg = local % M.n_seg;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = sg * kSegCols + lane * 8;
+  const int r = tr * kStreamRows + w * R;            // this wave's first row
+  const int nr = max(0, min(R, M.rows - r));          // uniform per wave
+  const int dg = sizeof(TG) == 2 ? DT_BF16 : DT_F32, dx = sizeof(TX) == 2 ? DT_BF16 : DT_F32;
+  const int nv = max(0, min(8, M.cols - c));
+  const bool fast = nr == R && nv == 8 && aligned16(M.g, M.ld_g, dg) &&
+                    (!NP || (aligned16(M.m, M.ld_m, DT_F32) && aligned16(M.xn, M.cols, dx)));
+  float x[R][8], m[R][8];
+  if (fast) {
+    typename G::Raw qg[R];
+    typename F::Raw qm[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) qg[k] = G::ld(M.g, (size_t)(r + k) * M.ld_g + c);
+    if (NP) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) qm[k] = F::ld(M.m, (size_t)(r + k) * M.ld_m + c);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      G::cvt(qg[k], x[k]);
+      if (NP) F::cvt(qm[k], m[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int n = k < nr ? nv : 0;
+      ld_part<TG>(M.g, (size_t)(r + k) * M.ld_g + c, n, x[k]);
+      if (NP) ld_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m[k]);
+    }
+  }
+  if (NP) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = x[k][e];
+        const float mn = m[k][e] + (1.f - mu) * (g - m[k][e]);
+        m[k][e] = mn;
+        x[k][e] = Ty<TX>::round(nesterov ? g + mu * (mn - g) : mn);
+      }
+    }
+    if (fast) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        F::st(M.m, (size_t)(r + k) * M.ld_m + c, m[k]);
+        Ty<TX>::st(M.xn, (size_t)(r + k) * M.cols + c, x[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int n = k < nr ? nv : 0;
+        st_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m[k]);
+        st_part<TX>(M.xn, (size_t)(r + k) * M.cols + c, n, x[k]);
+      }
+    }
+  }
+  float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { rs += x[k][e] * x[k][e]; col[e] += x[k][e] * x[k][e]; }
+    rs = wave_sum(rs);
+    if (lane == 0 && k < nr) gst<float>(M.rowpart + (size_t)(r + k) * M.n_seg + sg, rs);
+  }
+  if (M.rows < M.cols) {   // uniform per block
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cp[w * kSegCols + lane * 8 + e] = col[e];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < kSegCols / 256; ++h) {
+      const int j = h * 256 + threadIdx.x;
+      const float s = cp[j] + cp[kSegCols + j] + cp[2 * kSegCols + j] + cp[3 * kSegCols + j];
+      if (sg * kSegCols + j < M.cols) gst<float>(M.colpart + (size_t)tr * M.cols + sg * kSegCols + j, s);
+    }
+  }
+}
 
 __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict__ mats, LaunchList L,
                                                         int nesterov_pass, float mu, int nesterov) {
+  static_assert(kStreamRows == 4 * kWaveRows, "four waves per streaming tile");
+  __shared__ float cp[4 * kSegCols];
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  const int tr = local / M.n_ct, tc = local % M.n_ct;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = tc * kStreamCols + w * kSegCols + lane * 8;
-  const int seg = tc * (kStreamCols / kSegCols) + w;
-  const int r0 = tr * kStreamRows;
-  const int r1 = min(r0 + kStreamRows, M.rows);
-  const bool wide_cols = M.rows < M.cols;
-  const bool vg = aligned16(M.g, M.ld_g, M.dt_g);
-  const bool vm = nesterov_pass ? aligned16(M.m, M.ld_m, DT_F32) : false;
-  const bool vx = nesterov_pass ? aligned16(M.xn, M.cols, M.ns_t) : false;
-  const bool live = c < M.cols;
-  const bool seg_live = seg < M.n_seg;
-  float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = r0; r < r1; r += kRB) {
-    // all loads of kRB rows first: the compiler cannot prove that the
-    // stores of one row do not alias the next row's inputs, so a per-row
-    // loop would serialise the memory traffic row by row
-    float x[kRB][8], m[kRB][8];
-#pragma unroll
-    for (int k = 0; k < kRB; ++k) {
-      const bool ok = live && r + k < r1;
-      if (ok) {
-        load8(M.g, M.dt_g, M.ld_g, r + k, c, M.cols, vg, x[k]);
-        if (nesterov_pass) load8(M.m, DT_F32, M.ld_m, r + k, c, M.cols, vm, m[k]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[k][e] = m[k][e] = 0.f;
-      }
-    }
-    if (nesterov_pass) {
-#pragma unroll
-      for (int k = 0; k < kRB; ++k) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float g = x[k][e];
-          const float mn = m[k][e] + (1.f - mu) * (g - m[k][e]);
-          m[k][e] = mn;
-          x[k][e] = round_to(M.ns_t, nesterov ? g + mu * (mn - g) : mn);
-        }
-        if (live && r + k < r1) {
-          store8(M.m, DT_F32, M.ld_m, r + k, c, M.cols, vm, m[k]);
-          store8(M.xn, M.ns_t, M.cols, r + k, c, M.cols, vx, x[k]);
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kRB; ++k) {
-      float rs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { rs += x[k][e] * x[k][e]; col[e] += x[k][e] * x[k][e]; }
-      rs = wave_sum(rs);
-      if (lane == 0 && seg_live && r + k < r1) M.rowpart[(size_t)(r + k) * M.n_seg + seg] = rs;
-    }
-  }
-  if (wide_cols) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (c + e < M.cols) M.colpart[(size_t)tr * M.cols + c + e] = col[e];
+  // the grad's type is the NS type (plans are keyed by it)
+  if (M.dt_g == DT_BF16) {
+    if (nesterov_pass) momentum_body<__bf16, __bf16, true>(M, local, mu, nesterov, cp);
+    else momentum_body<__bf16, __bf16, false>(M, local, mu, nesterov, cp);
+  } else {
+    if (nesterov_pass) momentum_body<float, float, true>(M, local, mu, nesterov, cp);
+    else momentum_body<float, float, false>(M, local, mu, nesterov, cp);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Per-matrix finaliser of the norms: row/column sums of squares, ||X||_F^2,
-// the long-side norms rho, Aurora's initial D = 1 / max(rho, pp_eps), the
-// prologue scale 1 / (||D * T||_F + ns_eps) (D = 1 without Aurora), and the
-// power-iteration start v = ones / sqrt(cols).
+// Norms from the K1 partials, in two launches.
+// Lines: one thread per row (rowsq[r] = sum of the row's segment partials)
+// and, for wide matrices, per column (colsq[c] = sum over row tiles). A
+// long-side line l also gets rho_l = ||line||, D_l = 1 / max(rho_l, eps)
+// (Aurora's initial preconditioner) and (D_l rho_l)^2. Block b of a matrix
+// writes linepart[2b] = its sum of row sums, linepart[2b+1] = its sum of
+// (D rho)^2. Row blocks come first, then column blocks.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_norms_finalize(DevMat* __restrict__ mats, LaunchList L,
-                                                        float pp_eps, float ns_eps, int init_power) {
+__global__ __launch_bounds__(256) void k_norms_lines(DevMat* __restrict__ mats, LaunchList L, float pp_eps) {
+  __shared__ float red[8];
+  int local;
+  DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  const int nrb = (M.rows + 255) / 256;
+  const bool wide = M.rows < M.cols;
+  const bool rowline = local < nrb;
+  const int i = (rowline ? local : local - nrb) * 256 + threadIdx.x;
+  float tpart = 0.f, ypart = 0.f;
+  float lsq = -1.f;   // >= 0 on a long-side line
+  if (rowline) {
+    if (i < M.rows) {
+      const float s = strided_sum(M.rowpart + (size_t)i * M.n_seg, 1, M.n_seg);
+      gst<float>(M.rowsq + i, s);
+      tpart = s;
+      if (!wide) lsq = s;
+    }
+  } else if (i < M.cols) {
+    const float s = strided_sum(M.colpart + i, (size_t)M.cols, M.n_rt);
+    gst<float>(M.colsq + i, s);
+    lsq = s;
+  }
+  if (M.aurora && lsq >= 0.f) {
+    const float rho = sqrtf(lsq);
+    const float d = 1.f / fmaxf(rho, pp_eps);
+    gst<float>(M.rho + i, rho);
+    gst<float>(M.dvec + i, d);
+    ypart = (d * rho) * (d * rho);
+  }
+  tpart = block_sum(tpart, red);
+  ypart = block_sum(ypart, red);
+  if (threadIdx.x == 0) {
+    gst<float>(M.linepart + 2 * local, tpart);
+    gst<float>(M.linepart + 2 * local + 1, ypart);
+  }
+}
+
+// Per matrix: ||X||_F^2, the prologue scale 1 / (||D * T||_F + ns_eps) (D = 1
+// without Aurora), and the power-iteration start v = ones / sqrt(cols).
+__global__ __launch_bounds__(256) void k_norms_scalars(DevMat* __restrict__ mats, LaunchList L, float ns_eps,
+                                                       int init_power) {
   __shared__ float red[8];
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   const int t = threadIdx.x;
-  float tot = 0.f;
-  for (int r = t; r < M.rows; r += 256) {
-    float s = 0.f;
-    for (int k = 0; k < M.n_seg; ++k) s += M.rowpart[(size_t)r * M.n_seg + k];
-    M.rowsq[r] = s;
-    tot += s;
-  }
-  const bool wide = M.rows < M.cols;
-  if (wide) {
-    for (int c = t; c < M.cols; c += 256) {
-      float s = 0.f;
-      for (int k = 0; k < M.n_rt; ++k) s += M.colpart[(size_t)k * M.cols + c];
-      M.colsq[c] = s;
-    }
+  const int nrb = (M.rows + 255) / 256;
+  const int nlb = nrb + (M.rows < M.cols ? (M.cols + 255) / 256 : 0);
+  float tot = 0.f, ysq = 0.f;
+  for (int b = t; b < nlb; b += 256) {
+    tot += gld<float>(M.linepart + 2 * b);
+    ysq += gld<float>(M.linepart + 2 * b + 1);
   }
   tot = block_sum(tot, red);
-  __syncthreads();
-  float ysq = 0.f;
-  if (M.aurora) {
-    const float* lsq = wide ? M.colsq : M.rowsq;
-    for (int l = t; l < M.L; l += 256) {
-      const float rho = sqrtf(lsq[l]);
-      const float d = 1.f / fmaxf(rho, pp_eps);
-      M.rho[l] = rho;
-      M.dvec[l] = d;
-      ysq += (d * rho) * (d * rho);
-    }
-    ysq = block_sum(ysq, red);
-  } else {
-    ysq = tot;
-  }
+  ysq = block_sum(ysq, red);
+  if (!M.aurora) ysq = tot;
   if (init_power) {
     const float v0 = 1.f / sqrtf((float)M.cols);
-    for (int c = t; c < M.cols; c += 256) M.pv[c] = v0;
+    for (int c = t; c < M.cols; c += 256) gst<float>(M.pv + c, v0);
   }
   if (t == 0) {
     M.scal[SC_XNORM2] = tot;
@@ -257,50 +364,74 @@ __global__ __launch_bounds__(256) void k_norms_finalize(DevMat* __restrict__ mat
 // ---------------------------------------------------------------------------
 // NS prologue through an LDS transpose: X0 = scale * D o T in the wide
 // orientation, written to x[0] (s_pad x L_pad) and its transpose to xt[0]
-// (L_pad x s_pad), zero padded (the first iteration's products read both). T is the source in storage orientation (rows x cols); for a
-// tall source the wide iterate is its transpose. 64 x 64 tiles over the
-// padded storage frame.
+// (L_pad x s_pad), zero padded (the first iteration's products read both).
+// T is the source in storage orientation (rows x cols); for a tall source the
+// wide iterate is its transpose. 64 x 64 tiles over the padded storage frame;
+// a thread loads its two 8-column chunks (and their D entries) before using
+// either.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mats, LaunchList L, int use_xn) {
-  __shared__ float tile[64][65];
-  int local;
-  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+template <typename T, typename TS>
+__device__ __forceinline__ void prologue_body(const DevMat& M, int local, const void* src, int64_t lds,
+                                              float (*tile)[65]) {
+  const int dts = sizeof(TS) == 2 ? DT_BF16 : DT_F32;
   const int pc = M.tall ? M.s_pad : M.L_pad;   // padded storage frame: columns
   const int ntc = pc / 64;
   const int br = (local / ntc) * 64, bc = (local % ntc) * 64;
-  const void* src = use_xn ? (const void*)M.xn : M.g;
-  const int64_t lds = use_xn ? (int64_t)M.cols : M.ld_g;
-  const int sdt = use_xn ? M.ns_t : M.dt_g;
-  const bool vs = aligned16(src, lds, sdt);
+  const bool vs = aligned16(src, lds, dts);
   const float scale = M.scal[SC_SCALE];
   // direct frame: wide -> x[0] (ld L_pad); tall -> xt[0] (ld s_pad)
   void* dir = M.tall ? M.xt[0] : M.x[0];
   void* tra = M.tall ? M.x[0] : M.xt[0];
   const int ld_dir = M.tall ? M.s_pad : M.L_pad;
   const int ld_tra = M.tall ? M.L_pad : M.s_pad;
-  const int odt = sizeof(T) == 2 ? DT_BF16 : DT_F32;
   // 64 x 64 tile = 512 chunks of 8 columns; two chunks per thread
+  int rr[2], cc[2], nv[2];
+  bool fv[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int q = h * 256 + threadIdx.x;
-    const int i = q >> 3, j = (q & 7) * 8;
-    const int r = br + i, c = bc + j;
-    float v[8];
-    if (r < M.rows) {
-      load8(src, sdt, lds, r, c, M.cols, vs, v);   // zero past cols
-    } else {
+    rr[h] = br + (q >> 3);
+    cc[h] = bc + (q & 7) * 8;
+    nv[h] = rr[h] < M.rows ? max(0, min(8, M.cols - cc[h])) : 0;
+    fv[h] = vs && nv[h] == 8;
+  }
+  typename Ty<TS>::Raw qs[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  for (int h = 0; h < 2; ++h)
+    if (fv[h]) qs[h] = Ty<TS>::ld(src, (size_t)rr[h] * lds + cc[h]);
+  // D entries: along the columns of a wide source, one per row of a tall one
+  float dv[2][8];
+  if (M.aurora) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (M.tall) {
+        const float d = nv[h] > 0 ? gld<float>(M.dvec + rr[h]) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dv[h][e] = d;
+      } else if (nv[h] == 8) {
+        Ty<float>::cvt(Ty<float>::ld(M.dvec, (size_t)cc[h]), dv[h]);   // dvec: 256-byte aligned, cc % 8 == 0
+      } else {
+        ld_part<float>(M.dvec, (size_t)cc[h], nv[h], dv[h]);
+      }
     }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dv[h][e] = 1.f;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float v[8];
+    if (fv[h]) Ty<TS>::cvt(qs[h], v);
+    else ld_part<TS>(src, (size_t)rr[h] * lds + cc[h], nv[h], v);
+    const int i = rr[h] - br, j = cc[h] - bc;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float d = scale;
-      if (M.aurora && r < M.rows && c + e < M.cols) d *= M.dvec[M.tall ? r : c + e];
-      v[e] *= d;
+      v[e] *= scale * dv[h][e];
       tile[i][j + e] = v[e];
     }
-    store8(dir, odt, ld_dir, r, c, c + 8, true, v);
+    Ty<T>::st(dir, (size_t)rr[h] * ld_dir + cc[h], v);
   }
   __syncthreads();
 #pragma unroll
@@ -310,15 +441,27 @@ __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mat
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tile[i0 + e][jc];
-    store8(tra, odt, ld_tra, bc + jc, br + i0, br + i0 + 8, true, v);
+    Ty<T>::st(tra, (size_t)(bc + jc) * ld_tra + br + i0, v);
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mats, LaunchList L, int use_xn) {
+  __shared__ float tile[64][65];
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  const void* src = use_xn ? (const void*)M.xn : M.g;
+  const int64_t lds = use_xn ? (int64_t)M.cols : M.ld_g;
+  const int sdt = use_xn ? M.ns_t : M.dt_g;
+  if (sdt == DT_BF16) prologue_body<T, __bf16>(M, local, src, lds, tile);
+  else prologue_body<T, float>(M, local, src, lds, tile);
 }
 
 // ---------------------------------------------------------------------------
 // Aurora D update between passes: row_sq_l = max(sum_i U[i][l]^2, eps^2) over
 // the short side (row l of U^T), D_l *= (target / row_sq_l)^beta with
 // target = s / L; then partial sums of (D_l rho_l)^2 per block. One wave per
-// long-side row l; 4 rows per block.
+// long-side row l; 4 rows per block; a lane loads two chunks per round.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mats, LaunchList L,
@@ -330,16 +473,26 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
   const int l = local * 4 + w;
   float contrib = 0.f;
   if (l < M.L) {
-    const T* ut = (const T*)M.xt[fin] + (size_t)l * M.s_pad;
+    const void* ut = M.xt[fin];
+    const size_t row = (size_t)l * M.s_pad;
     float s = 0.f;
-    for (int i = lane * 8; i < M.s; i += 512) {
+    // entries past s are zero padding (the row holds s_pad entries)
+    int i = lane * 8;
+    for (; i + 512 < M.s; i += 1024) {
+      const typename Ty<T>::Raw q0 = Ty<T>::ld(ut, row + i), q1 = Ty<T>::ld(ut, row + i + 512);
+      float u0[8], u1[8];
+      Ty<T>::cvt(q0, u0);
+      Ty<T>::cvt(q1, u1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float u;
-        if constexpr (sizeof(T) == 2) u = bf2f(((const unsigned short*)ut)[i + e]);
-        else u = ((const float*)ut)[i + e];
-        s += u * u;     // entries past s are zero padding
-      }
+      for (int e = 0; e < 8; ++e) s += u0[e] * u0[e];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += u1[e] * u1[e];
+    }
+    if (i < M.s) {
+      float u0[8];
+      Ty<T>::cvt(Ty<T>::ld(ut, row + i), u0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += u0[e] * u0[e];
     }
     s = wave_sum(s);
     if (lane == 0) {
@@ -362,7 +515,7 @@ __global__ __launch_bounds__(256) void k_aurora_scale(DevMat* __restrict__ mats,
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   const int nb = (M.L + 3) / 4;
   float s = 0.f;
-  for (int i = threadIdx.x; i < nb; i += 256) s += M.tailpart[i];
+  for (int i = threadIdx.x; i < nb; i += 256) s += gld<float>(M.tailpart + i);
   s = block_sum(s, red);
   if (threadIdx.x == 0) M.scal[SC_SCALE] = 1.f / (sqrtf(s) + ns_eps);
 }
@@ -380,63 +533,125 @@ __device__ __forceinline__ float inv_fro(const DevMat& M) {
 
 // u = (X / ||X||) v : each wave owns kMvRows rows (16 rows per block); a
 // lane loads 8 consecutive entries of v once and reuses them for every row.
+// Rows past the end are read as the last row and their sums dropped.
 constexpr int kMvRows = 4;
-__global__ __launch_bounds__(256) void k_power_matvec(const DevMat* __restrict__ mats, LaunchList L,
-                                                      int steps, int final_pass) {
-  int local;
-  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  if (!final_pass && M.ist[IS_PSTEPS] >= steps) return;
+template <typename T>
+__device__ __forceinline__ void matvec_body(const DevMat& M, int local) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r0 = (local * 4 + w) * kMvRows;
   if (r0 >= M.rows) return;
-  const bool vx = aligned16(M.xn, M.cols, M.ns_t);
+  const bool vx = aligned16(M.xn, M.cols, sizeof(T) == 2 ? DT_BF16 : DT_F32);
+  size_t ro[kMvRows];
+#pragma unroll
+  for (int k = 0; k < kMvRows; ++k) ro[k] = (size_t)min(r0 + k, M.rows - 1) * M.cols;
   float s[kMvRows];
 #pragma unroll
   for (int k = 0; k < kMvRows; ++k) s[k] = 0.f;
   for (int c = lane * 8; c < M.cols; c += 512) {
-    float v[8];
-    load8(M.pv, DT_F32, 0, 0, c, M.cols, true, v);   // pv is 256-byte aligned workspace
+    const int nv = min(8, M.cols - c);
+    float v[8], x[kMvRows][8];
+    if (vx && nv == 8) {
+      const Ty<float>::Raw qv = Ty<float>::ld(M.pv, (size_t)c);   // pv is 256-byte aligned workspace
+      typename Ty<T>::Raw q[kMvRows];
 #pragma unroll
-    for (int k = 0; k < kMvRows; ++k) {
-      if (r0 + k < M.rows) {
-        float x[8];
-        load8(M.xn, M.ns_t, M.cols, r0 + k, c, M.cols, vx, x);
+      for (int k = 0; k < kMvRows; ++k) q[k] = Ty<T>::ld(M.xn, ro[k] + c);
+      Ty<float>::cvt(qv, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[k] += x[e] * v[e];
-      }
+      for (int k = 0; k < kMvRows; ++k) Ty<T>::cvt(q[k], x[k]);
+    } else {
+      ld_part<float>(M.pv, (size_t)c, nv, v);
+#pragma unroll
+      for (int k = 0; k < kMvRows; ++k) ld_part<T>(M.xn, ro[k] + c, nv, x[k]);
     }
+#pragma unroll
+    for (int k = 0; k < kMvRows; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[k] += x[k][e] * v[e];
   }
   const float inv = inv_fro(M);
 #pragma unroll
   for (int k = 0; k < kMvRows; ++k) {
     const float t = wave_sum(s[k]);
-    if (lane == 0 && r0 + k < M.rows) M.pu[r0 + k] = t * inv;
+    if (lane == 0 && r0 + k < M.rows) gst<float>(M.pu + r0 + k, t * inv);
   }
 }
 
-// partial w = (X / ||X||)^T u over kRmvRows rows x kStreamCols columns per block.
+__global__ __launch_bounds__(256) void k_power_matvec(const DevMat* __restrict__ mats, LaunchList L,
+                                                      int steps, int final_pass) {
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  if (!final_pass && M.ist[IS_PSTEPS] >= steps) return;
+  if (M.ns_t == DT_BF16) matvec_body<__bf16>(M, local);
+  else matvec_body<float>(M, local);
+}
+
+// partial w = (X / ||X||)^T u over kRmvRows rows x kStreamCols columns per
+// block; a lane issues the loads of kRmvBatch rows before using them.
+constexpr int kRmvBatch = 8;
+template <typename T>
+__device__ __forceinline__ void rmatvec_body(const DevMat& M, int local) {
+  const int tr = local / M.n_ct, tc = local % M.n_ct;
+  const int c = tc * kStreamCols + threadIdx.x * 8;
+  if (c >= M.cols) return;
+  const int r0 = tr * kRmvRows, r1 = min(r0 + kRmvRows, M.rows);
+  const int nv = min(8, M.cols - c);
+  const bool fast = nv == 8 && aligned16(M.xn, M.cols, sizeof(T) == 2 ? DT_BF16 : DT_F32);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int r = r0;
+  if (fast) {
+    for (; r + kRmvBatch <= r1; r += kRmvBatch) {
+      typename Ty<T>::Raw q[kRmvBatch];
+      float u[kRmvBatch];
+#pragma unroll
+      for (int k = 0; k < kRmvBatch; ++k) q[k] = Ty<T>::ld(M.xn, (size_t)(r + k) * M.cols + c);
+#pragma unroll
+      for (int k = 0; k < kRmvBatch; ++k) u[k] = gld<float>(M.pu + r + k);
+#pragma unroll
+      for (int k = 0; k < kRmvBatch; ++k) {
+        float x[8];
+        Ty<T>::cvt(q[k], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += u[k] * x[e];
+      }
+    }
+  }
+  for (; r < r1; ++r) {
+    float x[8];
+    ld_part<T>(M.xn, (size_t)r * M.cols + c, nv, x);
+    const float u = gld<float>(M.pu + r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += u * x[e];
+  }
+  const float s = inv_fro(M);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (c + e < M.cols) gst<float>(M.pwpart + (size_t)tr * M.cols + c + e, acc[e] * s);
+}
+
 __global__ __launch_bounds__(256) void k_power_rmatvec(const DevMat* __restrict__ mats, LaunchList L, int steps) {
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   if (M.ist[IS_PSTEPS] >= steps) return;
-  const int tr = local / M.n_ct, tc = local % M.n_ct;
-  const int c = tc * kStreamCols + threadIdx.x * 8;
-  const int r0 = tr * kRmvRows, r1 = min(r0 + kRmvRows, M.rows);
-  const bool vx = aligned16(M.xn, M.cols, M.ns_t);
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (M.ns_t == DT_BF16) rmatvec_body<__bf16>(M, local);
+  else rmatvec_body<float>(M, local);
+}
+
+// w = sum over the row tiles of the partials (one thread per column, stored
+// in row 0 of the partials); block b of a matrix writes linepart[b] = its
+// part of ||w||^2.
+__global__ __launch_bounds__(256) void k_power_wsum(DevMat* __restrict__ mats, LaunchList L, int steps) {
+  __shared__ float red[8];
+  int local;
+  DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  if (M.ist[IS_PSTEPS] >= steps) return;
+  const int c = local * 256 + threadIdx.x;
+  float s = 0.f;
   if (c < M.cols) {
-    for (int r = r0; r < r1; ++r) {
-      float x[8];
-      load8(M.xn, M.ns_t, M.cols, r, c, M.cols, vx, x);
-      const float u = M.pu[r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += u * x[e];
-    }
-    const float s = inv_fro(M);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (c + e < M.cols) M.pwpart[(size_t)tr * M.cols + c + e] = acc[e] * s;
+    s = strided_sum(M.pwpart + c, (size_t)M.cols, M.n_rmv);
+    gst<float>(M.pwpart + c, s);   // only this thread reads column c
   }
+  const float n2 = block_sum(s * s, red);
+  if (threadIdx.x == 0) gst<float>(M.linepart + local, n2);
 }
 
 // v = w / ||w|| (one block per matrix), with the restart rule for a start
@@ -449,19 +664,14 @@ __global__ __launch_bounds__(256) void k_power_normalize(DevMat* __restrict__ ma
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   if (M.ist[IS_PSTEPS] >= steps) return;
   const int t = threadIdx.x;
-  const int nr = (M.rows + kRmvRows - 1) / kRmvRows;
+  const int ncb = (M.cols + 255) / 256;
   float n2 = 0.f;
-  for (int c = t; c < M.cols; c += 256) {
-    float s = 0.f;
-    for (int k = 0; k < nr; ++k) s += M.pwpart[(size_t)k * M.cols + c];
-    M.pwpart[c] = s;     // row 0 of the partials now holds w (read back below)
-    n2 += s * s;
-  }
+  for (int b = t; b < ncb; b += 256) n2 += gld<float>(M.linepart + b);
   n2 = block_sum(n2, red);
   __syncthreads();
   if (n2 > 0.f) {
     const float inv = 1.f / sqrtf(n2);
-    for (int c = t; c < M.cols; c += 256) M.pv[c] = M.pwpart[c] * inv;
+    for (int c = t; c < M.cols; c += 256) gst<float>(M.pv + c, gld<float>(M.pwpart + c) * inv);
     if (t == 0) { M.ist[IS_PSTEPS] += 1; M.scal[SC_PNORM] = sqrtf(n2); }
     return;
   }
@@ -477,12 +687,11 @@ __global__ __launch_bounds__(256) void k_power_normalize(DevMat* __restrict__ ma
   for (int c = t; c < M.cols; c += 256) {
     float s;
     if (wide) {
-      s = M.colsq[c];
+      s = gld<float>(M.colsq + c);
     } else {
       s = 0.f;
       for (int r = 0; r < M.rows; ++r) {
-        const size_t idx = (size_t)r * M.cols + c;
-        const float x = (M.ns_t == DT_BF16) ? bf2f(((const unsigned short*)M.xn)[idx]) : ((const float*)M.xn)[idx];
+        const float x = ld1_rt(M.xn, M.ns_t, (size_t)r * M.cols + c);
         s += x * x;
       }
     }
@@ -499,7 +708,7 @@ __global__ __launch_bounds__(256) void k_power_normalize(DevMat* __restrict__ ma
   }
   __syncthreads();
   const int j = besti[0];
-  for (int c = t; c < M.cols; c += 256) M.pv[c] = (c == j) ? 1.f : 0.f;
+  for (int c = t; c < M.cols; c += 256) gst<float>(M.pv + c, (c == j) ? 1.f : 0.f);
 }
 
 // sigma = ||X v|| (from u = (X/||X||) v), kappa = (contra/2) / max(sigma, 1e-7).
@@ -508,7 +717,10 @@ __global__ __launch_bounds__(256) void k_power_sigma(DevMat* __restrict__ mats, 
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   float s = 0.f;
-  for (int r = threadIdx.x; r < M.rows; r += 256) s += M.pu[r] * M.pu[r];
+  for (int r = threadIdx.x; r < M.rows; r += 256) {
+    const float u = gld<float>(M.pu + r);
+    s += u * u;
+  }
   s = block_sum(s, red);
   if (threadIdx.x == 0) {
     const float n2 = M.scal[SC_XNORM2];
@@ -520,49 +732,95 @@ __global__ __launch_bounds__(256) void k_power_sigma(DevMat* __restrict__ mats, 
 
 // ---------------------------------------------------------------------------
 // Tail. U is the final NS iterate read in storage orientation: x[fin] for
-// wide/square (ld L_pad), xt[fin] for tall (ld s_pad).
+// wide/square (ld L_pad), xt[fin] for tall (ld s_pad). U rows are padded to
+// a multiple of 256 with zeros, so U chunks are always read whole.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ const void* u_ptr(const DevMat& M, int fin, int64_t* ld) {
   if (M.tall) { *ld = M.s_pad; return M.xt[fin]; }
   *ld = M.L_pad; return M.x[fin];
 }
 
-// Partial sums per tile: ||U||^2, ||U - kappa X||^2, ||W||^2.
-__global__ __launch_bounds__(256) void k_tail_reduce(const DevMat* __restrict__ mats, LaunchList L, int fin) {
-  __shared__ float red[3][4];
-  int local;
-  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  const int tr = local / M.n_ct, tc = local % M.n_ct;
+// The U, X and W rows r..r+R-1 at column c: vector loads of all three
+// issued before any is converted (X only when kappa != 0, W only when given).
+template <typename T, typename TW, int R>
+__device__ __forceinline__ void tail_load(const DevMat& M, const void* U, int64_t ldu, int r, int c, bool use_x,
+                                          bool has_w, float (&u)[R][8], float (&x)[R][8], float (&w)[R][8]) {
+  typename Ty<T>::Raw qu[R], qx[R];
+  typename Ty<TW>::Raw qw[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) qu[k] = Ty<T>::ld(U, (size_t)(r + k) * ldu + c);
+  if (use_x) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) qx[k] = Ty<T>::ld(M.xn, (size_t)(r + k) * M.cols + c);
+  }
+  if (has_w) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) qw[k] = Ty<TW>::ld(M.w, (size_t)(r + k) * M.ld_w + c);
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    Ty<T>::cvt(qu[k], u[k]);
+    if (use_x) Ty<T>::cvt(qx[k], x[k]);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[k][e] = 0.f;
+    }
+    if (has_w) Ty<TW>::cvt(qw[k], w[k]);
+  }
+}
+// Element-wise form for one row (ragged chunk, short tile, or unaligned
+// caller buffers).
+template <typename T, typename TW>
+__device__ __forceinline__ void tail_load_part(const DevMat& M, const void* U, int64_t ldu, int r, int c, int nv,
+                                               bool use_x, bool has_w, float u[8], float x[8], float w[8]) {
+  ld_part<T>(U, (size_t)r * ldu + c, nv, u);
+  if (use_x) ld_part<T>(M.xn, (size_t)r * M.cols + c, nv, x);
+  else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+  if (has_w) ld_part<TW>(M.w, (size_t)r * M.ld_w + c, nv, w);
+}
+
+// Partial sums per streaming tile: ||U||^2, ||U - kappa X||^2, ||W||^2.
+template <typename T, typename TW>
+__device__ __forceinline__ void tail_reduce_body(const DevMat& M, int local, int fin, float (*red)[4]) {
+  constexpr int R = kWaveRows;
+  const int tr = local / M.n_seg, sg = local % M.n_seg;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = tc * kStreamCols + w * kSegCols + lane * 8;
-  const int r0 = tr * kStreamRows, r1 = min(r0 + kStreamRows, M.rows);
+  const int c = sg * kSegCols + lane * 8;
+  const int r = tr * kStreamRows + w * R;
+  const int nr = max(0, min(R, M.rows - r));
   int64_t ldu;
   const void* U = u_ptr(M, fin, &ldu);
   const float kappa = M.scal[SC_KAPPA];
-  const bool vx = aligned16(M.xn, M.cols, M.ns_t);
-  const bool vw = M.w ? aligned16(M.w, M.ld_w, M.dt_w) : false;
+  const bool use_x = kappa != 0.f, has_w = M.w != nullptr;
+  const int nv = max(0, min(8, M.cols - c));
+  const bool fast = nr == R && nv == 8 && aligned16(M.xn, M.cols, M.ns_t) &&
+                    (!has_w || aligned16(M.w, M.ld_w, M.dt_w));
   float su = 0.f, sv = 0.f, sw = 0.f;
-  if (c < M.cols) {
-    for (int r = r0; r < r1; ++r) {
-      float u[8], x[8];
-      load8(U, M.ns_t, ldu, r, c, M.cols, true, u);
-      if (kappa != 0.f) load8(M.xn, M.ns_t, M.cols, r, c, M.cols, vx, x);
-      else {
+  auto acc = [&](const float* u, const float* x, const float* wv) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
+    for (int e = 0; e < 8; ++e) {
+      su += u[e] * u[e];
+      const float v = u[e] - kappa * x[e];
+      sv += v * v;
+    }
+    if (has_w) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        su += u[e] * u[e];
-        const float v = u[e] - kappa * x[e];
-        sv += v * v;
-      }
-      if (M.w) {
-        float wv[8];
-        load8(M.w, M.dt_w, M.ld_w, r, c, M.cols, vw, wv);
+      for (int e = 0; e < 8; ++e) sw += wv[e] * wv[e];
+    }
+  };
+  if (fast) {
+    float u[R][8], x[R][8], wv[R][8];
+    tail_load<T, TW, R>(M, U, ldu, r, c, use_x, has_w, u, x, wv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sw += wv[e] * wv[e];
-      }
+    for (int k = 0; k < R; ++k) acc(u[k], x[k], wv[k]);
+  } else if (nv > 0) {
+    for (int k = 0; k < nr; ++k) {
+      float u[8], x[8], wv[8];
+      tail_load_part<T, TW>(M, U, ldu, r + k, c, nv, use_x, has_w, u, x, wv);
+      acc(u, x, wv);
     }
   }
   su = wave_sum(su); sv = wave_sum(sv); sw = wave_sum(sw);
@@ -570,8 +828,28 @@ __global__ __launch_bounds__(256) void k_tail_reduce(const DevMat* __restrict__ 
   __syncthreads();
   if (threadIdx.x < 3) {
     const int k = threadIdx.x;
-    M.tailpart[(size_t)local * 4 + k] = red[k][0] + red[k][1] + red[k][2] + red[k][3];
+    gst<float>(M.tailpart + (size_t)local * 4 + k, red[k][0] + red[k][1] + red[k][2] + red[k][3]);
   }
+}
+
+// W's type when there is no W: any (its loads are skipped); T keeps one body.
+#define TAIL_DISPATCH(BODY, ...)                                                    \
+  do {                                                                              \
+    const int tw_ = M.w ? M.dt_w : M.ns_t;                                          \
+    if (M.ns_t == DT_BF16) {                                                        \
+      if (tw_ == DT_BF16) BODY<__bf16, __bf16>(__VA_ARGS__);                       \
+      else BODY<__bf16, float>(__VA_ARGS__);                                        \
+    } else {                                                                        \
+      if (tw_ == DT_BF16) BODY<float, __bf16>(__VA_ARGS__);                        \
+      else BODY<float, float>(__VA_ARGS__);                                         \
+    }                                                                               \
+  } while (0)
+
+__global__ __launch_bounds__(256) void k_tail_reduce(const DevMat* __restrict__ mats, LaunchList L, int fin) {
+  __shared__ float red[3][4];
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  TAIL_DISPATCH(tail_reduce_body, M, local, fin, red);
 }
 
 // alpha = ||U|| / max(||U - kappa X||, 1e-10) * sqrt(max(1, rows/cols)),
@@ -580,12 +858,12 @@ __global__ __launch_bounds__(256) void k_tail_finalize(DevMat* __restrict__ mats
   __shared__ float red[8];
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  const int nb = M.n_rt * M.n_ct;
+  const int nb = M.n_rt * M.n_seg;
   float su = 0.f, sv = 0.f, sw = 0.f;
   for (int i = threadIdx.x; i < nb; i += 256) {
-    su += M.tailpart[(size_t)i * 4 + 0];
-    sv += M.tailpart[(size_t)i * 4 + 1];
-    sw += M.tailpart[(size_t)i * 4 + 2];
+    su += gld<float>(M.tailpart + (size_t)i * 4 + 0);
+    sv += gld<float>(M.tailpart + (size_t)i * 4 + 1);
+    sw += gld<float>(M.tailpart + (size_t)i * 4 + 2);
   }
   su = block_sum(su, red);
   sv = block_sum(sv, red);
@@ -608,42 +886,57 @@ __global__ __launch_bounds__(256) void k_tail_finalize(DevMat* __restrict__ mats
 
 // V = alpha (U - kappa X); update_out <- V; W <- W - lr V.
 // copy_only: V = U (the polar entry points' output copy).
-__global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ mats, LaunchList L, int fin,
-                                                    float lr, int copy_only) {
-  int local;
-  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  const int tr = local / M.n_ct, tc = local % M.n_ct;
+template <typename T, typename TW>
+__device__ __forceinline__ void tail_apply_body(const DevMat& M, int local, int fin, float lr, int copy_only) {
+  constexpr int R = kWaveRows;
+  const int tr = local / M.n_seg, sg = local % M.n_seg;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = tc * kStreamCols + w * kSegCols + lane * 8;
-  if (c >= M.cols) return;
-  const int r0 = tr * kStreamRows, r1 = min(r0 + kStreamRows, M.rows);
+  const int c = sg * kSegCols + lane * 8;
+  const int r = tr * kStreamRows + w * R;
+  const int nr = max(0, min(R, M.rows - r));
+  if (c >= M.cols || nr == 0) return;
   int64_t ldu;
   const void* U = u_ptr(M, fin, &ldu);
   const float kappa = copy_only ? 0.f : M.scal[SC_KAPPA];
   const float alpha = copy_only ? 1.f : M.scal[SC_ALPHA];
-  const bool vx = aligned16(M.xn, M.cols, M.ns_t);
-  const bool vw = M.w ? aligned16(M.w, M.ld_w, M.dt_w) : false;
-  const bool vo = M.uo ? aligned16(M.uo, M.ld_uo, M.dt_uo) : false;
-  for (int r = r0; r < r1; ++r) {
-    float u[8], x[8];
-    load8(U, M.ns_t, ldu, r, c, M.cols, true, u);
-    if (kappa != 0.f) load8(M.xn, M.ns_t, M.cols, r, c, M.cols, vx, x);
-    else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
+  const bool use_x = kappa != 0.f, has_w = M.w != nullptr, has_o = M.uo != nullptr;
+  const int nv = min(8, M.cols - c);
+  const bool fast = nr == R && nv == 8 && aligned16(M.xn, M.cols, M.ns_t) &&
+                    (!has_w || aligned16(M.w, M.ld_w, M.dt_w)) && (!has_o || aligned16(M.uo, M.ld_uo, M.dt_uo));
+  auto out = [&](int rr, const float* u, const float* x, float* wv, bool vec) {
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = alpha * (u[e] - kappa * x[e]);
-    if (M.uo) store8(M.uo, M.dt_uo, M.ld_uo, r, c, M.cols, vo, v);
-    if (M.w) {
-      float wv[8];
-      load8(M.w, M.dt_w, M.ld_w, r, c, M.cols, vw, wv);
+    if (has_o) {
+      const size_t io = (size_t)rr * M.ld_uo + c;
+      if (vec) st_vec_rt(M.uo, M.dt_uo, io, v); else st_part_rt(M.uo, M.dt_uo, io, nv, v);
+    }
+    if (has_w) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) wv[e] = wv[e] - lr * v[e];
-      store8(M.w, M.dt_w, M.ld_w, r, c, M.cols, vw, wv);
+      const size_t iw = (size_t)rr * M.ld_w + c;
+      if (vec) Ty<TW>::st(M.w, iw, wv); else st_part<TW>(M.w, iw, nv, wv);
+    }
+  };
+  if (fast) {
+    float u[R][8], x[R][8], wv[R][8];
+    tail_load<T, TW, R>(M, U, ldu, r, c, use_x, has_w, u, x, wv);
+#pragma unroll
+    for (int k = 0; k < R; ++k) out(r + k, u[k], x[k], wv[k], true);
+  } else {
+    for (int k = 0; k < nr; ++k) {
+      float u[8], x[8], wv[8];
+      tail_load_part<T, TW>(M, U, ldu, r + k, c, nv, use_x, has_w, u, x, wv);
+      out(r + k, u, x, wv, false);
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ mats, LaunchList L, int fin,
+                                                    float lr, int copy_only) {
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  TAIL_DISPATCH(tail_apply_body, M, local, fin, lr, copy_only);
 }
 
 // ---------------------------------------------------------------------------
@@ -659,9 +952,12 @@ hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int ne
   LAUNCH(k_momentum_stats, nblk, m, L, nesterov_pass, mu, nesterov);
   return hipGetLastError();
 }
-hipError_t launch_norms_finalize(DevMat* m, LaunchList L, int nblk, float pp_eps, float ns_eps,
-                                 int init_power, hipStream_t st) {
-  LAUNCH(k_norms_finalize, nblk, m, L, pp_eps, ns_eps, init_power);
+hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st) {
+  LAUNCH(k_norms_lines, nblk, m, L, pp_eps);
+  return hipGetLastError();
+}
+hipError_t launch_norms_scalars(DevMat* m, LaunchList L, int nblk, float ns_eps, int init_power, hipStream_t st) {
+  LAUNCH(k_norms_scalars, nblk, m, L, ns_eps, init_power);
   return hipGetLastError();
 }
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st) {
@@ -685,6 +981,10 @@ hipError_t launch_power_matvec(const DevMat* m, LaunchList L, int nblk, int step
 }
 hipError_t launch_power_rmatvec(const DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st) {
   LAUNCH(k_power_rmatvec, nblk, m, L, steps);
+  return hipGetLastError();
+}
+hipError_t launch_power_wsum(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st) {
+  LAUNCH(k_power_wsum, nblk, m, L, steps);
   return hipGetLastError();
 }
 hipError_t launch_power_normalize(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st) {
