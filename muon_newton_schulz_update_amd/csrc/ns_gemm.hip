@@ -78,6 +78,15 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // ring. Every wait it needs is explicit before it.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Hand-off through LDS between the lanes of one wave: the LDS executes a
+// wave's accesses in order, so only the compiler has to be kept from moving
+// this wave's reads and writes of its slab across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ unsigned short f2bf(float f) {
   // round to nearest even (inputs here are finite)
   unsigned int u = __float_as_uint(f);
@@ -92,8 +101,9 @@ template <typename T> struct Elem;
 template <> struct Elem<__bf16> {
   static constexpr int kPerChunk = 8;          // bf16 per 16-byte chunk
   typedef bf16x8_t Frag;                       // one MFMA operand per lane
-  __device__ static void ld8(const void* p, size_t i, float v[8]) {
-    const u16x8_t q = *(const u16x8_t*)((const unsigned short*)p + i);
+  typedef u16x8_t Raw;                         // 8 elements as loaded
+  __device__ static Raw ldraw(const void* p, size_t i) { return *(const u16x8_t*)((const unsigned short*)p + i); }
+  __device__ static void cvt(const Raw& q, float v[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = bf2f(q[e]);
   }
@@ -107,10 +117,18 @@ template <> struct Elem<__bf16> {
 template <> struct Elem<float> {
   static constexpr int kPerChunk = 4;
   typedef f32x4_t Frag;                        // four MFMA operands (4 consecutive k) per lane
-  __device__ static void ld8(const void* p, size_t i, float v[8]) {
-    const f32x4_t a = *(const f32x4_t*)((const float*)p + i), b = *(const f32x4_t*)((const float*)p + i + 4);
+  struct Raw {
+    f32x4_t a, b;
+  };
+  __device__ static Raw ldraw(const void* p, size_t i) {
+    Raw q;
+    q.a = *(const f32x4_t*)((const float*)p + i);
+    q.b = *(const f32x4_t*)((const float*)p + i + 4);
+    return q;
+  }
+  __device__ static void cvt(const Raw& q, float v[8]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[e + 4] = b[e]; }
+    for (int e = 0; e < 4; ++e) { v[e] = q.a[e]; v[e + 4] = q.b[e]; }
   }
   __device__ static void st8(void* p, size_t i, const float v[8]) {
     *(f32x4_t*)((float*)p + i) = (f32x4_t){v[0], v[1], v[2], v[3]};
@@ -311,9 +329,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
 
   // Epilogue. Accumulator register r of 32x32 block (mi, ni) holds
   // row 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of that block. Each wave
-  // stages one 32-row slab of its tile at a time in the now idle LDS, then
-  // writes it row-major (8 consecutive columns per lane) and, for mirrored
-  // and X'^T outputs, transposed (8 consecutive rows per lane).
+  // stages one 32-row slab of its tile at a time in its own part of the now
+  // idle LDS, then writes it row-major (8 consecutive columns per lane) and,
+  // for mirrored and X'^T outputs, transposed (8 consecutive rows per lane).
+  // The second product's A values for a slab are loaded before the slab is
+  // staged, so their latency overlaps the staging.
   const int row0 = it.tm * kTile + wm * MI * 32;
   const int col0 = it.tn * kTile + wn * NI * 32;
   void* out;
@@ -328,18 +348,28 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
   }
   const bool write_t = (mode == GM_BX) || (it.tm != it.tn);
   float* buf = (float*)(smem + wave * kSlabBytes);
-  __syncthreads();   // every wave is done with the ring
+  __syncthreads();   // every wave is done with the slots
   constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
+  constexpr int KK = SC / 16;                // 8-column chunks per lane per slab
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
+    typename Elem<T>::Raw araw[mode == GM_SQ ? KK : 1];
+    if constexpr (mode == GM_SQ) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int q = kk * 64 + lane;
+        const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
+        araw[kk] = Elem<T>::ldraw(M.a, (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8);
+      }
+    }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         buf[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + ni * 32 + (lane & 31)] = agpr_read(acc[mi][ni][r]);
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
-    for (int kk = 0; kk < SC / 16; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const int q = kk * 64 + lane;
       const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
       float v[8];
@@ -347,7 +377,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
       if constexpr (mode == GM_SQ) {
         // B' = b A + c A^2 + a I
         float av[8];
-        Elem<T>::ld8(M.a, idx, av);
+        Elem<T>::cvt(araw[kk], av);
         const int dg = (row0 + mi * 32 + rr) - (col0 + c8);   // the diagonal is at e = dg
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = cc * buf[rr * kPitch + c8 + e] + cb * av[e] + (e == dg ? ca : 0.f);
@@ -356,15 +386,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
         for (int e = 0; e < 8; ++e) v[e] = buf[rr * kPitch + c8 + e];
       }
       Elem<T>::st8(out, idx, v);
-      if (write_t) {
+      if (mode == GM_SQ && write_t) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) buf[rr * kPitch + c8 + e] = v[e];
       }
     }
-    __syncthreads();
     if (write_t) {
+      wave_lds_sync();
 #pragma unroll
-      for (int kk = 0; kk < SC / 16; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
         const int q = kk * 64 + lane;
         const int c1 = q >> 2, rc = (q & 3) * 8;
         float v[8];
@@ -373,7 +403,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
         Elem<T>::st8(outT, (size_t)(col0 + c1) * ldt + row0 + mi * 32 + rc, v);
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
 }
 
