@@ -44,6 +44,7 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -347,8 +348,70 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
     out = M.x[cur ^ 1]; outT = M.xt[cur ^ 1]; ldo = Lp; ldt = sp;
   }
   const bool write_t = (mode == GM_BX) || (it.tm != it.tn);
-  float* buf = (float*)(smem + wave * kSlabBytes);
   __syncthreads();   // every wave is done with the slots
+  if constexpr (sizeof(T) == 2 && mode != GM_SQ) {
+    // bf16 outputs that are the accumulators rounded: each wave stages its
+    // whole (MI*32) x (NI*32) tile at once, rounded, column-major (a column's
+    // rows contiguous), so a lane's four consecutive-row accumulators go in
+    // one 8-byte write and a column's rows leave in one 16-byte read; the
+    // row-major output gathers 2-byte elements. Rows are held in 8-row
+    // chunks, chunk index XOR-ed with f(col) = (col ^ col/8) % 8, which keeps
+    // all three access patterns off repeated LDS banks.
+    constexpr int TR = MI * 32, TC = NI * 32;   // the wave's tile
+    static_assert(NW * TR * TC * 2 <= S * kOpBytes, "bf16 staging fits in the slots");
+    unsigned short* st = (unsigned short*)(smem + wave * (TR * TC * 2));
+    auto sidx = [](int row, int col) {           // element index of (row, col) in the staged tile
+      return col * TR + ((((row >> 3) ^ col ^ (col >> 3)) & 7) | ((row >> 3) & ~7)) * 8 + (row & 7);
+    };
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = ni * 32 + (lane & 31);
+          const int row = mi * 32 + 8 * g + 4 * (lane >> 5);   // rows row..row+3: registers 4g..4g+3
+          const unsigned int lo = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g])) |
+                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 1])) << 16);
+          const unsigned int hi = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 2])) |
+                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 3])) << 16);
+          *(u32x2_t*)(st + sidx(row, col)) = (u32x2_t){lo, hi};
+        }
+    wave_lds_sync();
+    const int row0 = it.tm * kTile + wm * TR;
+    const int col0 = it.tn * kTile + wn * TC;
+    void* out;
+    void* outT;
+    int ldo, ldt;
+    if constexpr (mode == GM_GRAM) {
+      out = M.a; outT = M.a; ldo = sp; ldt = sp;
+    } else {
+      out = M.x[cur ^ 1]; outT = M.xt[cur ^ 1]; ldo = Lp; ldt = sp;
+    }
+    // row-major: 8 consecutive columns of one row per lane
+#pragma unroll
+    for (int kk = 0; kk < TR * TC / 8 / 64; ++kk) {
+      const int q = kk * 64 + lane;
+      const int r = q / (TC / 8), c8 = (q % (TC / 8)) * 8;
+      u16x8_t v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = st[sidx(r, c8 + e)];
+      *(u16x8_t*)((unsigned short*)out + (size_t)(row0 + r) * ldo + col0 + c8) = v;
+    }
+    if (write_t) {
+      // transposed: 8 consecutive rows of one column per lane, a column's
+      // TR rows (a whole number of 128-byte lines) by consecutive lanes
+#pragma unroll
+      for (int kk = 0; kk < TR * TC / 8 / 64; ++kk) {
+        const int q = kk * 64 + lane;
+        const int c = q / (TR / 8), r8 = (q % (TR / 8)) * 8;
+        const u16x8_t v = *(const u16x8_t*)(st + sidx(r8, c));
+        *(u16x8_t*)((unsigned short*)outT + (size_t)(col0 + c) * ldt + row0 + r8) = v;
+      }
+    }
+    return;
+  }
+  float* buf = (float*)(smem + wave * kSlabBytes);
   constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
   constexpr int KK = SC / 16;                // 8-column chunks per lane per slab
 #pragma unroll
