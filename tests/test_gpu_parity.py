@@ -219,6 +219,58 @@ def test_aurora_bf16(dev):
 # ---------------------------------------------------------------------------
 # muon_update
 # ---------------------------------------------------------------------------
+def test_ns_polar_misaligned_bf16_view(dev):
+    say("ns_polar on a bf16 view with an odd column offset and odd ld")
+    x = gen.custom_matrix((140, 260), 310, dev, grad_dtype=torch.bfloat16)[0]
+    want = O.newton_schulz(f64(x))
+    big = torch.full((140, 267), 3.0, device=dev, dtype=torch.bfloat16)
+    view = big[:, 1:261]                                    # 2-byte offset, ld = 267
+    view.copy_(x)
+    out_big = torch.full((140, 263), 7.0, device=dev, dtype=torch.bfloat16)
+    out = out_big[:, 3:263]
+    mu.ns_polar([view], [out])
+    torch.cuda.synchronize()
+    e = rel(f64(out), want)
+    say(f"  rel={e:.2e}")
+    assert e <= BF16_TOL
+    assert torch.equal(view, x) and bool((big[:, 0] == 3.0).all()) and bool((big[:, 261:] == 3.0).all())
+    assert bool((out_big[:, :3] == 7.0).all())
+
+
+@pytest.mark.parametrize("aligned", [True, False])
+def test_update_strided_caller_buffers(dev, aligned):
+    """G, M, W and update_out as row-strided views: 16-byte aligned rows take
+    the vector path of the streaming kernels with ld != cols; an odd column
+    offset and odd ld take the element-wise path. Nothing outside a view
+    may change."""
+    say(f"muon_update on strided {'aligned' if aligned else 'misaligned'} caller views")
+    pad, off = (16, 8) if aligned else (5, 1)
+    cases = [((200, 300), torch.bfloat16, BF16_TOL), ((300, 200), torch.float32, FP32_TOL)]
+    views, bigs, ref = [], [], []
+    for i, (shape, dt, _) in enumerate(cases):
+        g, m, w = gen.custom_matrix(shape, 1200 + i, dev, grad_dtype=dt, weight_dtype=dt)
+        r, c = shape
+        bg = torch.full((r, c + pad), 3.0, device=dev, dtype=dt)
+        bm = torch.full((r, c + pad), 5.0, device=dev, dtype=torch.float32)
+        bw = torch.full((r, c + pad), 6.0, device=dev, dtype=dt)
+        bv = torch.full((r, c + pad), 7.0, device=dev, dtype=torch.float32)
+        vg, vm, vw, vv = (b[:, off:off + c] for b in (bg, bm, bw, bv))
+        vg.copy_(g); vm.copy_(m); vw.copy_(w)
+        views.append((vg, vm, vw, vv)); bigs.append((bg, bm, bw, bv)); ref.append((g, m.clone(), w.clone()))
+    mu.muon_update([v[0] for v in views], [v[1] for v in views], [v[2] for v in views], mu.default_config(),
+                   update_out=[v[3] for v in views])
+    torch.cuda.synchronize()
+    for i, (shape, dt, tol) in enumerate(cases):
+        vg, vm, vw, vv = views[i]
+        g, m0, w0 = ref[i]
+        check_update(f"strided[{i}]", g, m0, w0, vm, vv, vw, mu.default_config(), tol)
+        assert torch.equal(vg, g), "the grad is read-only"
+        c = shape[1]
+        for b, fill in zip(bigs[i], (3.0, 5.0, 6.0, 7.0)):
+            outside = torch.cat([b[:, :off], b[:, off + c:]], dim=1)
+            assert bool((outside == fill).all()), "a write landed outside a view"
+
+
 def test_update_single_fp32_256x1024(dev):
     say("muon_update single_fp32_256x1024")
     g, m, w = gen.make_matrix(gen.WORKLOADS["single_fp32_256x1024"], 0, dev)
