@@ -33,7 +33,7 @@
 namespace muon {
 
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
-                          float ca, float cb, float cc, int variant, hipStream_t st);
+                          float ca, float cb, float cc, int variant, int tile, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  hipStream_t st);
 hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st);
@@ -85,9 +85,16 @@ struct HostList {
 
 struct GemmList {
   int n = 0;
+  int tile = kTile;                 // output tile edge of its items (256, or 128 for small launches)
   size_t off = 0;                   // byte offset of TileItem array in meta
   double counted = 0, executed = 0; // flops
 };
+
+// A product launch with fewer 256-tiles than this uses 128-tiles: with one
+// 256-tile workgroup per CU such a launch is a few rounds of workgroups and
+// its last round leaves CUs idle, while 128-tiles (two workgroups per CU)
+// cover the CUs in finer steps. MUON_NS_TILE=128 or 256 forces one size.
+constexpr int kSmallLaunchTiles = 768;
 
 struct Plan {
   int kind = 0;
@@ -299,6 +306,8 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
   }
   // Newton-Schulz tile lists: longest reduction first (LPT); within a matrix,
   // tiles sharing a tile row are consecutive.
+  int force_tile = 0;
+  if (const char* v = getenv("MUON_NS_TILE")) force_tile = atoi(v) == 128 ? 128 : atoi(v) == 256 ? 256 : 0;
   for (int g = 0; g < 2; ++g)
     for (int t = 0; t < 2; ++t)
       for (int mode = 0; mode < 3; ++mode) {
@@ -315,9 +324,17 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
         std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kdim(a) > kdim(b); });
         std::vector<TileItem> items;
         GemmList& G = P->gemm[g][t][mode];
+        long n256 = 0;
+        for (int i : order) {
+          const long ts = P->mats[i].s_pad / kTile, tl = P->mats[i].L_pad / kTile;
+          n256 += mode == GM_BX ? ts * tl : ts * (ts + 1) / 2;
+        }
+        G.tile = n256 < kSmallLaunchTiles ? 128 : kTile;
+        if (force_tile) G.tile = force_tile;
+        const int tile = G.tile;
         for (int i : order) {
           const MatInfo& m = P->mats[i];
-          const int ts = m.s_pad / kTile, tl = m.L_pad / kTile;
+          const int ts = m.s_pad / tile, tl = m.L_pad / tile;
           const double s = m.s, L = m.L;
           const int tcols = mode == GM_BX ? tl : ts;
           // Super-tiles of kSuperM x kSuperN tiles, row-major inside and
@@ -332,11 +349,11 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
                 }
           if (mode == GM_BX) {
             G.counted += 2.0 * s * s * L;
-            G.executed += 2.0 * ts * tl * kTile * (double)kTile * m.s_pad;
+            G.executed += 2.0 * ts * tl * tile * (double)tile * m.s_pad;
           } else {
             const double K = mode == GM_GRAM ? m.L_pad : m.s_pad;
             G.counted += mode == GM_GRAM ? 2.0 * s * s * L : 2.0 * s * s * s;
-            G.executed += 2.0 * (ts * (ts + 1) / 2) * kTile * (double)kTile * K;
+            G.executed += 2.0 * (ts * (ts + 1) / 2) * tile * (double)tile * K;
           }
         }
         add_gemm(meta, G, items);
@@ -642,7 +659,7 @@ muon_status run(muon_handle* h, const Call& c) {
           if (G.n == 0) continue;
           ProfScope ps(h, 0, G.counted, G.executed);
           CHECK_LAUNCH(h, launch_ns_gemm(t, D, (const TileItem*)((uint8_t*)P->meta_dev + G.off), G.n, mode, cur,
-                                         cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, st));
+                                         cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, G.tile, st));
         }
     }
     if (p + 1 < P->passes) {

@@ -17,11 +17,13 @@
 // 4 x 2, each wave 64 x 128 (2 x 4 MFMA 32x32 blocks, accumulators in
 // AGPRs, two waves per SIMD, so one wave's matrix-core work covers the other
 // wave's stalls on the in-order issue of memory instructions); a 4-wave
-// layout (2 x 2 waves of 128 x 128) is kept for tuning.
+// layout (2 x 2 waves of 128 x 128) is kept for tuning. Launches with few
+// tiles use 128 x 128 tiles (2 x 2 waves of 64 x 64, half the LDS, two
+// workgroups per CU), which spread them over the CUs in finer steps.
 //
 // K advances 128 bytes per tile row per stage (64 bf16 or 32 fp32), so each
-// direct-load request covers whole 128-byte lines. The LDS holds five 32 KB
-// operand slots, filled by buffer-form direct global->LDS loads (they count
+// direct-load request covers whole 128-byte lines. The LDS holds five
+// operand slots (32 KB each for 256-tiles), filled by buffer-form direct global->LDS loads (they count
 // on vmcnt only, so waits on LDS fragment reads do not also wait for them);
 // stage k's two operands occupy slots 2k and 2k+1 (mod 5), so while one
 // stage feeds the matrix cores the next stage and half of the one after
@@ -51,7 +53,6 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 namespace {
 
 constexpr int kRowBytes = 128;                 // K bytes per tile row per stage
-constexpr int kOpBytes = kTile * kRowBytes;    // 32 KB: one operand of one stage (one LDS slot)
 constexpr int kPitch = 132;                    // floats per staged epilogue row (128 + 4 spreads banks)
 constexpr int kSlabBytes = 32 * kPitch * 4;    // one wave's 32 x 128 staging slab
 
@@ -144,14 +145,15 @@ template <> struct Elem<float> {
 // b % 8. Items are dealt to XCDs in runs of `group` consecutive items (one
 // super-tile of the planner's raster, whose tiles share operand panels), so a
 // run executes together on one XCD and reuses its L2.
-template <typename T, int mode, int S, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __restrict__ mats,
+template <typename T, int mode, int S, int WM, int WN, int TILE>
+__global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(const DevMat* __restrict__ mats,
                                                              const TileItem* __restrict__ items, int n_items,
                                                              int group, int cur, float ca, float cb, float cc) {
   constexpr int NW = WM * WN;                // waves per workgroup
-  constexpr int MI = kTile / WM / 32;        // 32x32 blocks per wave, down
-  constexpr int NI = kTile / WN / 32;        // 32x32 blocks per wave, across
-  constexpr int LPO = 32 / NW;               // direct loads per wave per operand per stage
+  constexpr int MI = TILE / WM / 32;         // 32x32 blocks per wave, down
+  constexpr int NI = TILE / WN / 32;         // 32x32 blocks per wave, across
+  constexpr int kOpBytes = TILE * kRowBytes; // one operand of one stage (one LDS slot)
+  constexpr int LPO = TILE / 8 / NW;         // direct loads per wave per operand per stage
   constexpr int kMfmaStep = MI * NI * (sizeof(T) == 2 ? 1 : 4);   // MFMAs per k-step
   constexpr int kReadStep = MI + NI;                              // LDS reads per k-step
   // S operand slots; after the K loop the same memory stages the epilogue
@@ -174,17 +176,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
   int ld, K;
   if constexpr (mode == GM_GRAM) {
     const T* x = (const T*)M.x[cur];
-    P = x + (size_t)it.tm * kTile * Lp;
-    Q = x + (size_t)it.tn * kTile * Lp;
+    P = x + (size_t)it.tm * TILE * Lp;
+    Q = x + (size_t)it.tn * TILE * Lp;
     ld = Lp; K = Lp;
   } else if constexpr (mode == GM_SQ) {
     const T* a = (const T*)M.a;
-    P = a + (size_t)it.tm * kTile * sp;
-    Q = a + (size_t)it.tn * kTile * sp;
+    P = a + (size_t)it.tm * TILE * sp;
+    Q = a + (size_t)it.tn * TILE * sp;
     ld = sp; K = sp;
   } else {
-    P = (const T*)M.b + (size_t)it.tm * kTile * sp;
-    Q = (const T*)M.xt[cur] + (size_t)it.tn * kTile * sp;
+    P = (const T*)M.b + (size_t)it.tm * TILE * sp;
+    Q = (const T*)M.xt[cur] + (size_t)it.tn * TILE * sp;
     ld = sp; K = sp;
   }
 
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
   // panel: the second resource gets no records, so its loads fetch nothing
   // (the issue count, and with it every wait, stays the same), and both
   // operands' fragments are read from the first panel's slot.
-  const int ext = (int)((int64_t)kTile * ld * sizeof(T));
+  const int ext = (int)((int64_t)TILE * ld * sizeof(T));
   const bool same = (mode != GM_BX) && (it.tm == it.tn);
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void*)P, (short)0, ext, 0x00020000);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Q, (short)0, same ? 0 : ext, 0x00020000);
@@ -335,8 +337,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
   // for mirrored and X'^T outputs, transposed (8 consecutive rows per lane).
   // The second product's A values for a slab are loaded before the slab is
   // staged, so their latency overlaps the staging.
-  const int row0 = it.tm * kTile + wm * MI * 32;
-  const int col0 = it.tn * kTile + wn * NI * 32;
+  const int row0 = it.tm * TILE + wm * MI * 32;
+  const int col0 = it.tn * TILE + wn * NI * 32;
   void* out;
   void* outT;
   int ldo, ldt;
@@ -378,8 +380,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
           *(u32x2_t*)(st + sidx(row, col)) = (u32x2_t){lo, hi};
         }
     wave_lds_sync();
-    const int row0 = it.tm * kTile + wm * TR;
-    const int col0 = it.tn * kTile + wn * TC;
+    const int row0 = it.tm * TILE + wm * TR;
+    const int col0 = it.tn * TILE + wn * TC;
     void* out;
     void* outT;
     int ldo, ldt;
@@ -473,31 +475,36 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_ns_gemm(const DevMat* __res
 // ---------------------------------------------------------------------------
 // Host-side launcher.
 // ---------------------------------------------------------------------------
-// variant 0: 8 waves in 4 x 2 (64 x 128 per wave, two waves per SIMD);
-// variant 1: 4 waves in 2 x 2 (128 x 128 per wave, one wave per SIMD).
+// tile 256, variant 0: 8 waves in 4 x 2 (64 x 128 per wave, two waves per
+// SIMD); tile 256, variant 1: 4 waves in 2 x 2 (128 x 128 per wave, one wave
+// per SIMD); tile 128: 4 waves in 2 x 2 (64 x 64 per wave), 80 KB of slots,
+// two workgroups per CU, for launches with few tiles.
 // The third product always writes X'^T beside X' (the next iteration's
 // product, the preconditioner update and the output read it).
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
-                          float ca, float cb, float cc, int variant, hipStream_t st) {
+                          float ca, float cb, float cc, int variant, int tile, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
+  if (tile != 256 && tile != 128) return hipErrorInvalidValue;
   const int group = 32;   // one super-tile of the planner's raster per XCD wave
   const int per_xcd_groups = (n_items + 8 * group - 1) / (8 * group);
   const dim3 grid(per_xcd_groups * group * 8);
-#define NS_LAUNCH(T, MODE, WM, WN)                                                                          \
-  hipLaunchKernelGGL((k_ns_gemm<T, MODE, 5, WM, WN>), grid, dim3(WM * WN * 64), 0, st, mats, items, n_items, \
+#define NS_LAUNCH(T, MODE, WM, WN, TL)                                                                            \
+  hipLaunchKernelGGL((k_ns_gemm<T, MODE, 5, WM, WN, TL>), grid, dim3(WM * WN * 64), 0, st, mats, items, n_items, \
                      group, cur, ca, cb, cc)
-#define NS_MODES(T, WM, WN)                             \
-  do {                                                  \
-    if (mode == GM_GRAM) NS_LAUNCH(T, GM_GRAM, WM, WN); \
-    else if (mode == GM_SQ) NS_LAUNCH(T, GM_SQ, WM, WN); \
-    else NS_LAUNCH(T, GM_BX, WM, WN);                   \
+#define NS_MODES(T, WM, WN, TL)                             \
+  do {                                                      \
+    if (mode == GM_GRAM) NS_LAUNCH(T, GM_GRAM, WM, WN, TL); \
+    else if (mode == GM_SQ) NS_LAUNCH(T, GM_SQ, WM, WN, TL); \
+    else NS_LAUNCH(T, GM_BX, WM, WN, TL);                   \
   } while (0)
   if (ns_t == DT_BF16) {
-    if (variant == 1) NS_MODES(__bf16, 2, 2);
-    else NS_MODES(__bf16, 4, 2);
+    if (tile == 128) NS_MODES(__bf16, 2, 2, 128);
+    else if (variant == 1) NS_MODES(__bf16, 2, 2, 256);
+    else NS_MODES(__bf16, 4, 2, 256);
   } else {
-    if (variant == 1) NS_MODES(float, 2, 2);
-    else NS_MODES(float, 4, 2);
+    if (tile == 128) NS_MODES(float, 2, 2, 128);
+    else if (variant == 1) NS_MODES(float, 2, 2, 256);
+    else NS_MODES(float, 4, 2, 256);
   }
 #undef NS_MODES
 #undef NS_LAUNCH
