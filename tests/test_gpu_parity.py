@@ -96,7 +96,7 @@ def check_update(case, G, M0, W0, M1, V, W1, cfg, tol, rows_tol=None):
     return e_v
 
 
-def run_update(dev, mats, cfg=None, out_dtype=torch.float32):
+def run_update(dev, mats, cfg=None, out_dtype=torch.float32, handle=None):
     """mats: list of (G, M, W-or-None) on the device. Returns (M1, V, W1) lists and the originals."""
     cfg = cfg or mu.default_config()
     G = [g for g, _, _ in mats]
@@ -106,7 +106,7 @@ def run_update(dev, mats, cfg=None, out_dtype=torch.float32):
     W = [None if w is None else w.clone() for _, _, w in mats]
     V = [torch.empty(g.shape, device=dev, dtype=out_dtype) for g in G]
     have_w = any(w is not None for w in W)
-    mu.muon_update(G, M, W if have_w else None, cfg, update_out=V)
+    mu.muon_update(G, M, W if have_w else None, cfg, update_out=V, handle=handle)
     torch.cuda.synchronize()
     return G, M0, W0, M, V, W
 
@@ -269,6 +269,34 @@ def test_update_strided_caller_buffers(dev, aligned):
         for b, fill in zip(bigs[i], (3.0, 5.0, 6.0, 7.0)):
             outside = torch.cat([b[:, :off], b[:, off + c:]], dim=1)
             assert bool((outside == fill).all()), "a write landed outside a view"
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_engine_tile_sizes(dev, tile, monkeypatch):
+    """Both engine tile edges on odd, padded shapes (launches this small
+    choose 128 by default; 256 is forced here), fp32 and bf16, through
+    ns_polar and the Aurora path of muon_update. A fresh handle builds its
+    plans with the forced size."""
+    say(f"engine forced to {tile}x{tile} tiles")
+    monkeypatch.setenv("MUON_NS_TILE", str(tile))
+    h = mu.Handle(dev.index)
+    try:
+        shapes = [(33, 517), (300, 700), (517, 33), (260, 260)]
+        for dt, tol in ((torch.float32, FP32_TOL), (torch.bfloat16, BF16_TOL)):
+            xs = [gen.custom_matrix(sh, 1300 + i, dev, grad_dtype=dt)[0] for i, sh in enumerate(shapes)]
+            outs = mu.ns_polar(xs, handle=h)
+            torch.cuda.synchronize()
+            for x, o in zip(xs, outs):
+                e = rel(f64(o), O.newton_schulz(f64(x)))
+                say(f"  ns_polar {tuple(x.shape)} {dt} rel={e:.2e}")
+                assert e <= tol
+        mats = [gen.custom_matrix((384, 130), 1320, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16),
+                gen.custom_matrix((130, 600), 1321, dev)]
+        G, M0, W0, M, V, W = run_update(dev, mats, handle=h)
+        check_update("tile-bf16", G[0], M0[0], W0[0], M[0], V[0], W[0], mu.default_config(), BF16_TOL, ROW_TOL)
+        check_update("tile-fp32", G[1], M0[1], W0[1], M[1], V[1], W[1], mu.default_config(), FP32_TOL)
+    finally:
+        h.close()
 
 
 def test_update_single_fp32_256x1024(dev):
