@@ -196,62 +196,70 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
   const int nv = max(0, min(8, M.cols - c));
   const bool fast = nr == R && nv == 8 && aligned16(M.g, M.ld_g, dg) &&
                     (!NP || (aligned16(M.m, M.ld_m, DT_F32) && aligned16(M.xn, M.cols, dx)));
-  float x[R][8], m[R][8];
-  if (fast) {
-    typename G::Raw qg[R];
-    typename F::Raw qm[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) qg[k] = G::ld(M.g, (size_t)(r + k) * M.ld_g + c);
+  float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float rsl[R];   // this lane's part of each row's sum of squares
+  // one row: the update (stored through vector or element-wise stores), then
+  // this lane's sums of squares; a row's floats die before the next row is
+  // converted. Lanes of one wave may take different paths, so the cross-lane
+  // row sums wait until the paths have rejoined.
+  auto row = [&](int k, float* x, float* m, bool vec) {
     if (NP) {
 #pragma unroll
-      for (int k = 0; k < R; ++k) qm[k] = F::ld(M.m, (size_t)(r + k) * M.ld_m + c);
+      for (int e = 0; e < 8; ++e) {
+        const float g = x[e];
+        const float mn = m[e] + (1.f - mu) * (g - m[e]);
+        m[e] = mn;
+        x[e] = Ty<TX>::round(nesterov ? g + mu * (mn - g) : mn);
+      }
+      if (vec) {
+        F::st(M.m, (size_t)(r + k) * M.ld_m + c, m);
+        Ty<TX>::st(M.xn, (size_t)(r + k) * M.cols + c, x);
+      } else {
+        const int n = k < nr ? nv : 0;
+        st_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m);
+        st_part<TX>(M.xn, (size_t)(r + k) * M.cols + c, n, x);
+      }
     }
+    float rs = 0.f;
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      G::cvt(qg[k], x[k]);
-      if (NP) F::cvt(qm[k], m[k]);
+    for (int e = 0; e < 8; ++e) { rs += x[e] * x[e]; col[e] += x[e] * x[e]; }
+    rsl[k] = rs;
+  };
+  if (fast) {
+    // fp32 grads load in two batches of R/2 rows: the kernel's register
+    // budget is set by its largest body
+    constexpr int RB = sizeof(TG) == 2 ? R : R / 2;
+#pragma unroll
+    for (int k0 = 0; k0 < R; k0 += RB) {
+      typename G::Raw qg[RB];
+      typename F::Raw qm[RB];
+#pragma unroll
+      for (int k = 0; k < RB; ++k) qg[k] = G::ld(M.g, (size_t)(r + k0 + k) * M.ld_g + c);
+      if (NP) {
+#pragma unroll
+        for (int k = 0; k < RB; ++k) qm[k] = F::ld(M.m, (size_t)(r + k0 + k) * M.ld_m + c);
+      }
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        float x[8], m[8];
+        G::cvt(qg[k], x);
+        if (NP) F::cvt(qm[k], m);
+        row(k0 + k, x, m, true);
+      }
     }
   } else {
 #pragma unroll
     for (int k = 0; k < R; ++k) {
+      float x[8], m[8];
       const int n = k < nr ? nv : 0;
-      ld_part<TG>(M.g, (size_t)(r + k) * M.ld_g + c, n, x[k]);
-      if (NP) ld_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m[k]);
+      ld_part<TG>(M.g, (size_t)(r + k) * M.ld_g + c, n, x);
+      if (NP) ld_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m);
+      row(k, x, m, false);
     }
   }
-  if (NP) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float g = x[k][e];
-        const float mn = m[k][e] + (1.f - mu) * (g - m[k][e]);
-        m[k][e] = mn;
-        x[k][e] = Ty<TX>::round(nesterov ? g + mu * (mn - g) : mn);
-      }
-    }
-    if (fast) {
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        F::st(M.m, (size_t)(r + k) * M.ld_m + c, m[k]);
-        Ty<TX>::st(M.xn, (size_t)(r + k) * M.cols + c, x[k]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int n = k < nr ? nv : 0;
-        st_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m[k]);
-        st_part<TX>(M.xn, (size_t)(r + k) * M.cols + c, n, x[k]);
-      }
-    }
-  }
-  float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    float rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { rs += x[k][e] * x[k][e]; col[e] += x[k][e] * x[k][e]; }
-    rs = wave_sum(rs);
+    const float rs = wave_sum(rsl[k]);
     if (lane == 0 && k < nr) gst<float>(M.rowpart + (size_t)(r + k) * M.n_seg + sg, rs);
   }
   if (M.rows < M.cols) {   // uniform per block
@@ -741,33 +749,35 @@ __device__ __forceinline__ const void* u_ptr(const DevMat& M, int fin, int64_t* 
 }
 
 // The U, X and W rows r..r+R-1 at column c: vector loads of all three
-// issued before any is converted (X only when kappa != 0, W only when given).
+// issued before any is used (X only when kappa != 0, W only when given);
+// a row is converted when it is consumed.
 template <typename T, typename TW, int R>
-__device__ __forceinline__ void tail_load(const DevMat& M, const void* U, int64_t ldu, int r, int c, bool use_x,
-                                          bool has_w, float (&u)[R][8], float (&x)[R][8], float (&w)[R][8]) {
+struct TailRows {
   typename Ty<T>::Raw qu[R], qx[R];
   typename Ty<TW>::Raw qw[R];
+  __device__ __forceinline__ void load(const DevMat& M, const void* U, int64_t ldu, int r, int c, bool use_x,
+                                       bool has_w) {
 #pragma unroll
-  for (int k = 0; k < R; ++k) qu[k] = Ty<T>::ld(U, (size_t)(r + k) * ldu + c);
-  if (use_x) {
+    for (int k = 0; k < R; ++k) qu[k] = Ty<T>::ld(U, (size_t)(r + k) * ldu + c);
+    if (use_x) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) qx[k] = Ty<T>::ld(M.xn, (size_t)(r + k) * M.cols + c);
+      for (int k = 0; k < R; ++k) qx[k] = Ty<T>::ld(M.xn, (size_t)(r + k) * M.cols + c);
+    }
+    if (has_w) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) qw[k] = Ty<TW>::ld(M.w, (size_t)(r + k) * M.ld_w + c);
+    }
   }
-  if (has_w) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) qw[k] = Ty<TW>::ld(M.w, (size_t)(r + k) * M.ld_w + c);
-  }
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    Ty<T>::cvt(qu[k], u[k]);
-    if (use_x) Ty<T>::cvt(qx[k], x[k]);
+  __device__ __forceinline__ void row(int k, bool use_x, bool has_w, float u[8], float x[8], float w[8]) const {
+    Ty<T>::cvt(qu[k], u);
+    if (use_x) Ty<T>::cvt(qx[k], x);
     else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[k][e] = 0.f;
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
     }
-    if (has_w) Ty<TW>::cvt(qw[k], w[k]);
+    if (has_w) Ty<TW>::cvt(qw[k], w);
   }
-}
+};
 // Element-wise form for one row (ragged chunk, short tile, or unaligned
 // caller buffers).
 template <typename T, typename TW>
@@ -812,10 +822,20 @@ __device__ __forceinline__ void tail_reduce_body(const DevMat& M, int local, int
     }
   };
   if (fast) {
-    float u[R][8], x[R][8], wv[R][8];
-    tail_load<T, TW, R>(M, U, ldu, r, c, use_x, has_w, u, x, wv);
+    // fp32 operands load in two batches of R/2 rows: the kernel's register
+    // budget is set by its largest body
+    constexpr int RB = (sizeof(T) == 2 && sizeof(TW) == 2) ? R : R / 2;
 #pragma unroll
-    for (int k = 0; k < R; ++k) acc(u[k], x[k], wv[k]);
+    for (int k0 = 0; k0 < R; k0 += RB) {
+      TailRows<T, TW, RB> q;
+      q.load(M, U, ldu, r + k0, c, use_x, has_w);
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        float u[8], x[8], wv[8];
+        q.row(k, use_x, has_w, u, x, wv);
+        acc(u, x, wv);
+      }
+    }
   } else if (nv > 0) {
     for (int k = 0; k < nr; ++k) {
       float u[8], x[8], wv[8];
@@ -919,10 +939,20 @@ __device__ __forceinline__ void tail_apply_body(const DevMat& M, int local, int 
     }
   };
   if (fast) {
-    float u[R][8], x[R][8], wv[R][8];
-    tail_load<T, TW, R>(M, U, ldu, r, c, use_x, has_w, u, x, wv);
+    // fp32 operands load in two batches of R/2 rows: the kernel's register
+    // budget is set by its largest body
+    constexpr int RB = (sizeof(T) == 2 && sizeof(TW) == 2) ? R : R / 2;
 #pragma unroll
-    for (int k = 0; k < R; ++k) out(r + k, u[k], x[k], wv[k], true);
+    for (int k0 = 0; k0 < R; k0 += RB) {
+      TailRows<T, TW, RB> q;
+      q.load(M, U, ldu, r + k0, c, use_x, has_w);
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        float u[8], x[8], wv[8];
+        q.row(k, use_x, has_w, u, x, wv);
+        out(r + k0 + k, u, x, wv, true);
+      }
+    }
   } else {
     for (int k = 0; k < nr; ++k) {
       float u[8], x[8], wv[8];
