@@ -299,6 +299,22 @@ def test_engine_tile_sizes(dev, tile, monkeypatch):
         h.close()
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, FP32_TOL), (torch.bfloat16, BF16_TOL)])
+def test_update_ragged_columns_mixed_lanes(dev, dtype, tol):
+    """Column counts whose last 8-column chunk is partial, so one wave holds
+    lanes on the vector path, a lane on the element-wise path and idle
+    lanes (cross-lane sums must wait until they rejoin); rows not a
+    multiple of the 8-row wave batch."""
+    say(f"muon_update with ragged columns, {dtype}")
+    shapes = [(37, 260), (260, 37), (70, 1030), (1030, 70), (9, 515)]
+    mats = [gen.custom_matrix(sh, 1400 + i, dev, grad_dtype=dtype, weight_dtype=dtype)
+            for i, sh in enumerate(shapes)]
+    G, M0, W0, M, V, W = run_update(dev, mats)
+    for i in range(len(shapes)):
+        check_update(f"ragged[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], mu.default_config(), tol,
+                     ROW_TOL if dtype == torch.bfloat16 else None)
+
+
 def test_update_single_fp32_256x1024(dev):
     say("muon_update single_fp32_256x1024")
     g, m, w = gen.make_matrix(gen.WORKLOADS["single_fp32_256x1024"], 0, dev)
