@@ -23,8 +23,9 @@
 //
 // K advances 128 bytes per tile row per stage (64 bf16 or 32 fp32), so each
 // direct-load request covers whole 128-byte lines. The LDS holds five
-// operand slots (32 KB each for 256-tiles), filled by buffer-form direct global->LDS loads (they count
-// on vmcnt only, so waits on LDS fragment reads do not also wait for them);
+// operand slots (32 KB each for 256-tiles), filled by buffer-form direct
+// global->LDS loads (they count on vmcnt only, so waits on LDS fragment reads
+// do not also wait for them);
 // stage k's two operands occupy slots 2k and 2k+1 (mod 5), so while one
 // stage feeds the matrix cores the next stage and half of the one after
 // stream in. A stage is four k-steps; each step's fragments are read between
@@ -53,7 +54,7 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 namespace {
 
 constexpr int kRowBytes = 128;                 // K bytes per tile row per stage
-constexpr int kPitch = 132;                    // floats per staged epilogue row (128 + 4 spreads banks)
+constexpr int kPitch = 132;                    // floats per staged epilogue row (widest slab 128, + 4 spreads banks)
 constexpr int kSlabBytes = 32 * kPitch * 4;    // one wave's 32 x 128 staging slab
 
 // Read one accumulator through an explicit AGPR->VGPR move. The "a"
@@ -66,7 +67,8 @@ __device__ __forceinline__ float agpr_read(float a) {
 }
 
 // s_waitcnt vmcnt(n), lgkmcnt and expcnt left free: all but this wave's n
-// most recent vector-memory loads have completed (loads complete in order).
+// most recent vector-memory operations have completed (the counter retires
+// them in issue order; in the K loop every such operation is a stage load).
 template <int n>
 __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt immediate");   // 6 bits: [3:0] and [15:14]
@@ -332,11 +334,11 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
 
   // Epilogue. Accumulator register r of 32x32 block (mi, ni) holds
   // row 8*(r/4) + 4*(lane/32) + r%4, column lane%32 of that block. Each wave
-  // stages one 32-row slab of its tile at a time in its own part of the now
-  // idle LDS, then writes it row-major (8 consecutive columns per lane) and,
-  // for mirrored and X'^T outputs, transposed (8 consecutive rows per lane).
-  // The second product's A values for a slab are loaded before the slab is
-  // staged, so their latency overlaps the staging.
+  // stages its accumulators in its own part of the now idle LDS and writes
+  // them row-major (8 consecutive columns per lane) and, for mirrored and
+  // X'^T outputs, transposed (8 consecutive rows per lane): bf16 Gram and X'
+  // tiles in one pass (below), the second product and fp32 tiles one 32-row
+  // fp32 slab at a time.
   const int row0 = it.tm * TILE + wm * MI * 32;
   const int col0 = it.tn * TILE + wn * NI * 32;
   void* out;
@@ -380,16 +382,6 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
           *(u32x2_t*)(st + sidx(row, col)) = (u32x2_t){lo, hi};
         }
     wave_lds_sync();
-    const int row0 = it.tm * TILE + wm * TR;
-    const int col0 = it.tn * TILE + wn * TC;
-    void* out;
-    void* outT;
-    int ldo, ldt;
-    if constexpr (mode == GM_GRAM) {
-      out = M.a; outT = M.a; ldo = sp; ldt = sp;
-    } else {
-      out = M.x[cur ^ 1]; outT = M.xt[cur ^ 1]; ldo = Lp; ldt = sp;
-    }
     // row-major: 8 consecutive columns of one row per lane
 #pragma unroll
     for (int kk = 0; kk < TR * TC / 8 / 64; ++kk) {
@@ -413,6 +405,8 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     }
     return;
   }
+  // 32-row fp32 slabs; the second product's A values for a slab are loaded
+  // before the slab is staged, so their latency overlaps the staging
   float* buf = (float*)(smem + wave * kSlabBytes);
   constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
   constexpr int KK = SC / 16;                // 8-column chunks per lane per slab
