@@ -8,10 +8,13 @@
 //
 // Sequence of one muon_update (Aurora record page, www.xxmr.cn/news/295280,
 // section 组合优化栈 and the pseudocode in Aurora 的迭代伪代码):
-//   momentum + Nesterov + norms -> per-matrix finalise (rho, D0, scale)
-//   -> power iteration (power_steps + 1 rounds, then sigma)
+//   momentum + Nesterov + row partial norms -> norm lines (row and column
+//   norms, rho, D0) -> per-matrix scalars (||X||, prologue scale)
+//   -> power iteration (power_steps + 1 rounds of Xv, X^T u, ||w||, v = w/||w||;
+//      then sigma)
 //   -> for each Aurora pass: prologue (scale * D o T, both orientations),
-//      ns_steps x {Gram, B = bA + cA^2, X = aX + BX}, D update between passes
+//      ns_steps x {A = XX^T, B' = bA + cA^2 + aI, X = B'X}, D update between
+//      passes
 //   -> tail reduce -> tail finalise (Contra, Frobenius restore, aspect, floor)
 //   -> tail apply (update_out, W -= lr V).
 #include <hip/hip_runtime.h>
