@@ -156,6 +156,14 @@ const char* muon_version(void);
  * owned. The handle owns its device workspace and plan cache; both grow on
  * demand and are freed by muon_destroy. Returns MUON_ERR_NO_DEVICE when no
  * gfx950 device is current.
+ *
+ * Tuning (environment; results are the same up to floating-point rounding):
+ *   MUON_NS_VARIANT=1      read here: Newton-Schulz products on 256x256 tiles
+ *                          with 4 waves of 128x128 instead of 8 of 64x128.
+ *   MUON_NS_TILE=128|256   read when a plan is built (first call with a new
+ *                          set of shapes): force the product tile edge;
+ *                          otherwise launches with fewer than 768 256-tiles
+ *                          use 128-tiles.
  */
 muon_status muon_create(muon_handle** handle, void* stream);
 
