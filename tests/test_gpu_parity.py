@@ -114,7 +114,7 @@ def run_update(dev, mats, cfg=None, out_dtype=torch.float32, handle=None):
 # ---------------------------------------------------------------------------
 # ns_polar
 # ---------------------------------------------------------------------------
-ODD = [(1, 1), (1, 7), (7, 1), (5, 5), (33, 517), (517, 33), (255, 257), (300, 700)]
+ODD = [(1, 1), (1, 7), (7, 1), (5, 5), (33, 517), (517, 33), (255, 257), (300, 700), (4096, 1), (1, 4096)]
 
 
 def test_ns_polar_fp32_odd_shapes(dev):
@@ -313,6 +313,24 @@ def test_update_ragged_columns_mixed_lanes(dev, dtype, tol):
     for i in range(len(shapes)):
         check_update(f"ragged[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], mu.default_config(), tol,
                      ROW_TOL if dtype == torch.bfloat16 else None)
+
+
+def test_workspace_allocation_failure_leaves_handle_usable(dev):
+    """A workspace larger than the device (40 matrices of 16384 x 65536 bf16,
+    about 440 GB of workspace) fails in hipMalloc: MUON_ERR_ALLOC with a
+    message, nothing enqueued, and the same handle then runs a normal call."""
+    say("workspace allocation failure")
+    h = mu.Handle(dev.index)
+    try:
+        with pytest.raises(mu.LibMuonError) as ei:
+            h.reserve([(16384, 65536, torch.bfloat16)] * 40)
+        assert ei.value.status == -4 and "workspace allocation" in str(ei.value)
+        x = gen.custom_matrix((96, 200), 1500, dev)[0]
+        out = mu.ns_polar([x], handle=h)[0]
+        torch.cuda.synchronize()
+        assert rel(f64(out), O.newton_schulz(f64(x))) <= FP32_TOL
+    finally:
+        h.close()
 
 
 def test_update_single_fp32_256x1024(dev):
