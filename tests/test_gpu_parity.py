@@ -368,13 +368,24 @@ def test_update_floor_forced(dev):
     assert float(ratio) == pytest.approx(0.35, rel=1e-4)
 
 
-@pytest.mark.parametrize("opt", ["contra0", "nesterov0", "pp0", "pp3", "no_weight_floor"])
+OPTIONS = {
+    "contra0": dict(contra=0.0), "contra1": dict(contra=1.0), "nesterov0": dict(nesterov=0),
+    "pp0": dict(pp_iterations=0), "pp1": dict(pp_iterations=1), "pp3": dict(pp_iterations=3),
+    "beta1": dict(pp_beta=1.0), "no_weight_floor": dict(target_uw=0.0), "ns_steps1": dict(ns_steps=1),
+    "ns_steps20": dict(ns_steps=20), "power1": dict(power_steps=1), "power9": dict(power_steps=9),
+    "mu0": dict(mu=0.0), "mu0p5": dict(mu=0.5), "lr0": dict(lr=0.0),
+}
+
+
+@pytest.mark.parametrize("opt", list(OPTIONS))
 def test_update_options(dev, opt):
+    """Each configuration field away from its default (pp 1 is the row-
+    normalised Muon baseline the Aurora page compares against)."""
     say(f"muon_update option {opt}")
-    over = {"contra0": dict(contra=0.0), "nesterov0": dict(nesterov=0), "pp0": dict(pp_iterations=0),
-            "pp3": dict(pp_iterations=3), "no_weight_floor": dict(target_uw=0.0)}[opt]
+    over = OPTIONS[opt]
     cfg = mu.make_config(**over)
-    g, m, w = gen.custom_matrix((260, 140), 1000 + len(opt), dev, weight_sd=1.0)
+    i = list(OPTIONS).index(opt)
+    g, m, w = gen.custom_matrix((260, 140) if i % 2 == 0 else (140, 260), 1000 + i, dev, weight_sd=1.0)
     G, M0, W0, M, V, W = run_update(dev, [(g, m, w)], cfg)
     check_update(opt, G[0], M0[0], W0[0], M[0], V[0], W[0], cfg, FP32_TOL)
 
