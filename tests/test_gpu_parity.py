@@ -350,6 +350,27 @@ def test_update_mixed_batch_bf16(dev):
         check_update(f"mixed[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], mu.default_config(), BF16_TOL, ROW_TOL)
 
 
+def test_update_many_small_matrices(dev):
+    """1500 small matrices of 1500 distinct shapes (733 tall, 735 wide, 32
+    square, 1 to 48 on a side) in one call: the planner's per-launch block lists and tile lists
+    at a batch size far beyond the named workloads, every matrix checked."""
+    say("muon_update 1500 small matrices in one call")
+    shapes = [(1 + (7 * i) % 48, 1 + (11 * i + 3 + i // 48) % 48) for i in range(1500)]   # 1500 distinct
+    mats = [gen.custom_matrix(sh, 5000 + i, dev, weight_sd=1.0) for i, sh in enumerate(shapes)]
+    G, M0, W0, M, V, W = run_update(dev, mats)
+    cfg = mu.default_config()
+    oc = ocfg(cfg)
+    worst = 0.0
+    for i in range(len(shapes)):
+        Mo, Vo, Wo = O.muon_update(f64(G[i]), f64(M0[i]), f64(W0[i]), oc)
+        e = rel(f64(V[i]), Vo)
+        worst = max(worst, e)
+        assert e <= FP32_TOL, (i, shapes[i], e)
+        assert rel(f64(M[i]), Mo) <= MOM_TOL, i
+        assert weight_add_ok(W0[i], V[i], W[i], cfg), i
+    say(f"  worst rel(V) over 1500 matrices {worst:.2e}")
+
+
 def test_update_mixed_dtypes_in_one_call(dev):
     say("muon_update fp32 and bf16 matrices in one call")
     a = gen.custom_matrix((200, 90), 800, dev)
