@@ -115,8 +115,8 @@ def main() -> int:
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(each matrix's step is independent; see the sharding note in the design notes)",
+        print("bench.py runs on one GPU only: libmuon has no multi-GPU path (every matrix's step is "
+              "independent, so a multi-GPU run would shard whole matrices across ranks)",
               file=sys.stderr)
         return 2
 
