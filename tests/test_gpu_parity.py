@@ -315,6 +315,22 @@ def test_update_ragged_columns_mixed_lanes(dev, dtype, tol):
                      ROW_TOL if dtype == torch.bfloat16 else None)
 
 
+def test_calls_follow_the_current_stream(dev):
+    """The binding hands torch's current stream to the handle (muon_set_stream
+    when it changes): a call on a side stream, then one back on the default
+    stream, each ordered after the work that produced its inputs."""
+    say("muon_update on a side stream, then on the default stream")
+    side = torch.cuda.Stream(device=dev)   # default priority
+    cfg = mu.default_config()
+    shapes = [(200, 90), (90, 200)]
+    for rnd, stream in enumerate([side, torch.cuda.current_stream(dev)]):
+        with torch.cuda.stream(stream):
+            mats = [gen.custom_matrix(sh, 1700 + 10 * rnd + i, dev, weight_sd=1.0) for i, sh in enumerate(shapes)]
+            G, M0, W0, M, V, W = run_update(dev, mats, cfg)
+        for i in range(len(shapes)):
+            check_update(f"stream{rnd}[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], cfg, FP32_TOL)
+
+
 def test_workspace_allocation_failure_leaves_handle_usable(dev):
     """A workspace larger than the device (40 matrices of 16384 x 65536 bf16,
     about 440 GB of workspace) fails in hipMalloc: MUON_ERR_ALLOC with a
