@@ -10,8 +10,9 @@
 // section 组合优化栈 and the pseudocode in Aurora 的迭代伪代码):
 //   momentum + Nesterov + row partial norms -> norm lines (row and column
 //   norms, rho, D0) -> per-matrix scalars (||X||, prologue scale)
-//   -> power iteration (power_steps + 1 rounds of Xv, X^T u, ||w||, v = w/||w||;
-//      then sigma)
+//   -> power iteration (power_steps + 1 rounds of w = X^T X v, one read of X
+//      in a fused pass, or X v then X^T u for matrices wider than
+//      kFusedCols; ||w||, v = w/||w||; then X v and sigma)
 //   -> for each Aurora pass: prologue (scale * D o T, both orientations),
 //      ns_steps x {A = XX^T, B' = bA + cA^2 + aI, X = B'X}, D update between
 //      passes
@@ -47,6 +48,8 @@ hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, in
 hipError_t launch_aurora_scale(DevMat* m, LaunchList L, int nblk, float ns_eps, hipStream_t st);
 hipError_t launch_power_matvec(const DevMat* m, LaunchList L, int nblk, int steps, int final_pass, hipStream_t st);
 hipError_t launch_power_rmatvec(const DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
+hipError_t launch_power_fused(int ns_t, const DevMat* m, LaunchList L, int nblk, int steps, int max_cols,
+                              hipStream_t st);
 hipError_t launch_power_wsum(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_normalize(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_sigma(DevMat* m, LaunchList L, int nblk, float contra, hipStream_t st);
@@ -73,10 +76,17 @@ struct MatInfo {
   int rows, cols, s, L, s_pad, L_pad;
   bool tall, square, aurora;
   int ns_t;
-  int n_rt, n_ct, n_seg, n_rmv;
+  int n_rt, n_ct, n_seg, n_rmv, wband;
   size_t o_xn, o_x[2], o_xt[2], o_a, o_b, o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
       o_pwpart, o_tailpart, o_linepart, o_scal, o_ist;
 };
+
+// The fused power pass takes matrices up to kFusedCols columns whose rows are
+// whole 16-byte chunks of the NS type (it loads 8-element chunks only); it
+// depends on the matrix alone, never on the rest of the batch.
+inline bool fused_power(const MatInfo& m) {
+  return m.cols <= kFusedCols && ((size_t)m.cols * (m.ns_t == DT_BF16 ? 2 : 4)) % 16 == 0;
+}
 
 // Host copy of one LaunchList: offset of its int arrays in the meta buffer.
 struct HostList {
@@ -84,6 +94,7 @@ struct HostList {
   int nblk = 0;
   size_t off_off = 0, off_mat = 0;  // byte offsets into meta
   double bytes = 0;                 // algorithmic bytes of one launch over it
+  int max_cols = 0;                 // widest matrix in the list (the fused power pass sizes its LDS by it)
 };
 
 struct GemmList {
@@ -98,6 +109,10 @@ struct GemmList {
 // its last round leaves CUs idle, while 128-tiles (two workgroups per CU)
 // cover the CUs in finer steps. MUON_NS_TILE=128 or 256 forces one size.
 constexpr int kSmallLaunchTiles = 768;
+// Fused power pass: band rows go down from kRmvRows to kFusedMinBand until a
+// launch has at least kFusedMinBlocks blocks (four per CU).
+constexpr int kFusedMinBand = kFusedPart;
+constexpr int kFusedMinBlocks = 1024;
 
 struct Plan {
   int kind = 0;
@@ -106,7 +121,9 @@ struct Plan {
   int passes = 1;
   bool any_aurora = false;
   // lists
-  HostList stream, permat, lines, colblk, matvec, rmatvec, ascale;
+  HostList stream, permat, lines, colblk, matvec, ascale;
+  HostList fused[2];                      // power rounds: fused X^T X v pass, one list per NS type
+  HostList matvec_w, rmatvec_w;           // X v + X^T u for matrices wider than kFusedCols
   HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
   HostList dupdate[2];      // [ns_t]
   GemmList gemm[2][2][3];   // [group][ns_t][mode]
@@ -229,6 +246,7 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
     m.n_rt = cdiv(m.rows, kStreamRows);
     m.n_ct = cdiv(m.cols, kStreamCols);
     m.n_seg = cdiv(m.cols, kSegCols);
+    m.wband = kRmvRows;
     m.n_rmv = cdiv(m.rows, kRmvRows);
     const size_t e = esz(m.ns_t);
     const size_t nsl = (size_t)m.s_pad * m.L_pad * e;
@@ -247,7 +265,10 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
     m.o_dvec = take((size_t)m.L * 4);
     m.o_pu = take((size_t)m.rows * 4);
     m.o_pv = take((size_t)m.cols * 4);
-    m.o_pwpart = take(kind == KIND_UPDATE ? (size_t)m.n_rmv * m.cols * 4 : 4);
+    // partial w rows: one per kRmvRows rows, or per kFusedPart rows for the fused pass
+    m.o_pwpart = take(kind == KIND_UPDATE ? (size_t)cdiv(m.rows, fused_power(m) ? kFusedPart : kRmvRows) *
+                                                m.cols * 4
+                                          : 4);
     m.o_tailpart = take(std::max((size_t)m.n_rt * m.n_seg * 4, (size_t)cdiv(m.L, 4)) * 4);
     m.o_linepart = take((size_t)2 * line_blocks(m.rows, m.cols) * 4);
     m.o_scal = take(SC_COUNT * 4);
@@ -279,9 +300,43 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
   for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].cols, 256);
   add_list(meta, P->colblk, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].rows, 16);   // 4 waves x 4 rows
-  add_list(meta, P->matvec, all, blocks);
-  for (int i = 0; i < nm; ++i) blocks[i] = P->mats[i].n_rmv * P->mats[i].n_ct;
-  add_list(meta, P->rmatvec, all, blocks);
+  add_list(meta, P->matvec, all, blocks);   // the final X v of every matrix
+  {
+    // Power rounds: the matrices fused_power() takes run the fused X^T X v
+    // pass, one launch per NS type, widest first; the others take X v then
+    // X^T u. A fused block takes a band of rows: the widest of 256, 128, 64
+    // that still gives its launch kFusedMinBlocks blocks (a few matrices need
+    // narrow bands to fill the CUs; many take wide ones, which spend less on
+    // per-block set-up). The partial sums do not depend on the band.
+    std::vector<int> wm, wb, wr;
+    for (int t = 0; t < 2; ++t) {
+      std::vector<int> fm;
+      for (int i = 0; i < nm; ++i)
+        if (fused_power(P->mats[i]) && P->mats[i].ns_t == t) fm.push_back(i);
+      std::stable_sort(fm.begin(), fm.end(), [&](int a, int b) { return P->mats[a].cols > P->mats[b].cols; });
+      int band = kRmvRows;
+      for (; band > kFusedMinBand; band /= 2) {
+        long nb = 0;
+        for (int i : fm) nb += cdiv(P->mats[i].rows, band);
+        if (nb >= kFusedMinBlocks) break;
+      }
+      std::vector<int> fb;
+      for (int i : fm) {
+        MatInfo& m = P->mats[i];
+        m.wband = band;
+        m.n_rmv = cdiv(m.rows, kFusedPart);
+        fb.push_back(cdiv(m.rows, band));
+        P->fused[t].max_cols = std::max(P->fused[t].max_cols, m.cols);
+      }
+      add_list(meta, P->fused[t], fm, fb);
+    }
+    for (int i = 0; i < nm; ++i) {
+      const MatInfo& m = P->mats[i];
+      if (!fused_power(m)) { wm.push_back(i); wb.push_back(cdiv(m.rows, 16)); wr.push_back(m.n_rmv * m.n_ct); }
+    }
+    add_list(meta, P->matvec_w, wm, wb);
+    add_list(meta, P->rmatvec_w, wm, wr);
+  }
   (void)bytes_stream;
 
   for (int g = 0; g < 2; ++g)
@@ -566,7 +621,7 @@ muon_status run(muon_handle* h, const Call& c) {
     }
     d.rows = m.rows; d.cols = m.cols; d.s = m.s; d.L = m.L; d.s_pad = m.s_pad; d.L_pad = m.L_pad;
     d.tall = m.tall; d.square = m.square; d.aurora = m.aurora; d.ns_t = m.ns_t;
-    d.n_rt = m.n_rt; d.n_ct = m.n_ct; d.n_seg = m.n_seg; d.n_rmv = m.n_rmv;
+    d.n_rt = m.n_rt; d.n_ct = m.n_ct; d.n_seg = m.n_seg; d.n_rmv = m.n_rmv; d.wband = m.wband;
     d.xn = c.kind == KIND_UPDATE ? ws + m.o_xn : nullptr;
     d.x[0] = ws + m.o_x[0]; d.x[1] = ws + m.o_x[1];
     d.xt[0] = ws + m.o_xt[0]; d.xt[1] = ws + m.o_xt[1];
@@ -588,7 +643,7 @@ muon_status run(muon_handle* h, const Call& c) {
   const bool contra = upd && cfg.contra != 0.f;
 
   // algorithmic byte counts for the profile
-  double el_ns = 0, el_all = 0;
+  double el_ns = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
   double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}};
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
@@ -596,6 +651,7 @@ muon_status run(muon_handle* h, const Call& c) {
     const DevMat& d = dm[i];
     el_all += el;
     el_ns += el * esz(m.ns_t);
+    (fused_power(m) ? el_fused[m.ns_t] : el_wide) += el * esz(m.ns_t);
     b_mom += upd ? el * (esz(d.dt_g) + 8 + esz(m.ns_t)) : el * esz(d.dt_g);
     b_tail_r += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? esz(d.dt_w) : 0));
     b_tail_a += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? 2 * esz(d.dt_w) : 0) + (d.uo ? esz(d.dt_uo) : 0));
@@ -621,13 +677,21 @@ muon_status run(muon_handle* h, const Call& c) {
   // 2. power iteration
   if (contra) {
     for (int r = 0; r <= cfg.power_steps; ++r) {
-      {
-        ProfScope ps(h, 1, el_ns);
-        CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(*P, P->matvec), P->matvec.nblk, cfg.power_steps, 0, st));
+      for (int t = 0; t < 2; ++t) {
+        const HostList& F = P->fused[t];
+        if (!F.nblk) continue;
+        ProfScope ps(h, 1, el_fused[t]);
+        CHECK_LAUNCH(h, launch_power_fused(t, D, dev_list(*P, F), F.nblk, cfg.power_steps, F.max_cols, st));
       }
-      {
-        ProfScope ps(h, 1, el_ns);
-        CHECK_LAUNCH(h, launch_power_rmatvec(D, dev_list(*P, P->rmatvec), P->rmatvec.nblk, cfg.power_steps, st));
+      if (P->matvec_w.nblk) {
+        {
+          ProfScope ps(h, 1, el_wide);
+          CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(*P, P->matvec_w), P->matvec_w.nblk, cfg.power_steps, 0,
+                                              st));
+        }
+        ProfScope ps(h, 1, el_wide);
+        CHECK_LAUNCH(h, launch_power_rmatvec(D, dev_list(*P, P->rmatvec_w), P->rmatvec_w.nblk, cfg.power_steps,
+                                             st));
       }
       {
         ProfScope ps(h, 1, 0);

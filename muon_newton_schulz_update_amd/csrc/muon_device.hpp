@@ -22,7 +22,9 @@ constexpr int kStreamRows = 32;   // rows per tile of the streaming kernels (4 w
 constexpr int kWaveRows = 8;      // rows per wave of a streaming tile, loaded in one batch
 constexpr int kSegCols = 512;     // columns per streaming tile (a lane covers 8 of them)
 constexpr int kStreamCols = 2048; // columns per tile of the X^T u kernel
-constexpr int kRmvRows = 256;     // rows per tile of the X^T u kernel
+constexpr int kRmvRows = 256;     // rows per tile of the X^T u kernel (and the fused pass's widest band)
+constexpr int kFusedCols = 12288; // widest matrix the fused X^T X v pass takes (its v sits in LDS)
+constexpr int kFusedPart = 64;    // rows per partial w of the fused pass (fixed: results do not depend on batching)
 
 enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1 };
 
@@ -61,7 +63,8 @@ struct DevMat {
   int32_t ns_t;     // DT_F32 or DT_BF16: type of xn, x, xt, a, b
   int32_t n_rt, n_ct;   // ceil(rows / kStreamRows), ceil(cols / kStreamCols)
   int32_t n_seg;        // ceil(cols / kSegCols): streaming tiles are n_rt x n_seg
-  int32_t n_rmv;        // ceil(rows / kRmvRows)
+  int32_t n_rmv;        // partial w rows of the power step: ceil(rows / kRmvRows), fused: ceil(rows / kFusedPart)
+  int32_t wband;        // rows per block of the fused pass (a multiple of kFusedPart)
   // workspace
   void* xn;
   void* x[2];
@@ -76,7 +79,7 @@ struct DevMat {
   float* dvec;      // L : Aurora preconditioner D
   float* pu;        // rows : u = X v
   float* pv;        // cols : v
-  float* pwpart;    // n_rmv x cols : partial X^T u
+  float* pwpart;    // n_rmv x cols : partial w per row band
   float* tailpart;  // n_rt * n_seg * 4 : partial tail sums per streaming tile
   float* linepart;  // 2 * (ceil(rows/256) + (rows < cols ? ceil(cols/256) : 0)): per-block norm
                     // partials of the line sums; reused for the blocks of ||w||^2

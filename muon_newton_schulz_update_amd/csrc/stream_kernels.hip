@@ -644,6 +644,227 @@ __global__ __launch_bounds__(256) void k_power_rmatvec(const DevMat* __restrict_
   else rmatvec_body<float>(M, local);
 }
 
+// Row-fused power step, for matrices with at most kFusedCols columns: a
+// block takes a band of M.wband rows (256, 128 or 64, chosen per plan so that
+// a launch has enough blocks) and writes, for each kFusedPart rows of it,
+// w_part = (X/||X||)^T (X/||X||) v over those rows, with X read once.
+// Thread t owns the 8-column chunks c = 8 t + 2048 j (j < J). A group of R
+// rows is loaded into registers; the block reduces the rows' dot products
+// with v (u_i, fixed order: each wave's lanes, then the four waves), and the
+// same registers then add u_i X_i into the thread's part of w. Output:
+// pwpart[part][c], summed over the parts in order by k_power_wsum as it sums
+// the X^T u kernel's partials.
+template <typename T>
+__device__ __forceinline__ typename Ty<T>::Raw ld_raw_part(const void* b, size_t i, int n) {
+  float v[8];
+  ld_part<T>(b, i, n, v);
+  typename Ty<T>::Raw q;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = f2bf(v[e]);   // exact: v holds bf16 values
+  } else {
+    q.a = (f32x4_t){v[0], v[1], v[2], v[3]};
+    q.b = (f32x4_t){v[4], v[5], v[6], v[7]};
+  }
+  return q;
+}
+
+// 8 consecutive elements through a buffer resource (16 or 32 bytes; a read
+// past the resource's range returns zeros).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ typename Ty<T>::Raw ld_rsrc(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typename Ty<T>::Raw q;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    q = __builtin_bit_cast(u16x8_t, v);
+  } else {
+    q.a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    q.b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0));
+  }
+  return q;
+}
+
+// Sum over the wave in a fixed order, valid in every lane: DPP exchanges
+// within each row of 16 lanes (pairs, quads, halves, rows), then the four
+// row sums read from lanes 0, 16, 32 and 48.
+template <int ctrl>
+__device__ __forceinline__ float dpp_sum_step(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_sum_step<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_sum_step<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_sum_step<0x141>(v);   // row_half_mirror
+  v = dpp_sum_step<0x140>(v);   // row_mirror
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a + b) + (c + d);
+}
+
+// Marks loaded chunks as changed, so the compiler converts them again after
+// the barrier instead of holding both the raw and the converted values
+// (twice the registers) across it.
+__device__ __forceinline__ void keep_raw(u16x8_t& q) { asm volatile("" : "+v"(q)); }
+__device__ __forceinline__ void keep_raw(Ty<float>::Raw& q) {
+  asm volatile("" : "+v"(q.a));
+  asm volatile("" : "+v"(q.b));
+}
+
+// One group of R rows of a fused block: its chunks, loaded through the
+// block's resource (rows past the matrix read as zeros without touching
+// memory, so every group issues the same loads).
+template <typename T, int J, int R>
+struct FusedGroup {
+  typename Ty<T>::Raw q[R][J];
+  // Rows are 16-byte multiples (the planner sends other matrices to the X v,
+  // X^T u kernels), so chunks are whole; a chunk past the row's end reads
+  // other data that neither the dot products nor the stored sums use.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rx, int rowb, int row0, int rb0) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        q[k][j] = ld_rsrc<T>(rx, (8 * t + 2048 * j) * (int)sizeof(T), (row0 + k - rb0) * rowb);
+  }
+  // u_k = (X_{row0+k} . v) / ||X||, reduced over the block (each wave's
+  // lanes, then the four waves in order); then acc += u_k X_{row0+k} for the
+  // rows of the matrix, in row order.
+  __device__ __forceinline__ void step(const DevMat& M, int row0, const float* vsh, float (*red)[4][16], int buf,
+                                       float inv, float (&acc)[J][8]) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, cols = M.cols;
+    float p[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) p[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = 8 * t + 2048 * j;
+      if (c < cols) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = vsh[c + e];   // zero past cols
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+          float x[8];
+          Ty<T>::cvt(q[k][j], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[k] += x[e] * v[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) p[k] = wave_sum_dpp(p[k]);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) red[buf][w][k] = p[k];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int j = 0; j < J; ++j) keep_raw(q[k][j]);
+    __syncthreads();   // red[buf] is rewritten two groups later, after the next group's barrier
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (row0 + k >= M.rows) break;   // uniform
+      const float u = (red[buf][0][k] + red[buf][1][k] + red[buf][2][k] + red[buf][3][k]) * inv;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float x[8];
+        Ty<T>::cvt(q[k][j], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] += u * x[e];
+      }
+    }
+  }
+};
+
+// A block's groups in order, two register buffers: group g+1's loads are in
+// flight during group g's reduction, barrier and accumulation. One partial w
+// per kFusedPart rows (R divides it), whatever the block's band, so the sums
+// do not depend on how the rows were grouped into blocks.
+template <typename T, int J, int R>
+__device__ __forceinline__ void fused_body(const DevMat& M, int band, const float* vsh, float (*red)[4][16]) {
+  static_assert(kFusedPart % R == 0, "groups tile a part");
+  const int t = threadIdx.x, cols = M.cols;
+  const float inv = inv_fro(M);
+  const int rb0 = band * M.wband, rbn = min(M.wband, M.rows - rb0);
+  const int rowb = cols * (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)M.xn + (size_t)rb0 * rowb), (short)0, rbn * rowb, 0x00020000);
+  constexpr int kGpp = kFusedPart / R;     // groups per part
+  const int ng = (rbn + R - 1) / R;        // groups holding rows of the matrix (uniform)
+  float acc[J][8];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  auto flush = [&](int g) {   // after group g: write and reset the part's sums at its end
+    if ((g + 1) % kGpp != 0 && g + 1 != ng) return;
+    const int part = rb0 / kFusedPart + g / kGpp;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = 8 * t + 2048 * j;
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[e] = acc[j][e] * inv;
+        acc[j][e] = 0.f;
+      }
+      // cols is a multiple of 4 and the array 256-byte aligned: 16-byte stores
+      float* dst = M.pwpart + (size_t)part * cols + c;
+      if (c < cols) gst<f32x4_t>(dst, (f32x4_t){o[0], o[1], o[2], o[3]});
+      if (c + 4 < cols) gst<f32x4_t>(dst + 4, (f32x4_t){o[4], o[5], o[6], o[7]});
+    }
+  };
+  FusedGroup<T, J, R> ga, gb;
+  ga.load(rx, rowb, rb0, rb0);
+  for (int g = 0; g < ng; g += 2) {
+    gb.load(rx, rowb, rb0 + (g + 1) * R, rb0);
+    ga.step(M, rb0 + g * R, vsh, red, 0, inv, acc);
+    flush(g);
+    ga.load(rx, rowb, rb0 + (g + 2) * R, rb0);
+    if (g + 1 < ng) {
+      gb.step(M, rb0 + (g + 1) * R, vsh, red, 1, inv, acc);
+      flush(g + 1);
+    }
+  }
+}
+
+// R rows per group (a power of two): at most 16 raw chunks per thread and
+// buffer for bf16, 4 for fp32.
+constexpr int pow2_floor(int x) { return x >= 8 ? 8 : x >= 4 ? 4 : x >= 2 ? 2 : 1; }
+template <typename T, int J>
+__device__ __forceinline__ void fused_dispatch_r(const DevMat& M, int band, const float* vsh, float (*red)[4][16]) {
+  constexpr int R = pow2_floor((sizeof(T) == 2 ? 16 : 4) / J);
+  fused_body<T, J, R>(M, band, vsh, red);
+}
+// Dynamic LDS: v, padded with zeros to the launch's widest matrix rounded up
+// to 8 columns (at most kFusedCols). One launch per NS type (the fp32 forms
+// need more registers); a block takes the form for its matrix's chunk count
+// J = ceil(cols / 2048), so matrices of all widths share the launch.
+template <typename T>
+__global__ __launch_bounds__(256) void k_power_fused(const DevMat* __restrict__ mats, LaunchList L, int steps) {
+  extern __shared__ float vsh[];
+  __shared__ float red[2][4][16];
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  if (M.ist[IS_PSTEPS] >= steps) return;
+  const int cp = (M.cols + 7) & ~7;
+  for (int c = threadIdx.x; c < cp; c += 256) vsh[c] = c < M.cols ? gld<float>(M.pv + c) : 0.f;
+  __syncthreads();
+  switch ((M.cols + 2047) / 2048) {
+    case 1: fused_dispatch_r<T, 1>(M, local, vsh, red); break;
+    case 2: fused_dispatch_r<T, 2>(M, local, vsh, red); break;
+    case 3: fused_dispatch_r<T, 3>(M, local, vsh, red); break;
+    case 4: fused_dispatch_r<T, 4>(M, local, vsh, red); break;
+    case 5: fused_dispatch_r<T, 5>(M, local, vsh, red); break;
+    default: fused_dispatch_r<T, 6>(M, local, vsh, red); break;
+  }
+}
+
 // w = sum over the row tiles of the partials (one thread per column, stored
 // in row 0 of the partials); block b of a matrix writes linepart[b] = its
 // part of ||w||^2.
@@ -1011,6 +1232,15 @@ hipError_t launch_power_matvec(const DevMat* m, LaunchList L, int nblk, int step
 }
 hipError_t launch_power_rmatvec(const DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st) {
   LAUNCH(k_power_rmatvec, nblk, m, L, steps);
+  return hipGetLastError();
+}
+hipError_t launch_power_fused(int ns_t, const DevMat* m, LaunchList L, int nblk, int steps, int max_cols,
+                              hipStream_t st) {
+  if (max_cols > kFusedCols || max_cols < 1) return hipErrorInvalidValue;
+  const size_t lds = (size_t)((max_cols + 7) & ~7) * sizeof(float);
+  if (nblk <= 0) return hipSuccess;
+  if (ns_t == DT_BF16) hipLaunchKernelGGL(k_power_fused<__bf16>, dim3(nblk), dim3(256), lds, st, m, L, steps);
+  else hipLaunchKernelGGL(k_power_fused<float>, dim3(nblk), dim3(256), lds, st, m, L, steps);
   return hipGetLastError();
 }
 hipError_t launch_power_wsum(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st) {
