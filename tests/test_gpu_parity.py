@@ -387,6 +387,20 @@ def test_update_many_small_matrices(dev):
     say(f"  worst rel(V) over 1500 matrices {worst:.2e}")
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, FP32_TOL), (torch.bfloat16, BF16_TOL)])
+def test_update_power_step_forms(dev, dtype, tol):
+    """The power step's forms in one call: the fused X^T X v pass for 1 to 6
+    chunks of 2048 columns (up to its 12288-column limit), and the X v, X^T u
+    kernels for a matrix past that limit and for one with ragged rows."""
+    say(f"muon_update power-step forms {dtype}")
+    shapes = [(70, 2000), (130, 4000), (70, 6000), (200, 8000), (64, 10000), (96, 12288), (40, 12304), (50, 3001)]
+    mats = [gen.custom_matrix(sh, 2100 + i, dev, grad_dtype=dtype, grad_sd=1e-3, mom_sd=1e-3, weight_dtype=dtype)
+            for i, sh in enumerate(shapes)]
+    G, M0, W0, M, V, W = run_update(dev, mats)
+    for i in range(len(shapes)):
+        check_update(f"power[{shapes[i]}]", G[i], M0[i], W0[i], M[i], V[i], W[i], mu.default_config(), tol)
+
+
 def test_update_mixed_dtypes_in_one_call(dev):
     say("muon_update fp32 and bf16 matrices in one call")
     a = gen.custom_matrix((200, 90), 800, dev)
