@@ -654,21 +654,6 @@ __global__ __launch_bounds__(256) void k_power_rmatvec(const DevMat* __restrict_
 // same registers then add u_i X_i into the thread's part of w. Output:
 // pwpart[part][c], summed over the parts in order by k_power_wsum as it sums
 // the X^T u kernel's partials.
-template <typename T>
-__device__ __forceinline__ typename Ty<T>::Raw ld_raw_part(const void* b, size_t i, int n) {
-  float v[8];
-  ld_part<T>(b, i, n, v);
-  typename Ty<T>::Raw q;
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = f2bf(v[e]);   // exact: v holds bf16 values
-  } else {
-    q.a = (f32x4_t){v[0], v[1], v[2], v[3]};
-    q.b = (f32x4_t){v[4], v[5], v[6], v[7]};
-  }
-  return q;
-}
-
 // 8 consecutive elements through a buffer resource (16 or 32 bytes; a read
 // past the resource's range returns zeros).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
