@@ -18,8 +18,8 @@
  *  - Batches: every call takes n descriptors of mixed shapes and types; each
  *    matrix is processed on its own (its own norms, preconditioner and power
  *    iteration) and the batch is fused into shared kernel launches.
- *  - Limits: rows, cols <= 65536, min(rows, cols) <= 16384 and
- *    rows * cols < 2^31 per matrix.
+ *  - Limits: rows, cols <= 65536, min(rows, cols) <= 16384,
+ *    rows * cols < 2^31 and ld <= 2^40 per matrix.
  *  - Precision: a matrix whose input is MUON_BF16 runs Newton-Schulz on bf16
  *    matrix cores with fp32 accumulation; a MUON_F32 input runs it with fp32
  *    matrix-core arithmetic throughout. Norms, the preconditioner, the power

@@ -41,6 +41,8 @@ int check_matrix(const muon_matrix& m, const char* what, int i, char* msg, int l
   if (m.ld < m.cols)
     return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: ld %lld < cols %lld", what, i, (long long)m.ld,
                 (long long)m.cols);
+  if (m.ld > kMaxLd)
+    return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: ld %lld exceeds 2^40", what, i, (long long)m.ld);
   if (m.rows > kMaxDim || m.cols > kMaxDim)
     return fail(msg, len, MUON_ERR_SHAPE_MISMATCH, "%s[%d]: %lld x %lld exceeds the %d per-dimension limit", what, i,
                 (long long)m.rows, (long long)m.cols, kMaxDim);

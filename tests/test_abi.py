@@ -82,6 +82,7 @@ def test_valid_batch_passes(lib):
     ("null_ptr", INVALID), ("ld_lt_cols", SHAPE), ("bad_dtype", DTYPE), ("mom_bf16", DTYPE),
     ("shape_mismatch", SHAPE), ("weight_mismatch", SHAPE), ("out_mismatch", SHAPE),
     ("negative", SHAPE), ("too_big", SHAPE), ("short_too_big", SHAPE), ("misaligned", INVALID),
+    ("ld_too_big", SHAPE),
 ])
 def test_update_validation(lib, case, code):
     g, mom, w, uo = [m(4, 8)], [m(4, 8, 0)], None, None
@@ -107,6 +108,8 @@ def test_update_validation(lib, case, code):
         g, mom = [m(20000, 20000)], [m(20000, 20000, 0)]
     elif case == "misaligned":
         g = [m(4, 8, ptr=FAKE + 1)]
+    elif case == "ld_too_big":
+        g = [m(4, 8, ld=(1 << 40) + 1)]
     rc, msg = mu.check_update_args(g, mom, w, uo)
     assert rc == code, (case, rc, msg)
     assert msg
