@@ -528,6 +528,54 @@ def test_update_power_restart(dev):
     check_update("restart", G[0], M0[0], W0[0], M[0], V[0], W[0], mu.default_config(), FP32_TOL)
 
 
+def test_update_resume_equals_uninterrupted(dev):
+    """The library keeps no state between calls: two steps on one handle equal
+    step 1, momentum and weights saved to the host, a fresh handle, the state
+    restored and step 2, bit for bit."""
+    say("muon_update: step k, save, reload, step k+1 == uninterrupted")
+    shapes = [(300, 140), (140, 300), (256, 256)]
+    first = [gen.custom_matrix(sh, 2400 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3, mom_sd=1e-3,
+                               weight_dtype=torch.bfloat16) for i, sh in enumerate(shapes)]
+    second = [gen.custom_matrix(sh, 2500 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3)[0]
+              for i, sh in enumerate(shapes)]
+    g1 = [g for g, _, _ in first]
+    # uninterrupted: both steps on one handle
+    h = mu.Handle(dev.index)
+    try:
+        M = [m.clone() for _, m, _ in first]
+        W = [w.clone() for _, _, w in first]
+        V = [torch.empty(sh, device=dev) for sh in shapes]
+        mu.muon_update(g1, M, W, update_out=V, handle=h)
+        mu.muon_update(second, M, W, update_out=V, handle=h)
+        torch.cuda.synchronize()
+    finally:
+        h.close()
+    # interrupted: step 1, save to the host, new handle, restore, step 2
+    ha = mu.Handle(dev.index)
+    try:
+        Ma = [m.clone() for _, m, _ in first]
+        Wa = [w.clone() for _, _, w in first]
+        mu.muon_update(g1, Ma, Wa, handle=ha)
+        torch.cuda.synchronize()
+        saved = ([t.cpu() for t in Ma], [t.cpu() for t in Wa])
+    finally:
+        ha.close()
+    del Ma, Wa
+    hb = mu.Handle(dev.index)
+    try:
+        Mb = [t.to(dev) for t in saved[0]]
+        Wb = [t.to(dev) for t in saved[1]]
+        Vb = [torch.empty(sh, device=dev) for sh in shapes]
+        mu.muon_update(second, Mb, Wb, update_out=Vb, handle=hb)
+        torch.cuda.synchronize()
+    finally:
+        hb.close()
+    for i in range(len(shapes)):
+        assert torch.equal(M[i], Mb[i]), i
+        assert torch.equal(W[i], Wb[i]), i
+        assert torch.equal(V[i], Vb[i]), i
+
+
 def test_update_deterministic(dev):
     say("muon_update bitwise determinism")
     mats = [gen.custom_matrix(s, 1100 + i, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16)
