@@ -654,18 +654,21 @@ __global__ __launch_bounds__(256) void k_power_rmatvec(const DevMat* __restrict_
 // same registers then add u_i X_i into the thread's part of w. Output:
 // pwpart[part][c], summed over the parts in order by k_power_wsum as it sums
 // the X^T u kernel's partials.
-// 8 consecutive elements through a buffer resource (16 or 32 bytes; a read
-// past the resource's range returns zeros).
+// 8 consecutive elements at byte offset `off` of a buffer resource (16 or 32
+// bytes). The whole offset goes in the per-lane offset and the scalar offset
+// is zero: the range check compares only the per-lane offset with the
+// resource's size, so this is what makes a read past the range return zeros
+// without touching memory.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 template <typename T>
-__device__ __forceinline__ typename Ty<T>::Raw ld_rsrc(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+__device__ __forceinline__ typename Ty<T>::Raw ld_rsrc(__amdgpu_buffer_rsrc_t r, int off) {
   typename Ty<T>::Raw q;
   if constexpr (sizeof(T) == 2) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     q = __builtin_bit_cast(u16x8_t, v);
   } else {
-    q.a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-    q.b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0));
+    q.a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    q.b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
   }
   return q;
 }
@@ -713,7 +716,7 @@ struct FusedGroup {
     for (int k = 0; k < R; ++k)
 #pragma unroll
       for (int j = 0; j < J; ++j)
-        q[k][j] = ld_rsrc<T>(rx, (8 * t + 2048 * j) * (int)sizeof(T), (row0 + k - rb0) * rowb);
+        q[k][j] = ld_rsrc<T>(rx, (row0 + k - rb0) * rowb + (8 * t + 2048 * j) * (int)sizeof(T));
   }
   // u_k = (X_{row0+k} . v) / ||X||, reduced over the block (each wave's
   // lanes, then the four waves in order); then acc += u_k X_{row0+k} for the
