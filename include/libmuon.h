@@ -208,7 +208,10 @@ muon_status muon_reserve(muon_handle* handle, int n, const muon_matrix* shapes);
  * A = X X^T formed on the short side.
  *   in[i]   input, any shape, F32 or BF16; read only.
  *   out[i]  output, same shape as in[i], F32 or BF16 (rounded to nearest
- *           even); may alias in[i] exactly.
+ *           even). An output may share memory with any input, in place or
+ *           not: every input is read before the first output is written.
+ *           Outputs must not share an element with one another
+ *           (MUON_ERR_INVALID_ARG); column slices of one buffer do not.
  *   cfg     ns_* fields are used; NULL = defaults.
  */
 muon_status ns_polar(muon_handle* handle, int n, const muon_matrix* in,
@@ -248,7 +251,11 @@ muon_status aurora_orthogonalize(muon_handle* handle, int n,
  *   update_out    NULL, or update_out[i] receives V after the floor and
  *                 before lr (F32 or BF16; ptr NULL = not wanted).
  *   cfg           NULL = defaults.
- * update_out must not overlap grad, momentum or weight.
+ * Every buffer the call writes (momentum, weight, update_out) must not share
+ * an element with any other buffer of the call, of the same matrix or
+ * another: MUON_ERR_INVALID_ARG names the first such pair. Grads may share
+ * memory with one another (they are only read), and column slices of one
+ * buffer (same ld, disjoint columns) share no element.
  */
 muon_status muon_update(muon_handle* handle, int n, const muon_matrix* grad,
                         const muon_matrix* momentum, const muon_matrix* weight,

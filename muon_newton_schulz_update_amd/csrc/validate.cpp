@@ -7,6 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "../../include/libmuon.h"
 #include "validate.hpp"
 
@@ -58,6 +61,90 @@ int check_matrix(const muon_matrix& m, const char* what, int i, char* msg, int l
   return MUON_OK;
 }
 
+// Buffers of one call that share memory. A matrix occupies the byte
+// intervals [ptr + r ld e, ptr + r ld e + cols e) for r < rows (e = element
+// size): disjoint and in address order, since ld >= cols. Two matrices
+// overlap when one of these intervals meets one of the other's, so column
+// slices of one parent buffer (same ld, disjoint columns) do not overlap.
+// Offsets are 128-bit: rows x ld x e reaches 2^58 and the pointer adds to it.
+typedef unsigned __int128 u128;
+struct Span {
+  u128 lo, hi;     // first byte; one past the last row's last byte
+  u128 ldb, rowb;  // row stride and row length, in bytes
+  int64_t rows;
+  const char* what;
+  int idx;
+  bool writes;     // the call writes this buffer
+};
+
+Span make_span(const muon_matrix& m, const char* what, int idx, bool writes) {
+  const u128 e = (u128)elem_size(m.dtype);
+  Span s;
+  s.lo = (u128)(uintptr_t)m.ptr;
+  s.ldb = (u128)m.ld * e;
+  s.rowb = (u128)m.cols * e;
+  s.rows = m.rows;
+  s.hi = s.lo + (u128)(m.rows - 1) * s.ldb + s.rowb;
+  s.what = what;
+  s.idx = idx;
+  s.writes = writes;
+  return s;
+}
+
+bool spans_meet(const Span& a, const Span& b) {
+  if (a.hi <= b.lo || b.hi <= a.lo) return false;
+  const Span& p = a.lo <= b.lo ? a : b;   // starts first
+  const Span& q = a.lo <= b.lo ? b : a;
+  if (p.ldb == q.ldb) {
+    // q's row s starts at byte `rem` of p's row k + s and, when it runs past
+    // that row's stride, ends in row k + s + 1 (never further: rowb <= ldb)
+    const u128 d = q.lo - p.lo, k = d / p.ldb, rem = d % p.ldb, prow = (u128)p.rows;
+    if (k < prow && rem < p.rowb) return true;
+    return rem + q.rowb > p.ldb && k + 1 < prow;
+  }
+  // different strides: for each row of the matrix with fewer rows, the other
+  // matrix's last row starting before that row's end is the only one that
+  // can reach into it
+  const Span& x = a.rows <= b.rows ? a : b;
+  const Span& y = a.rows <= b.rows ? b : a;
+  for (int64_t r = 0; r < x.rows; ++r) {
+    const u128 x0 = x.lo + (u128)r * x.ldb, x1 = x0 + x.rowb;
+    if (x1 <= y.lo) continue;
+    if (x0 >= y.hi) break;
+    u128 t = (x1 - 1 - y.lo) / y.ldb;
+    if (t >= (u128)y.rows) t = (u128)y.rows - 1;
+    if (y.lo + t * y.ldb + y.rowb > x0) return true;
+  }
+  return false;
+}
+
+// Sweep in address order; `outputs_may_overlap_inputs`: a pair of one
+// written and one read-only buffer is allowed (the polar entry points read
+// every input before they write the first output).
+int check_overlaps(std::vector<Span>& v, bool outputs_may_overlap_inputs, char* msg, int len) {
+  std::stable_sort(v.begin(), v.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  std::vector<int> live;   // earlier spans that may still reach the current one
+  for (int i = 0; i < (int)v.size(); ++i) {
+    size_t k = 0;
+    for (int j : live)
+      if (v[j].hi > v[i].lo) live[k++] = j;
+    live.resize(k);
+    for (int j : live) {
+      const Span& a = v[j];
+      const Span& b = v[i];
+      if (!a.writes && !b.writes) continue;
+      if (outputs_may_overlap_inputs && a.writes != b.writes) continue;
+      if (spans_meet(a, b))
+        return fail(msg, len, MUON_ERR_INVALID_ARG, "%s[%d] and %s[%d] share memory", a.what, a.idx, b.what,
+                    b.idx);
+    }
+    live.push_back(i);
+  }
+  return MUON_OK;
+}
+
+bool nonempty(const muon_matrix& m) { return m.rows > 0 && m.cols > 0; }
+
 int same_shape(const muon_matrix& a, const muon_matrix& b, const char* wa, const char* wb, int i, char* msg,
                int len) {
   if (a.rows != b.rows || a.cols != b.cols)
@@ -103,7 +190,12 @@ int check_polar(int n, const muon_matrix* in, const muon_matrix* out, const muon
     if ((rc = check_matrix(out[i], "out", i, msg, len))) return rc;
     if ((rc = same_shape(in[i], out[i], "in", "out", i, msg, len))) return rc;
   }
-  return MUON_OK;
+  std::vector<Span> v;
+  for (int i = 0; i < n; ++i) {
+    if (nonempty(in[i])) v.push_back(make_span(in[i], "in", i, false));
+    if (nonempty(out[i])) v.push_back(make_span(out[i], "out", i, true));
+  }
+  return check_overlaps(v, true, msg, len);
 }
 
 int check_update(int n, const muon_matrix* g, const muon_matrix* m, const muon_matrix* w, const muon_matrix* uo,
@@ -128,7 +220,14 @@ int check_update(int n, const muon_matrix* g, const muon_matrix* m, const muon_m
       if ((rc = same_shape(g[i], uo[i], "grad", "update_out", i, msg, len))) return rc;
     }
   }
-  return MUON_OK;
+  std::vector<Span> v;
+  for (int i = 0; i < n; ++i) {
+    if (nonempty(g[i])) v.push_back(make_span(g[i], "grad", i, false));
+    if (nonempty(m[i])) v.push_back(make_span(m[i], "momentum", i, true));
+    if (w && w[i].ptr && nonempty(w[i])) v.push_back(make_span(w[i], "weight", i, true));
+    if (uo && uo[i].ptr && nonempty(uo[i])) v.push_back(make_span(uo[i], "update_out", i, true));
+  }
+  return check_overlaps(v, false, msg, len);
 }
 
 }  // namespace muon

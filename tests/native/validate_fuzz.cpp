@@ -86,6 +86,88 @@ void pick_config(muon_config* c) {
   }
 }
 
+// The overlap rule restated by brute force: two buffers share memory when a
+// row of one meets a row of the other, as byte intervals.
+struct Buf {
+  uintptr_t p;
+  int64_t rows, cols, ld;
+  int esz;
+  bool writes;
+};
+bool meet(const Buf& a, const Buf& b) {
+  for (int64_t r = 0; r < a.rows; ++r)
+    for (int64_t s = 0; s < b.rows; ++s) {
+      const uintptr_t a0 = a.p + (uintptr_t)(r * a.ld * a.esz), a1 = a0 + (uintptr_t)(a.cols * a.esz);
+      const uintptr_t b0 = b.p + (uintptr_t)(s * b.ld * b.esz), b1 = b0 + (uintptr_t)(b.cols * b.esz);
+      if (a0 < b1 && b0 < a1) return true;
+    }
+  return false;
+}
+
+// Small matrices packed into a few hundred bytes, so that buffers often share
+// memory; every other rule holds, so the status is OK or INVALID_ARG exactly
+// as the restated overlap rule says.
+int overlap_fuzz() {
+  const uintptr_t arena = 0x100000;
+  auto place = [&](int64_t rows, int64_t cols, muon_dtype dt) {
+    muon_matrix x;
+    x.rows = rows;
+    x.cols = cols;
+    x.ld = cols + (int64_t)(rng() % 6);
+    x.dtype = dt;
+    x.ptr = (void*)(arena + 4 * (uintptr_t)(rng() % 200));
+    return x;
+  };
+  auto pick_dt = [&]() { return rng() % 2 ? MUON_F32 : MUON_BF16; };
+  auto buf = [](const muon_matrix& x, bool writes) {
+    return Buf{(uintptr_t)x.ptr, x.rows, x.cols, x.ld, x.dtype == MUON_BF16 ? 2 : 4, writes};
+  };
+  char msg[300];
+  int rejected = 0, total = 0;
+  for (int it = 0; it < 20000; ++it) {
+    const int n = 1 + (int)(rng() % 4);
+    std::vector<muon_matrix> g(n), m(n), w(n), o(n);
+    std::vector<Buf> bufs;
+    const bool update = it % 2 == 1;
+    for (int i = 0; i < n; ++i) {
+      const int64_t rows = 1 + (int64_t)(rng() % 12), cols = 1 + (int64_t)(rng() % 12);
+      g[i] = place(rows, cols, pick_dt());
+      o[i] = place(rows, cols, pick_dt());
+      if (update) {
+        m[i] = place(rows, cols, MUON_F32);
+        w[i] = place(rows, cols, pick_dt());
+        if (rng() % 3 == 0) w[i].ptr = nullptr;
+        if (rng() % 3 == 0) o[i].ptr = nullptr;
+      }
+      bufs.push_back(buf(g[i], false));
+      if (update) {
+        bufs.push_back(buf(m[i], true));
+        if (w[i].ptr) bufs.push_back(buf(w[i], true));
+      }
+      if (o[i].ptr) bufs.push_back(buf(o[i], true));
+    }
+    bool clash = false;
+    for (size_t a = 0; a < bufs.size() && !clash; ++a)
+      for (size_t b = a + 1; b < bufs.size() && !clash; ++b) {
+        if (!bufs[a].writes && !bufs[b].writes) continue;
+        if (!update && bufs[a].writes != bufs[b].writes) continue;   // an output over an input is allowed
+        clash = meet(bufs[a], bufs[b]);
+      }
+    const int rc = update ? muon_check_update_args(n, g.data(), m.data(), w.data(), o.data(), nullptr, msg, sizeof(msg))
+                          : muon_check_polar_args(n, g.data(), o.data(), nullptr, msg, sizeof(msg));
+    const int want = clash ? MUON_ERR_INVALID_ARG : MUON_OK;
+    if (rc != want) {
+      printf("overlap rule: call %d (%s, n=%d) returned %d, expected %d: %s\n", it, update ? "update" : "polar", n,
+             rc, want, msg);
+      return 1;
+    }
+    rejected += clash;
+    ++total;
+  }
+  printf("overlap %d calls, %d rejected\n", total, rejected);
+  return 0;
+}
+
 }  // namespace
 
 int main() {
@@ -126,6 +208,7 @@ int main() {
     }
     if (rc == MUON_OK) ++accepted;
   }
+  if (overlap_fuzz()) return 1;
   printf("ok %d calls, %d accepted\n", calls, accepted);
   return 0;
 }

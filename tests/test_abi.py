@@ -64,9 +64,14 @@ def test_status_strings(lib):
 
 
 FAKE = 0x10000  # never dereferenced: validation is host-only
+_fresh = [1 << 40]
 
 
-def m(rows, cols, dtype=1, ld=None, ptr=FAKE):
+def m(rows, cols, dtype=1, ld=None, ptr="fresh"):
+    """A descriptor; by default at an address of its own, 64 GiB from any other."""
+    if ptr == "fresh":
+        ptr = _fresh[0]
+        _fresh[0] += 1 << 36
     return MuonMatrix(ptr, rows, cols, cols if ld is None else ld, dtype)
 
 
@@ -143,6 +148,83 @@ def test_polar_validation(lib):
     assert mu.check_polar_args([m(5, 3)], [m(3, 5)])[0] == SHAPE
     assert mu.check_polar_args([m(5, 3)], [m(5, 3, 9)])[0] == DTYPE
     assert mu.check_polar_args([m(5, 3, ptr=None)], [m(5, 3)])[0] == INVALID
+
+
+BASE = 1 << 62   # far above every fresh address
+
+
+def at(off, rows, cols, ld, dtype=0):
+    """A descriptor at byte offset `off` of one parent allocation."""
+    return MuonMatrix(BASE + off, rows, cols, ld, dtype)
+
+
+@pytest.mark.parametrize("case,code", [
+    ("grad_is_momentum", INVALID), ("weight_is_grad", INVALID), ("out_is_grad", INVALID),
+    ("momentum_meets_other_weight", INVALID), ("out_meets_other_momentum", INVALID),
+    ("column_slices", OK), ("column_slices_one_shared", INVALID),
+    ("wraps_into_next_row", INVALID), ("ends_at_last_row", OK),
+    ("strides_differ_interleaved", OK), ("strides_differ_meet", INVALID),
+    ("grads_share", OK), ("bf16_out_inside_f32_gap", OK),
+])
+def test_update_buffer_overlap(lib, case, code):
+    """Buffers the call writes must share no element with any other buffer;
+    the check is exact per element, so slices of one parent are allowed."""
+    g, mom, w, uo = [m(4, 8, 0), m(4, 8, 0)], [m(4, 8, 0), m(4, 8, 0)], None, None
+    if case == "grad_is_momentum":
+        mom[1] = g[1]
+    elif case == "weight_is_grad":
+        w = [m(4, 8, 0), g[0]]
+    elif case == "out_is_grad":
+        uo = [g[1], MuonMatrix(None, 0, 0, 0, 0)]
+    elif case == "momentum_meets_other_weight":
+        w = [m(4, 8, 0), mom[0]]
+    elif case == "out_meets_other_momentum":
+        # update_out[0] starts inside momentum[1]'s last row
+        mom[1] = at(0, 4, 8, 8)
+        uo = [at(3 * 32 + 28, 4, 8, 8), MuonMatrix(None, 0, 0, 0, 0)]
+    elif case == "column_slices":
+        # one 4 x 16 fp32 parent: momentum 0 = columns 0..7, momentum 1 = columns 8..15
+        mom = [at(0, 4, 8, 16), at(32, 4, 8, 16)]
+    elif case == "column_slices_one_shared":
+        mom = [at(0, 4, 8, 16), at(28, 4, 8, 16)]
+    elif case == "wraps_into_next_row":
+        # momentum 1 starts 24 bytes into row 0 of momentum 0 (its columns end at
+        # byte 16) and runs 16 bytes, into momentum 0's row 1 (bytes 32..47)
+        g = [m(2, 4, 0), m(2, 4, 0)]
+        mom = [at(0, 2, 4, 8), at(24, 2, 4, 8)]
+    elif case == "ends_at_last_row":
+        # the same, but momentum 0 has one row: the wrapped bytes are outside it
+        g = [m(1, 4, 0), m(2, 4, 0)]
+        mom = [at(0, 1, 4, 8), at(24, 2, 4, 8)]
+    elif case == "strides_differ_interleaved":
+        # momentum 0: rows of 16 bytes every 64; momentum 1: rows of 16 bytes every
+        # 32, starting 16 bytes in: they alternate and never meet
+        g = [m(4, 4, 0), m(8, 4, 0)]
+        mom = [at(0, 4, 4, 16), at(16, 8, 4, 8)]
+    elif case == "strides_differ_meet":
+        g = [m(4, 4, 0), m(8, 4, 0)]
+        mom = [at(0, 4, 4, 16), at(8, 8, 4, 8)]
+    elif case == "grads_share":
+        g = [at(0, 4, 8, 8), at(0, 4, 8, 8)]
+    elif case == "bf16_out_inside_f32_gap":
+        # fp32 momentum rows use bytes 0..31 of every 64; the bf16 output's rows use 32..47
+        mom = [at(0, 4, 8, 16), m(4, 8, 0)]
+        uo = [at(32, 4, 8, 32, 1), MuonMatrix(None, 0, 0, 0, 0)]
+    rc, msg = mu.check_update_args(g, mom, w, uo)
+    assert rc == code, (case, rc, msg)
+    if code != OK:
+        assert "share memory" in msg, msg
+
+
+def test_polar_buffer_overlap(lib):
+    x = at(0, 4, 8, 8)
+    assert mu.check_polar_args([x], [x])[0] == OK                              # in place
+    assert mu.check_polar_args([x, m(4, 8, 0)], [m(4, 8, 0), x])[0] == OK      # an output over another input
+    shifted = at(4, 4, 8, 8)
+    assert mu.check_polar_args([x], [shifted])[0] == OK                        # partly over its own input
+    rc, msg = mu.check_polar_args([m(4, 8, 0), m(4, 8, 0)], [x, shifted])
+    assert rc == INVALID and "out[0] and out[1]" in msg, msg
+    assert mu.check_polar_args([m(4, 8, 0), m(4, 8, 0)], [at(0, 4, 8, 16), at(32, 4, 8, 16)])[0] == OK
 
 
 def test_batch_count_limits(lib):

@@ -4,7 +4,9 @@ The validation layer (csrc/validate.cpp) is pure C++ and runs before
 anything is enqueued, so it can be exercised without a GPU: it is built here
 with AddressSanitizer and UndefinedBehaviorSanitizer together with a seeded
 fuzz driver (tests/native/validate_fuzz.cpp) that throws edge and random
-descriptors, batch sizes and configurations at both checkers.
+descriptors, batch sizes and configurations at both checkers, then packs
+small matrices into a few hundred bytes and checks the buffer-overlap rule
+against a row-by-row brute force on every call.
 """
 import os
 import shutil
@@ -29,4 +31,6 @@ def test_validation_under_asan_ubsan(tmp_path):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
     run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
     assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
-    assert run.stdout.startswith("ok "), run.stdout
+    lines = run.stdout.splitlines()
+    assert any(l.startswith("overlap ") for l in lines), run.stdout   # the overlap rule's fuzz ran and agreed
+    assert lines and lines[-1].startswith("ok "), run.stdout
