@@ -349,6 +349,47 @@ def test_workspace_allocation_failure_leaves_handle_usable(dev):
         h.close()
 
 
+def test_entry_points_reject_shared_buffers(dev):
+    """A written buffer that shares memory with another buffer of the call is
+    rejected before anything is enqueued: the buffers keep their values. An
+    in-place polar call and momenta that are column slices of one parent
+    buffer are accepted and match the oracle."""
+    say("entry points reject shared written buffers")
+    g, m, w = gen.custom_matrix((64, 96), 1600, dev)
+    g0, m0, w0 = g.clone(), m.clone(), w.clone()
+    pw = torch.zeros((72, 96), device=dev)          # weight = rows 0..63, update_out = rows 8..71
+    pw[:64].copy_(w)
+    cases = [
+        ("momentum is the grad", dict(grads=[g], moms=[g], weights=[w])),
+        ("weight is the momentum", dict(grads=[g], moms=[m], weights=[m])),
+        ("update_out overlaps the weight", dict(grads=[g], moms=[m], weights=[pw[:64]], out=[pw[8:]])),
+    ]
+    for name, c in cases:
+        with pytest.raises(mu.LibMuonError) as ei:
+            mu.muon_update(c["grads"], c["moms"], c["weights"], update_out=c.get("out"))
+        assert ei.value.status == -1 and "share memory" in str(ei.value), (name, str(ei.value))
+    x = torch.zeros((64, 96), device=dev)
+    with pytest.raises(mu.LibMuonError) as ei:
+        mu.ns_polar([g, m], [x, x])                  # two outputs in one buffer
+    assert ei.value.status == -1 and "share memory" in str(ei.value), str(ei.value)
+    torch.cuda.synchronize()
+    assert torch.equal(g, g0) and torch.equal(m, m0) and torch.equal(w, w0), "a rejected call changed a buffer"
+    assert torch.equal(pw[:64], w0) and bool((pw[64:] == 0).all()) and bool((x == 0).all())
+    # momenta as column slices of one parent, weights likewise: accepted
+    parent_m = torch.empty((64, 192), device=dev)
+    parent_w = torch.empty((64, 192), device=dev)
+    g2, m2, w2 = gen.custom_matrix((64, 96), 1601, dev)
+    parent_m[:, :96].copy_(m); parent_m[:, 96:].copy_(m2)
+    parent_w[:, :96].copy_(w); parent_w[:, 96:].copy_(w2)
+    M = [parent_m[:, :96], parent_m[:, 96:]]
+    W = [parent_w[:, :96], parent_w[:, 96:]]
+    V = [torch.empty((64, 96), device=dev), torch.empty((64, 96), device=dev)]
+    mu.muon_update([g, g2], M, W, update_out=V)
+    torch.cuda.synchronize()
+    for i, (gi, mi, wi) in enumerate([(g0, m0, w0), (g2, m2, w2)]):
+        check_update(f"slices[{i}]", gi, mi, wi, M[i], V[i], W[i], mu.default_config(), FP32_TOL)
+
+
 def test_update_single_fp32_256x1024(dev):
     say("muon_update single_fp32_256x1024")
     g, m, w = gen.make_matrix(gen.WORKLOADS["single_fp32_256x1024"], 0, dev)
