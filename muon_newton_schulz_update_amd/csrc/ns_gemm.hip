@@ -209,12 +209,14 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   const int prow = 8 * wave + (lane >> 3);
   const uint32_t lane_off = (uint32_t)(((int64_t)prow * ld + ((lane & 7) ^ ((prow >> 1) & 7)) * CPR) * sizeof(T));
   const int rstep = (int)((int64_t)8 * NW * ld * sizeof(T));
-  // Buffer resources over the two operand panels, range-checked: a read
-  // beyond the panel returns zeros instead of touching other memory. On a
-  // diagonal tile of the two symmetric products both operands are the same
-  // panel: the second resource gets no records, so its loads fetch nothing
-  // (the issue count, and with it every wait, stays the same), and both
-  // operands' fragments are read from the first panel's slot.
+  // Buffer resources over the two operand panels. Every read stays inside
+  // its panel: the K offset travels in the scalar offset and stages past the
+  // end of K are clamped. On a diagonal tile of the two symmetric products
+  // both operands are the same panel: the second resource gets no records,
+  // and since the range check compares the per-lane offset with the record
+  // count, each of its loads fails the check and fetches nothing (the issue
+  // count, and with it every wait, stays the same); both operands' fragments
+  // are read from the first panel's slot.
   const int ext = (int)((int64_t)TILE * ld * sizeof(T));
   const bool same = (mode != GM_BX) && (it.tm == it.tn);
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void*)P, (short)0, ext, 0x00020000);
