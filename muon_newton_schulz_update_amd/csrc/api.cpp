@@ -219,8 +219,10 @@ void add_gemm(std::vector<uint8_t>& meta, GemmList& G, std::vector<TileItem>& it
   if (!items.empty()) memcpy(meta.data() + pos, items.data(), items.size() * sizeof(TileItem));
 }
 
-std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in, const muon_matrix* w,
-                                 const muon_matrix* uo) {
+// A plan depends only on the call kind, the pass count and the inputs' shapes
+// and element types (exactly what plan_key holds): caller pointers, strides,
+// weights and outputs go into the per-call descriptors.
+std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in) {
   auto P = std::make_unique<Plan>();
   P->kind = kind;
   size_t off = 0;
@@ -416,9 +418,6 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in,
         }
         add_gemm(meta, G, items);
       }
-  // algorithmic bytes of the streaming launches
-  (void)w;
-  (void)uo;
   return P;
 }
 
@@ -587,7 +586,7 @@ muon_status run(muon_handle* h, const Call& c) {
       if (victim->second->meta_dev) HIP_TRY(h, hipFree(victim->second->meta_dev));
       h->plans.erase(victim);
     }
-    auto p = build_plan(c.kind, pp, c.n, c.in, c.w, c.out);
+    auto p = build_plan(c.kind, pp, c.n, c.in);
     P = p.get();
     h->plans.emplace(key, std::move(p));
   } else {
@@ -829,7 +828,7 @@ extern "C" muon_status muon_reserve(muon_handle* h, int n, const muon_matrix* sh
   }
   size_t need = 0;
   for (int kind = 0; kind < 3; ++kind) {
-    auto P = build_plan(kind, 2, n, shapes, nullptr, nullptr);
+    auto P = build_plan(kind, 2, n, shapes);
     need = std::max(need, P->ws_bytes);
   }
   return ensure_workspace(h, need);
