@@ -310,12 +310,20 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // k-step 3: the refill of the freed slots with operand stages 2k+S and
-    // 2k+S+1 (longest latency first), then the next stage's first fragments
+    // 2k+S+1 (longest latency first), then the next stage's first fragments.
+    // With 256-tiles it runs at raised wave priority: a wave still in it
+    // outranks the waves of its SIMD that have moved on to the next stage, so
+    // the waves reach the next barrier closer together (1-1.2 % faster on the
+    // 3072-row products). 128-tiles, two workgroups per CU, keep the default.
+    if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_sched_barrier(0);
     issue(ps, 2 * k + S);
     issue(qs, 2 * k + S + 1);
     read_frags(pn, qn, 0, 0);
     mfmas(1);
     spread(2 * LPO + kReadStep, 2 * LPO);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     ps = pn; qs = qn;
     pn = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
