@@ -351,6 +351,7 @@ def test_classic_config_matches_page():
     c = O.classic_config()
     assert (c.ns_steps, c.ns_a, c.ns_b, c.ns_c) == (n["steps"], n["a"], n["b"], n["c"])
     assert (c.lr, c.mu, c.nesterov) == (k["lr"], k["mu"], k["nesterov"])
+    assert c.momentum == k["momentum_form"]
     # no Aurora preconditioner, no Contra term, no u/w-floor
     assert (c.pp_iterations, c.contra, c.target_uw) == (0, 0.0, 0.0)
 
@@ -372,16 +373,128 @@ def test_momentum_warmup_points_and_linearity():
 
 @pytest.mark.parametrize("shape", [(96, 40), (40, 96), (64, 64)])
 def test_classic_update_closed_form(shape):
-    """Classic step = Nesterov blend -> NS5 (SVD closed form) -> sqrt(max(1,
-    rows/cols)) -> W - lr V, with no further rescaling."""
+    """Classic step = SGD-momentum buffer and Nesterov blend -> NS5 (SVD closed
+    form) -> sqrt(max(1, rows/cols)) -> W - lr V, with no further rescaling."""
     rng = np.random.default_rng(11)
     G, M, W = (rng.standard_normal(shape) for _ in range(3))
     cfg = dataclasses.replace(O.classic_config(), mu=O.momentum_warmup(123))
     M1, V, W1 = O.muon_update(G, M, W, cfg)
-    Mw = M + (1.0 - cfg.mu) * (G - M)
-    X = G + cfg.mu * (Mw - G)
+    buf = cfg.mu * M + G                       # heavy-ball buffer, no dampening
+    X = G + cfg.mu * buf                       # Nesterov
     k = PAGE["ns5_classic"]
     want = svd_ns(X, steps=k["steps"], coeffs=(k["a"], k["b"], k["c"])) * math.sqrt(max(1.0, shape[0] / shape[1]))
-    assert rel(M1, Mw) < 1e-14
+    assert rel(M1, buf) < 1e-14
     assert rel(V, want) < 1e-10
     assert rel(W1, W - PAGE["classic_recipe"]["lr"] * want) < 1e-12
+
+
+def _momentum_sums(Gs, mus, form):
+    """Closed form of the momentum buffer after len(Gs) steps from zero, as an
+    explicit weighted sum of the gradients (not the recursion): with
+    P(j) = prod of mu_t for t > j, the SGD buffer is sum_j P(j) G_j and the
+    moving average is sum_j (1 - mu_j) P(j) G_j."""
+    k = len(Gs)
+    tot = np.zeros_like(Gs[0])
+    for j in range(k):
+        P = float(np.prod(mus[j + 1:k]))
+        w = P if form == "sgd" else (1.0 - mus[j]) * P
+        tot = tot + w * Gs[j]
+    return tot
+
+
+def test_classic_sgd_momentum_over_warmup():
+    """Five classic steps at the start of the momentum warm-up (mu from 0.85):
+    the oracle's buffer equals the SGD-momentum closed form and not the
+    moving-average one, and every step's update is NS5 of G_k + mu_k buf_k.
+    Swapping the two momentum forms fails both checks."""
+    shape = (48, 20)
+    rng = np.random.default_rng(31)
+    Gs = [rng.standard_normal(shape) * np.exp(rng.standard_normal((shape[0], 1))) for _ in range(5)]
+    w = PAGE["classic_recipe"]["warmup"]
+    k5 = PAGE["ns5_classic"]
+    base = O.classic_config()
+    M = np.zeros(shape)
+    mus = []
+    for step, G in enumerate(Gs):
+        mu_k = O.momentum_warmup(step * 100, w["mu_start"], w["mu_end"], w["steps"])
+        mus.append(mu_k)
+        M, V, _ = O.muon_update(G, M, None, dataclasses.replace(base, mu=mu_k))
+        sgd = _momentum_sums(Gs[:step + 1], mus, "sgd")
+        ema = _momentum_sums(Gs[:step + 1], mus, "ema")
+        assert rel(M, sgd) < 1e-13
+        assert rel(M, ema) > 0.5                       # about 1 / (1 - mu) apart
+        X = G + mu_k * sgd
+        want = svd_ns(X, steps=k5["steps"], coeffs=(k5["a"], k5["b"], k5["c"])) * math.sqrt(shape[0] / shape[1])
+        assert rel(V, want) < 1e-10
+        if step >= 1:                                  # the two forms' directions part under the warm-up
+            X_ema = (1 - mu_k) * G + mu_k * ema
+            bad = svd_ns(X_ema, steps=k5["steps"], coeffs=(k5["a"], k5["b"], k5["c"])) * math.sqrt(shape[0] / shape[1])
+            assert rel(V, bad) > 1e-3
+
+
+def test_momentum_forms_agree_in_direction_at_constant_mu():
+    """At constant mu and zero start the SGD buffer is the moving average
+    divided by (1 - mu), so NS (which divides by the norm) gives the same
+    update direction up to the 1e-7 norm guard."""
+    shape = (30, 12)
+    rng = np.random.default_rng(32)
+    Ms, Me = np.zeros(shape), np.zeros(shape)
+    for _ in range(3):
+        G = rng.standard_normal(shape)
+        Ms, Vs, _ = O.muon_update(G, Ms, None, dataclasses.replace(O.classic_config(), mu=0.9))
+        Me, Ve, _ = O.muon_update(G, Me, None, dataclasses.replace(O.classic_config(), mu=0.9, momentum="ema"))
+        assert rel(Ms * (1 - 0.9), Me) < 1e-13
+        assert rel(Vs, Ve) < 1e-6
+
+
+# --------------------------------------------------------------------------
+# Aurora on a wide matrix's own rows (reading R7)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(8, 24), (5, 31), (12, 40)])
+def test_wide_rows_pp1_is_row_normalise_then_polar(shape):
+    """pp = 1 on the wide matrix's own rows: normalise each row of G (no
+    transpose), then the SVD closed form of NS."""
+    rng = np.random.default_rng([33, *shape])
+    G = rng.standard_normal(shape) * np.exp(rng.standard_normal((shape[0], 1)))
+    Gn = G / np.linalg.norm(G, axis=1, keepdims=True)
+    got = O.aurora_orthogonalize(G, pp_iterations=1, wide_rows=True)
+    assert rel(got, svd_ns(Gn)) < 1e-11
+    # and it is not the default column equilibration
+    assert rel(got, O.aurora_orthogonalize(G, pp_iterations=1)) > 1e-3
+
+
+def test_wide_rows_invariances():
+    """Positive scaling of a wide G's rows cancels in D0 (but column scaling
+    does not); tall and square inputs are unchanged by the option; the rows
+    of the result are orthonormal for a well-conditioned input, so later
+    passes stay at the first pass's D (the fixed point of target 1)."""
+    rng = np.random.default_rng(34)
+    G = rng.standard_normal((10, 36))
+    s = np.exp(rng.standard_normal((10, 1)))
+    t = np.exp(rng.standard_normal((1, 36)))
+    for pp in (1, 2, 3):
+        a = O.aurora_orthogonalize(G, pp, 0.5, wide_rows=True)
+        assert rel(O.aurora_orthogonalize(s * G, pp, 0.5, wide_rows=True), a) < 1e-12
+        assert rel(O.aurora_orthogonalize(G * t, pp, 0.5, wide_rows=True), a) > 1e-3
+        assert np.max(np.abs(a @ a.T - np.eye(10))) < 1e-4
+    assert rel(O.aurora_orthogonalize(G, 2, 0.5, wide_rows=True),
+               O.aurora_orthogonalize(G, 1, 0.5, wide_rows=True)) < 1e-4
+    T = G.T
+    assert np.array_equal(O.aurora_orthogonalize(T, 2, 0.5, wide_rows=True), O.aurora_orthogonalize(T, 2, 0.5))
+    S = rng.standard_normal((9, 9))
+    assert np.array_equal(O.aurora_orthogonalize(S, 2, 0.5, wide_rows=True), O.newton_schulz(S))
+
+
+def test_wide_rows_moves_d_when_rows_are_ill_conditioned():
+    """Where NS has not converged (two nearly parallel rows, a singular value
+    near 1e-4 of the largest), the leverage of those rows is below 1 and the
+    second pass reweights them: pp = 2 then differs from pp = 1."""
+    rng = np.random.default_rng(35)
+    G = rng.standard_normal((6, 40))
+    G[1] = G[0] + 1e-4 * rng.standard_normal(40)
+    a1 = O.aurora_orthogonalize(G, 1, 0.5, wide_rows=True)
+    a2 = O.aurora_orthogonalize(G, 2, 0.5, wide_rows=True)
+    lev1 = np.sum(a1 * a1, axis=1)
+    assert lev1[0] < 0.9 and lev1[1] < 0.9
+    assert rel(a2, a1) > 1e-3
