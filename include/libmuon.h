@@ -92,7 +92,9 @@ typedef struct {
  *                       times the unit-operator-norm direction (0 = off).
  *   target_uw           u/w-floor target ratio (0 = off).
  *   lr                  learning rate of the parameter add.
- *   flags               reserved, must be 0.
+ *   flags               bitwise OR of MUON_FLAG_* below (0 = the Aurora
+ *                       page's step); unknown bits are rejected
+ *                       (MUON_ERR_INVALID_ARG).
  */
 typedef struct {
   int32_t  ns_steps;
@@ -107,6 +109,30 @@ typedef struct {
   float    lr;
   uint32_t flags;
 } muon_config;
+
+/*
+ * MUON_FLAG_SGD_MOMENTUM — the momentum form of the classic Muon recipe,
+ * [Track-1 page] §"训练管线与系统实现" ("SGD momentum" with Nesterov), read as
+ * the heavy-ball buffer with no dampening: M <- mu M + G, X = G + mu M
+ * (X = M without Nesterov). Without the flag the step keeps the Aurora page's
+ * moving average, M <- M + (1 - mu)(G - M), X = G + mu (M - G). The two give
+ * the same direction at constant mu from a zero buffer (the buffers differ
+ * by 1/(1 - mu)) and different ones under a momentum warm-up.
+ * muon_config_classic sets it.
+ *
+ * MUON_FLAG_WIDE_ROWS — [Aurora page] §"复现与扩展建议" names a later result
+ * that applies the row-balanced polar to a wide matrix (the MLP output
+ * projection) and gives no formula. With this flag a wide matrix (rows <
+ * cols) is equilibrated on its own rows, the short side: D = 1/max(row
+ * norm, pp_eps), then the same damped update with target 1 (the squared
+ * row norm of a polar factor with orthonormal rows). Tall and square
+ * matrices are unaffected. Since such a polar factor's rows are already
+ * orthonormal, later passes move D only where Newton-Schulz has not
+ * converged; pp_iterations 1 is row-normalise-then-polar on the rows.
+ */
+#define MUON_FLAG_SGD_MOMENTUM 0x1u
+#define MUON_FLAG_WIDE_ROWS    0x2u
+#define MUON_FLAG_ALL          0x3u
 
 /* Per-kernel-class timing gathered when profiling is on (see muon_profile_*). */
 typedef struct {
@@ -126,7 +152,8 @@ void muon_config_default(muon_config* cfg);
 
 /*
  * Fill *cfg with the classic Muon recipe of the Track-1 record page
- * (§"训练管线与系统实现"): Nesterov momentum 0.95, Newton-Schulz with
+ * (§"训练管线与系统实现"): SGD momentum 0.95 with Nesterov
+ * (flags = MUON_FLAG_SGD_MOMENTUM), Newton-Schulz with
  * (ns_a, ns_b, ns_c) = (3.4445, -4.7750, 2.0315) for ns_steps 5, no Aurora
  * preconditioner (pp_iterations 0), no Contra term (contra 0), no u/w-floor
  * (target_uw 0), the sqrt(max(1, rows/cols)) scale, lr 0.04. The remaining

@@ -26,13 +26,16 @@ __all__ = [
     "MuonConfig", "MuonProfile", "LibMuonError", "Handle", "load_library",
     "library_path", "default_config", "classic_config", "momentum_warmup", "make_config", "ns_polar",
     "aurora_orthogonalize", "muon_update", "check_update_args",
-    "check_polar_args", "get_handle", "STATUS",
+    "check_polar_args", "get_handle", "STATUS", "MUON_FLAG_SGD_MOMENTUM", "MUON_FLAG_WIDE_ROWS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmuon.so"
 
 MUON_F32, MUON_BF16 = 0, 1
+# muon_config.flags bits (include/libmuon.h)
+MUON_FLAG_SGD_MOMENTUM = 0x1    # classic recipe's SGD momentum (buf = mu buf + G)
+MUON_FLAG_WIDE_ROWS = 0x2       # Aurora on a wide matrix's own rows
 STATUS = {
     0: "MUON_OK", -1: "MUON_ERR_INVALID_ARG", -2: "MUON_ERR_UNSUPPORTED_DTYPE",
     -3: "MUON_ERR_SHAPE_MISMATCH", -4: "MUON_ERR_ALLOC", -5: "MUON_ERR_HIP",
@@ -187,8 +190,16 @@ def _desc(t: torch.Tensor | None, what: str) -> MuonMatrix:
             raise ValueError(f"{what}: tensor must live on a GPU")
         if t.stride(1) != 1 and cols > 1:
             raise ValueError(f"{what}: columns must be contiguous (stride(1) == 1)")
-    ld = t.stride(0) if rows > 1 else max(cols, 1)
-    return MuonMatrix(t.data_ptr() if rows and cols else None, rows, cols, max(ld, cols), _DT[t.dtype])
+    return MuonMatrix(t.data_ptr() if rows and cols else None, rows, cols, row_stride(t), _DT[t.dtype])
+
+
+def row_stride(t: torch.Tensor) -> int:
+    """The descriptor's ld for a 2-D tensor: its row stride as it is, so that a
+    view whose rows overlap (stride(0) < cols, e.g. an expanded tensor) is
+    rejected by the library (MUON_ERR_SHAPE_MISMATCH) instead of being given
+    rows it does not own. A single row has no stride to speak of."""
+    rows, cols = t.shape
+    return t.stride(0) if rows > 1 else max(cols, 1)
 
 
 def _array(descs: Sequence[MuonMatrix]):

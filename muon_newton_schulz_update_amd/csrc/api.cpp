@@ -39,7 +39,7 @@ namespace muon {
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
                           float ca, float cb, float cc, int variant, int tile, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
-                                 hipStream_t st);
+                                 int sgd, hipStream_t st);
 hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st);
 hipError_t launch_norms_scalars(DevMat* m, LaunchList L, int nblk, float ns_eps, int init_power, hipStream_t st);
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st);
@@ -74,7 +74,7 @@ inline int esz(int dt) { return dt == DT_BF16 ? 2 : 4; }
 struct MatInfo {
   int user;                  // index in the caller's batch
   int rows, cols, s, L, s_pad, L_pad;
-  bool tall, square, aurora;
+  bool tall, square, aurora, eq_short;
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv, wband;
   size_t o_xn, o_x[2], o_xt[2], o_a, o_b, o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
@@ -136,11 +136,11 @@ struct Plan {
   uint64_t last_use = 0;
 };
 
-std::string plan_key(int kind, int pp, int n, const muon_matrix* in) {
+std::string plan_key(int kind, int pp, bool wide_rows, int n, const muon_matrix* in) {
   std::string k;
   k.reserve(16 + n * 12);
   char buf[64];
-  snprintf(buf, sizeof(buf), "%d/%d/%d|", kind, pp, n);
+  snprintf(buf, sizeof(buf), "%d/%d/%d/%d|", kind, pp, (int)wide_rows, n);
   k += buf;
   for (int i = 0; i < n; ++i) {
     snprintf(buf, sizeof(buf), "%lld,%lld,%d;", (long long)in[i].rows, (long long)in[i].cols, (int)in[i].dtype);
@@ -219,10 +219,11 @@ void add_gemm(std::vector<uint8_t>& meta, GemmList& G, std::vector<TileItem>& it
   if (!items.empty()) memcpy(meta.data() + pos, items.data(), items.size() * sizeof(TileItem));
 }
 
-// A plan depends only on the call kind, the pass count and the inputs' shapes
-// and element types (exactly what plan_key holds): caller pointers, strides,
-// weights and outputs go into the per-call descriptors.
-std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in) {
+// A plan depends only on the call kind, the pass count, the wide-rows option
+// and the inputs' shapes and element types (exactly what plan_key holds):
+// caller pointers, strides, weights and outputs go into the per-call
+// descriptors.
+std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int n, const muon_matrix* in) {
   auto P = std::make_unique<Plan>();
   P->kind = kind;
   size_t off = 0;
@@ -244,6 +245,7 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in)
     m.tall = m.rows > m.cols;
     m.square = m.rows == m.cols;
     m.aurora = (kind != KIND_NS) && !m.square && pp > 0;
+    m.eq_short = m.aurora && wide_rows && m.rows < m.cols;
     m.ns_t = in[i].dtype == MUON_BF16 ? DT_BF16 : DT_F32;
     m.n_rt = cdiv(m.rows, kStreamRows);
     m.n_ct = cdiv(m.cols, kStreamCols);
@@ -355,7 +357,10 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, int n, const muon_matrix* in)
   for (int t = 0; t < 2; ++t) {
     std::vector<int> ms, bl;
     for (int i = 0; i < nm; ++i)
-      if (P->mats[i].aurora && P->mats[i].ns_t == t) { ms.push_back(i); bl.push_back(cdiv(P->mats[i].L, 4)); }
+      if (P->mats[i].aurora && P->mats[i].ns_t == t) {
+        ms.push_back(i);   // one wave per equilibrated line, 4 per block
+        bl.push_back(cdiv(P->mats[i].eq_short ? P->mats[i].s : P->mats[i].L, 4));
+      }
     add_list(meta, P->dupdate[t], ms, bl);
   }
   {
@@ -573,7 +578,8 @@ struct Call {
 muon_status run(muon_handle* h, const Call& c) {
   const muon_config& cfg = c.cfg;
   const int pp = c.kind == KIND_NS ? 0 : cfg.pp_iterations;
-  const std::string key = plan_key(c.kind, pp, c.n, c.in);
+  const bool wide_rows = (cfg.flags & MUON_FLAG_WIDE_ROWS) != 0;
+  const std::string key = plan_key(c.kind, pp, wide_rows, c.n, c.in);
   auto it = h->plans.find(key);
   Plan* P;
   if (it == h->plans.end()) {
@@ -586,7 +592,7 @@ muon_status run(muon_handle* h, const Call& c) {
       if (victim->second->meta_dev) HIP_TRY(h, hipFree(victim->second->meta_dev));
       h->plans.erase(victim);
     }
-    auto p = build_plan(c.kind, pp, c.n, c.in);
+    auto p = build_plan(c.kind, pp, wide_rows, c.n, c.in);
     P = p.get();
     h->plans.emplace(key, std::move(p));
   } else {
@@ -619,7 +625,7 @@ muon_status run(muon_handle* h, const Call& c) {
       d.dt_uo = c.out[m.user].dtype == MUON_BF16 ? DT_BF16 : DT_F32;
     }
     d.rows = m.rows; d.cols = m.cols; d.s = m.s; d.L = m.L; d.s_pad = m.s_pad; d.L_pad = m.L_pad;
-    d.tall = m.tall; d.square = m.square; d.aurora = m.aurora; d.ns_t = m.ns_t;
+    d.tall = m.tall; d.square = m.square; d.aurora = m.aurora; d.eq_short = m.eq_short; d.ns_t = m.ns_t;
     d.n_rt = m.n_rt; d.n_ct = m.n_ct; d.n_seg = m.n_seg; d.n_rmv = m.n_rmv; d.wband = m.wband;
     d.xn = c.kind == KIND_UPDATE ? ws + m.o_xn : nullptr;
     d.x[0] = ws + m.o_x[0]; d.x[1] = ws + m.o_x[1];
@@ -665,7 +671,7 @@ muon_status run(muon_handle* h, const Call& c) {
   {
     ProfScope ps(h, 1, b_mom);
     CHECK_LAUNCH(h, launch_momentum_stats(D, dev_list(*P, P->stream), P->stream.nblk, upd ? 1 : 0, cfg.mu,
-                                          cfg.nesterov, st));
+                                          cfg.nesterov, (cfg.flags & MUON_FLAG_SGD_MOMENTUM) ? 1 : 0, st));
   }
   {
     ProfScope ps(h, 1, 0);
@@ -828,7 +834,7 @@ extern "C" muon_status muon_reserve(muon_handle* h, int n, const muon_matrix* sh
   }
   size_t need = 0;
   for (int kind = 0; kind < 3; ++kind) {
-    auto P = build_plan(kind, 2, n, shapes);
+    auto P = build_plan(kind, 2, false, n, shapes);
     need = std::max(need, P->ws_bytes);
   }
   return ensure_workspace(h, need);

@@ -59,7 +59,8 @@ struct DevMat {
   int32_t rows, cols, s, L, s_pad, L_pad;
   int32_t tall;     // rows > cols: the NS iterate is the transpose of storage
   int32_t square;
-  int32_t aurora;   // diagonal preconditioner on the long side
+  int32_t aurora;   // diagonal preconditioner (on the long side unless eq_short)
+  int32_t eq_short; // aurora on a wide matrix's own rows (the short side)
   int32_t ns_t;     // DT_F32 or DT_BF16: type of xn, x, xt, a, b
   int32_t n_rt, n_ct;   // ceil(rows / kStreamRows), ceil(cols / kStreamCols)
   int32_t n_seg;        // ceil(cols / kSegCols): streaming tiles are n_rt x n_seg

@@ -172,8 +172,10 @@ __device__ __forceinline__ float strided_sum(const float* p, size_t stride, int 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// K1: momentum EMA + Nesterov blend, and the sums of squares of the result.
-//   M <- M + (1 - mu)(G - M);  X = G + mu (M - G)  (X = M without Nesterov)
+// K1: momentum + Nesterov blend, and the sums of squares of the result.
+//   moving average:  M <- M + (1 - mu)(G - M);  X = G + mu (M - G)
+//   SGD (sgd != 0):  M <- mu M + G;             X = G + mu M
+//   (X = M without Nesterov)
 // X is stored in the NS type (rounded), and the norms are taken of the stored
 // values. With `nesterov_pass` false this only gathers the norms of the
 // matrix given in `g` (the polar entry points).
@@ -183,7 +185,8 @@ __device__ __forceinline__ float strided_sum(const float* p, size_t stride, int 
 // over the tile's rows, the four waves combined in LDS).
 // ---------------------------------------------------------------------------
 template <typename TG, typename TX, bool NP>
-__device__ __forceinline__ void momentum_body(const DevMat& M, int local, float mu, int nesterov, float* cp) {
+__device__ __forceinline__ void momentum_body(const DevMat& M, int local, float mu, int nesterov, int sgd,
+                                              float* cp) {
   typedef Ty<TG> G;
   typedef Ty<float> F;
   constexpr int R = kWaveRows;
@@ -207,9 +210,9 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float g = x[e];
-        const float mn = m[e] + (1.f - mu) * (g - m[e]);
+        const float mn = sgd ? mu * m[e] + g : m[e] + (1.f - mu) * (g - m[e]);
         m[e] = mn;
-        x[e] = Ty<TX>::round(nesterov ? g + mu * (mn - g) : mn);
+        x[e] = Ty<TX>::round(nesterov ? (sgd ? g + mu * mn : g + mu * (mn - g)) : mn);
       }
       if (vec) {
         F::st(M.m, (size_t)(r + k) * M.ld_m + c, m);
@@ -276,18 +279,18 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
 }
 
 __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict__ mats, LaunchList L,
-                                                        int nesterov_pass, float mu, int nesterov) {
+                                                        int nesterov_pass, float mu, int nesterov, int sgd) {
   static_assert(kStreamRows == 4 * kWaveRows, "four waves per streaming tile");
   __shared__ float cp[4 * kSegCols];
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   // the grad's type is the NS type (plans are keyed by it)
   if (M.dt_g == DT_BF16) {
-    if (nesterov_pass) momentum_body<__bf16, __bf16, true>(M, local, mu, nesterov, cp);
-    else momentum_body<__bf16, __bf16, false>(M, local, mu, nesterov, cp);
+    if (nesterov_pass) momentum_body<__bf16, __bf16, true>(M, local, mu, nesterov, sgd, cp);
+    else momentum_body<__bf16, __bf16, false>(M, local, mu, nesterov, sgd, cp);
   } else {
-    if (nesterov_pass) momentum_body<float, float, true>(M, local, mu, nesterov, cp);
-    else momentum_body<float, float, false>(M, local, mu, nesterov, cp);
+    if (nesterov_pass) momentum_body<float, float, true>(M, local, mu, nesterov, sgd, cp);
+    else momentum_body<float, float, false>(M, local, mu, nesterov, sgd, cp);
   }
 }
 
@@ -296,7 +299,9 @@ __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict
 // Lines: one thread per row (rowsq[r] = sum of the row's segment partials)
 // and, for wide matrices, per column (colsq[c] = sum over row tiles). A
 // long-side line l also gets rho_l = ||line||, D_l = 1 / max(rho_l, eps)
-// (Aurora's initial preconditioner) and (D_l rho_l)^2. Block b of a matrix
+// (Aurora's initial preconditioner) and (D_l rho_l)^2; the equilibrated
+// lines are the long side, or a wide matrix's rows when M.eq_short is set
+// (its own rows, the short side). Block b of a matrix
 // writes linepart[2b] = its sum of row sums, linepart[2b+1] = its sum of
 // (D rho)^2. Row blocks come first, then column blocks.
 // ---------------------------------------------------------------------------
@@ -315,12 +320,12 @@ __global__ __launch_bounds__(256) void k_norms_lines(DevMat* __restrict__ mats, 
       const float s = strided_sum(M.rowpart + (size_t)i * M.n_seg, 1, M.n_seg);
       gst<float>(M.rowsq + i, s);
       tpart = s;
-      if (!wide) lsq = s;
+      if (!wide || M.eq_short) lsq = s;
     }
   } else if (i < M.cols) {
     const float s = strided_sum(M.colpart + i, (size_t)M.cols, M.n_rt);
     gst<float>(M.colsq + i, s);
-    lsq = s;
+    if (!M.eq_short) lsq = s;
   }
   if (M.aurora && lsq >= 0.f) {
     const float rho = sqrtf(lsq);
@@ -408,11 +413,13 @@ __device__ __forceinline__ void prologue_body(const DevMat& M, int local, const 
   for (int h = 0; h < 2; ++h)
     if (fv[h]) qs[h] = Ty<TS>::ld(src, (size_t)rr[h] * lds + cc[h]);
   // D entries: along the columns of a wide source, one per row of a tall one
+  // (and of a wide one equilibrated on its rows)
   float dv[2][8];
   if (M.aurora) {
+    const bool per_row = M.tall || M.eq_short;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (M.tall) {
+      if (per_row) {
         const float d = nv[h] > 0 ? gld<float>(M.dvec + rr[h]) : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) dv[h][e] = d;
@@ -466,10 +473,12 @@ __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mat
 }
 
 // ---------------------------------------------------------------------------
-// Aurora D update between passes: row_sq_l = max(sum_i U[i][l]^2, eps^2) over
-// the short side (row l of U^T), D_l *= (target / row_sq_l)^beta with
-// target = s / L; then partial sums of (D_l rho_l)^2 per block. One wave per
-// long-side row l; 4 rows per block; a lane loads two chunks per round.
+// Aurora D update between passes: row_sq_l = max(sum U_l^2, eps^2) over one
+// equilibrated line l of the pass's result U, D_l *= (target / row_sq_l)^beta,
+// then partial sums of (D_l rho_l)^2 per block. The lines are the long side
+// (row l of U^T, s entries, target s / L) or, with M.eq_short, a wide
+// matrix's own rows (row l of U, L entries, target 1). One wave per line; 4
+// lines per block; a lane loads two chunks per round.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mats, LaunchList L,
@@ -479,14 +488,16 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l = local * 4 + w;
+  const int nl = M.eq_short ? M.s : M.L;      // equilibrated lines
+  const int len = M.eq_short ? M.L : M.s;     // entries per line
   float contrib = 0.f;
-  if (l < M.L) {
-    const void* ut = M.xt[fin];
-    const size_t row = (size_t)l * M.s_pad;
+  if (l < nl) {
+    const void* ut = M.eq_short ? M.x[fin] : M.xt[fin];
+    const size_t row = (size_t)l * (M.eq_short ? M.L_pad : M.s_pad);
     float s = 0.f;
-    // entries past s are zero padding (the row holds s_pad entries)
+    // entries past len are zero padding (a line holds a multiple of 256)
     int i = lane * 8;
-    for (; i + 512 < M.s; i += 1024) {
+    for (; i + 512 < len; i += 1024) {
       const typename Ty<T>::Raw q0 = Ty<T>::ld(ut, row + i), q1 = Ty<T>::ld(ut, row + i + 512);
       float u0[8], u1[8];
       Ty<T>::cvt(q0, u0);
@@ -496,7 +507,7 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += u1[e] * u1[e];
     }
-    if (i < M.s) {
+    if (i < len) {
       float u0[8];
       Ty<T>::cvt(Ty<T>::ld(ut, row + i), u0);
 #pragma unroll
@@ -504,7 +515,7 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
     }
     s = wave_sum(s);
     if (lane == 0) {
-      const float target = (float)M.s / (float)M.L;
+      const float target = M.eq_short ? 1.f : (float)M.s / (float)M.L;
       const float rsq = fmaxf(s, pp_eps * pp_eps);
       const float d = M.dvec[l] * powf(target / rsq, pp_beta);
       M.dvec[l] = d;
@@ -521,7 +532,7 @@ __global__ __launch_bounds__(256) void k_aurora_scale(DevMat* __restrict__ mats,
   __shared__ float red[8];
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  const int nb = (M.L + 3) / 4;
+  const int nb = ((M.eq_short ? M.s : M.L) + 3) / 4;   // blocks of k_aurora_dupdate
   float s = 0.f;
   for (int i = threadIdx.x; i < nb; i += 256) s += gld<float>(M.tailpart + i);
   s = block_sum(s, red);
@@ -1187,8 +1198,8 @@ __global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ m
   } while (0)
 
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu,
-                                 int nesterov, hipStream_t st) {
-  LAUNCH(k_momentum_stats, nblk, m, L, nesterov_pass, mu, nesterov);
+                                 int nesterov, int sgd, hipStream_t st) {
+  LAUNCH(k_momentum_stats, nblk, m, L, nesterov_pass, mu, nesterov, sgd);
   return hipGetLastError();
 }
 hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st) {

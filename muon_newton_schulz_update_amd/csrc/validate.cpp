@@ -175,7 +175,8 @@ int check_config(const muon_config* c, char* msg, int len) {
   if (!finitef(c->target_uw) || c->target_uw < 0.f)
     return fail(msg, len, MUON_ERR_INVALID_ARG, "target_uw must be >= 0");
   if (!finitef(c->lr)) return fail(msg, len, MUON_ERR_INVALID_ARG, "lr must be finite");
-  if (c->flags != 0) return fail(msg, len, MUON_ERR_INVALID_ARG, "flags must be 0");
+  if (c->flags & ~MUON_FLAG_ALL)
+    return fail(msg, len, MUON_ERR_INVALID_ARG, "flags 0x%x has unknown bits", (unsigned)c->flags);
   return MUON_OK;
 }
 
@@ -276,6 +277,7 @@ extern "C" void muon_config_classic(muon_config* c) {
   c->mu = 0.95f;
   c->nesterov = 1;
   c->lr = 0.04f;
+  c->flags = MUON_FLAG_SGD_MOMENTUM;
 }
 
 // Linear momentum warm-up of the same page: frac = min(step / n, 1).

@@ -123,7 +123,7 @@ def test_update_validation(lib, case, code):
 @pytest.mark.parametrize("field,value", [
     ("ns_steps", 0), ("ns_steps", 65), ("pp_iterations", -1), ("pp_iterations", 9),
     ("mu", 1.5), ("mu", -0.1), ("nesterov", 2), ("power_steps", 0), ("pp_eps", 0.0),
-    ("target_uw", -1.0), ("flags", 1), ("lr", float("nan")), ("ns_a", float("inf")),
+    ("target_uw", -1.0), ("flags", 4), ("flags", 0x80000000), ("lr", float("nan")), ("ns_a", float("inf")),
 ])
 def test_config_validation(lib, field, value):
     cfg = mu.default_config()
@@ -250,8 +250,10 @@ def test_classic_config_equals_page_values(lib):
     assert (c.pp_iterations, c.contra, c.target_uw) == (0, 0.0, 0.0)
     # everything else keeps the default values
     d = mu.default_config()
-    for f in ("ns_eps", "pp_beta", "pp_eps", "power_steps", "flags"):
+    for f in ("ns_eps", "pp_beta", "pp_eps", "power_steps"):
         assert getattr(c, f) == getattr(d, f), f
+    # the page's SGD momentum (and nothing else) among the flags
+    assert k["momentum_form"] == "sgd" and c.flags == mu.MUON_FLAG_SGD_MOMENTUM
     assert mu.make_config("classic", lr=0.02).lr == pytest.approx(0.02)
 
 
@@ -263,3 +265,25 @@ def test_momentum_warmup_host_function(lib):
         got = lib.muon_momentum_warmup(s, w["mu_start"], w["mu_end"], w["steps"])
         assert got == pytest.approx(want, abs=1e-7), s
     assert lib.muon_momentum_warmup(5, 0.85, 0.95, 0) == pytest.approx(0.95)
+
+
+def test_overlapping_rows_are_rejected(lib):
+    """A tensor whose rows overlap (an expanded row, stride(0) = 0, or an
+    as_strided view with stride(0) < cols) keeps its stride in the
+    descriptor, and the library rejects it as momentum, weight or output
+    before anything is enqueued."""
+    import torch
+    ex = torch.zeros(1, 8).expand(4, 8)
+    ov = torch.zeros(40).as_strided((4, 8), (5, 1))
+    assert mu.row_stride(ex) == 0 and mu.row_stride(ov) == 5
+    assert mu.row_stride(torch.zeros(1, 8)) == 8 and mu.row_stride(torch.zeros(6, 8)[:, 2:5]) == 8
+    for ld in (mu.row_stride(ex), mu.row_stride(ov)):
+        bad = m(4, 8, 0, ld=ld)
+        rc, msg = mu.check_update_args([m(4, 8)], [bad], None, None)
+        assert rc == -3 and "ld" in msg, (ld, rc, msg)
+        rc, _ = mu.check_update_args([m(4, 8)], [m(4, 8, 0)], [bad], None)
+        assert rc == -3
+        rc, _ = mu.check_update_args([m(4, 8)], [m(4, 8, 0)], None, [bad])
+        assert rc == -3
+        rc, _ = mu.check_polar_args([m(4, 8)], [bad])
+        assert rc == -3
