@@ -10,10 +10,20 @@ resident in HBM, momentum and weights updated in place. Prints one JSON line.
 value = counted Newton-Schulz TFLOP/s of the whole step (4 s^2 L + 2 s^3 per
 iteration per matrix, s <= L, 12 iterations, 2 passes for non-square
 matrices; 5 iterations and one pass with --recipe classic) = counted flops /
-step time. `roofline` reports the matrix-core
-kernels alone (summed HIP-event time of their launches on the library's
-stream, over the timed steps) against the bf16 dense peak; `cpu_baseline`
-times the float64 oracle on a bounded sample of the same workload.
+step time.
+
+`roofline` is the matrix-core engine alone (summed HIP-event time of its
+launches on the library's stream over the timed steps) against the bf16 dense
+peak, on ALGORITHMIC flops: the work a product needs once its symmetric
+halves are skipped, 3 s^2 L + s^3 per iteration (A = X X^T: s^2 L, the upper
+half; A A^T: s^3, likewise; B'X: 2 s^2 L). Beside it: the counted-flop
+fraction (4 s^2 L + 2 s^3, the headline convention, which credits the skipped
+halves), the executed fraction (the flops the tiles issue, including padding
+and whole diagonal tiles; a hardware matrix-core counter gives the same
+figure), and the streaming kernels of the step against the page-level byte
+budget (momentum 14, power iteration 12, tail 8 bytes per bf16 element).
+`clocks` samples the GPU clocks during the timed steps; `cpu_baseline` times
+the float64 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -63,6 +73,117 @@ def step_flops(shapes, cfg) -> float:
     return tot
 
 
+def algorithmic_flops(shapes, cfg) -> float:
+    """3 s^2 L + s^3 per iteration per matrix: each product's flops with the
+    symmetric halves of A = X X^T and A A^T counted once."""
+    tot = 0.0
+    for r, c in shapes:
+        s, L = min(r, c), max(r, c)
+        passes = 1 if (r == c or cfg.pp_iterations == 0) else cfg.pp_iterations
+        tot += passes * cfg.ns_steps * (3.0 * s * s * L + float(s) ** 3)
+    return tot
+
+
+def stream_budget_bytes(shapes, grad_bytes, weight_bytes, cfg) -> float:
+    """Page-level HBM bytes of the streaming kernels per step: momentum pass
+    (read G, read and write fp32 M, write X, read W for its norm), power
+    iteration (six reads of X when the Contra term is on) and tail (read U
+    and X, read and write W); X and U in the grad's type. 34 B per element
+    for bf16 grads and weights."""
+    xb = grad_bytes
+    per = grad_bytes + 8 + xb + (weight_bytes or 0)
+    if cfg.contra != 0:
+        per += 6 * xb
+    per += xb + (xb if cfg.contra != 0 else 0) + 2 * (weight_bytes or 0)
+    return float(sum(r * c for r, c in shapes)) * per
+
+
+class ClockSampler:
+    """Samples the GPU's current clocks with the ROCm SMI tool on a thread
+    while the timed steps run (values in MHz, as the tool reports them)."""
+
+    def __init__(self, period_s: float = 1.0):
+        import threading
+        self.samples = []
+        self.source = None
+        self.error = None
+        self._stop = threading.Event()
+        self._period = period_s
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _sample(self):
+        import re
+        import subprocess
+        for cmd in (["rocm-smi", "--showgpuclocks", "--json"], ["amd-smi", "metric", "-c", "--json"]):
+            try:
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=10)
+            except Exception as e:          # tool missing or hung
+                self.error = f"{cmd[0]}: {e}"
+                continue
+            if r.returncode != 0:
+                self.error = f"{cmd[0]} rc {r.returncode}"
+                continue
+            try:
+                d = json.loads(r.stdout)
+            except ValueError:
+                self.error = f"{cmd[0]}: no JSON"
+                continue
+            found = {}
+
+            def walk(o, key=""):
+                if isinstance(o, dict):
+                    for k, v in o.items():
+                        walk(v, f"{key}/{k}".lower())
+                elif isinstance(o, (str, int, float)):
+                    m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", str(o).lower())
+                    val = float(m.group(1)) if m else (float(o) if isinstance(o, (int, float)) else None)
+                    if val is None:
+                        return
+                    for name in ("sclk", "gfx", "mclk", "fclk", "socclk"):
+                        if name in key and name not in found:
+                            found[name] = val
+            walk(d)
+            if found:
+                self.source = cmd[0]
+                return found
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            f = self._sample()
+            if f:
+                self.samples.append(f)
+            self._stop.wait(self._period)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=15)
+
+    def summary(self):
+        if not self.samples:
+            return {"source": None, "error": self.error}
+        out = {"source": self.source, "samples": len(self.samples)}
+        for k in sorted({k for s in self.samples for k in s}):
+            v = sorted(s[k] for s in self.samples if k in s)
+            out[f"{k}_mhz"] = {"min": v[0], "median": v[len(v) // 2], "max": v[-1]}
+        return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(name: str, grads, moms, weights, cfg, budget_s: float) -> dict:
     """Time the float64 oracle on a bounded sample of the workload's matrices."""
     import numpy as np
@@ -72,10 +193,12 @@ def cpu_baseline(name: str, grads, moms, weights, cfg, budget_s: float) -> dict:
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    oc = O.OracleConfig(ns_steps=cfg.ns_steps, pp_iterations=cfg.pp_iterations, pp_beta=cfg.pp_beta,
+    oc = O.OracleConfig(ns_steps=cfg.ns_steps, ns_a=cfg.ns_a, ns_b=cfg.ns_b, ns_c=cfg.ns_c,
+                        pp_iterations=cfg.pp_iterations, pp_beta=cfg.pp_beta,
                         mu=float(np.float32(cfg.mu)), nesterov=bool(cfg.nesterov),
                         power_steps=cfg.power_steps, contra=float(np.float32(cfg.contra)),
-                        target_uw=float(np.float32(cfg.target_uw)), lr=float(np.float32(cfg.lr)))
+                        target_uw=float(np.float32(cfg.target_uw)), lr=float(np.float32(cfg.lr)),
+                        momentum="sgd" if cfg.flags & 1 else "ema", wide_rows=bool(cfg.flags & 2))
     # smallest matrices first so the sample stays bounded
     order = sorted(range(len(grads)), key=lambda i: grads[i].numel())
     done, flops, t_total = [], 0.0, 0.0
@@ -95,7 +218,8 @@ def cpu_baseline(name: str, grads, moms, weights, cfg, budget_s: float) -> dict:
     kinds = ", ".join(f"{n} x {r}x{c}" for (r, c), n in Counter(done).items())
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(done)} matrices of {name} ({kinds}), smallest first, float64 numpy, "
-                      f"{t_total:.1f} s"}
+                      f"{t_total:.1f} s",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def main() -> int:
@@ -109,6 +233,7 @@ def main() -> int:
                          "five-step Muon recipe (momentum after its warm-up, NS5, no Aurora/Contra/floor)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-launch event timing")
+    ap.add_argument("--no-clocks", action="store_true", help="do not sample GPU clocks with the SMI tool")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -162,6 +287,9 @@ def main() -> int:
         h.profile_reset()
         h.profile_enable(True)
     torch.cuda.synchronize()
+    sampler = ClockSampler() if not a.no_clocks else None
+    if sampler:
+        sampler.__enter__()
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -171,6 +299,8 @@ def main() -> int:
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if sampler:
+        sampler.__exit__(None, None, None)
     ms_ev = ev0.elapsed_time(ev1)
     log(f"[bench] timed {a.steps} steps: wall {wall * 1e3:.1f} ms, events {ms_ev:.1f} ms")
     p = None
@@ -195,26 +325,44 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": a.workload, "recipe": a.recipe, "matrices": len(shapes), "matrix_params": params,
                    "counted_ns_tflop_per_step": round(flops / 1e12, 3),
+                   "algorithmic_ns_tflop_per_step": round(algorithmic_flops(shapes, cfg) / 1e12, 3),
                    "matrix_params_per_s": round(params / (ms_per_step * 1e-3), 1),
                    "pct_bf16_peak_whole_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
                    "parallelism": "single GPU"},
     }
     if p is not None and p["gemm_launches"] > 0:
-        achieved = p["gemm_counted_flop"] / (p["gemm_ms"] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if w.grad_dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+        gemm_s = p["gemm_ms"] * 1e-3
+        algo = algorithmic_flops(shapes, cfg) * a.steps
+        achieved = algo / gemm_s / 1e12
+        counted = p["gemm_counted_flop"] / gemm_s / 1e12
+        executed = p["gemm_executed_flop"] / gemm_s / 1e12
+        esz = 2 if w.grad_dtype == torch.bfloat16 else 4
+        wsz = (2 if w.weight_dtype == torch.bfloat16 else 4) if w.weights else 0
+        budget = stream_budget_bytes(shapes, esz, wsz, cfg) * a.steps
         out["roofline"] = {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             # the byte-counter record was taken on the Aurora step's launches
             "traffic": measured_traffic(a.workload) if a.recipe == "aurora" else None,
             "kernel": "k_ns_gemm (A = XX^T, B' = bA + cA^2 + aI, X' = B'X launches together)",
+            "flops": "algorithmic 3 s^2 L + s^3 per iteration (symmetric halves once)",
             "launches": int(p["gemm_launches"]),
             "avg_launch_ms": round(p["gemm_ms"] / p["gemm_launches"], 4),
-            "executed_tflops": round(p["gemm_executed_flop"] / (p["gemm_ms"] * 1e-3) / 1e12, 2),
+            "counted_tflops": round(counted, 2), "frac_counted": round(counted / peak, 4),
+            "executed_tflops": round(executed, 2), "frac_executed": round(executed / peak, 4),
             "stream_kernels_ms_per_step": round(p["stream_ms"] / a.steps, 3),
-            "stream_kernels_gbps": round(p["stream_bytes"] / (p["stream_ms"] * 1e-3) / 1e9, 1)
+            "stream_kernels_own_gbps": round(p["stream_bytes"] / (p["stream_ms"] * 1e-3) / 1e9, 1)
             if p["stream_ms"] > 0 else None,
+            "stream_budget_gb_per_step": round(budget / a.steps / 1e9, 3),
+            "stream_budget_gbps": round(budget / (p["stream_ms"] * 1e-3) / 1e9, 1) if p["stream_ms"] > 0 else None,
+            "stream_budget_frac_hbm": round(budget / (p["stream_ms"] * 1e-3) / 8e12, 4) if p["stream_ms"] > 0
+            else None,
+            "aurora_vector_ms_per_step": round(p["aux_ms"] / a.steps, 3),
+            "aurora_vector_gbps": round(p["aux_bytes"] / (p["aux_ms"] * 1e-3) / 1e9, 1) if p["aux_ms"] > 0 else None,
         }
+    if sampler:
+        out["clocks"] = sampler.summary()
     if a.cpu_budget > 0:
         log("[bench] timing the float64 oracle on a sample")
         grads0, moms0, weights0 = gen.make_batch(a.workload, dev)   # pristine inputs

@@ -140,9 +140,15 @@ typedef struct {
   double  gemm_ms;            /* summed event time of those launches */
   double  gemm_counted_flop;  /* 4 s^2 L + 2 s^3 per iteration per matrix (s <= L) */
   double  gemm_executed_flop; /* flops the tiles actually issue (symmetric tiles skipped) */
-  int64_t stream_launches;    /* bandwidth-bound launches (momentum, power, tail, ...) */
+  int64_t stream_launches;    /* bandwidth-bound launches of the step itself: momentum and
+                                 norms, power iteration, tail (and the latency kernels between) */
   double  stream_ms;
   double  stream_bytes;       /* algorithmic HBM bytes of those launches */
+  int64_t aux_launches;       /* Aurora vector kernels feeding the products: the pass prologue
+                                 (X0 = scale D o T in both orientations) and the D update */
+  double  aux_ms;
+  double  aux_bytes;          /* HBM bytes of those launches (source read, iterate pair written;
+                                 D update: one read of U) */
 } muon_profile;
 
 typedef struct muon_handle muon_handle;

@@ -68,7 +68,8 @@ class MuonProfile(ctypes.Structure):
                 ("gemm_counted_flop", ctypes.c_double),
                 ("gemm_executed_flop", ctypes.c_double),
                 ("stream_launches", ctypes.c_int64), ("stream_ms", ctypes.c_double),
-                ("stream_bytes", ctypes.c_double)]
+                ("stream_bytes", ctypes.c_double), ("aux_launches", ctypes.c_int64),
+                ("aux_ms", ctypes.c_double), ("aux_bytes", ctypes.c_double)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

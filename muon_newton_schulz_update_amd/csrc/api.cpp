@@ -151,7 +151,7 @@ std::string plan_key(int kind, int pp, bool wide_rows, int n, const muon_matrix*
 
 struct ProfRec {
   hipEvent_t a, b;
-  int cls;  // 0 gemm, 1 stream
+  int cls;  // 0 gemm, 1 stream, 2 aux (prologue, D update)
   double amount, amount2;
 };
 
@@ -544,10 +544,14 @@ muon_status drain_profile(muon_handle* h) {
       h->acc.gemm_ms += ms;
       h->acc.gemm_counted_flop += r.amount;
       h->acc.gemm_executed_flop += r.amount2;
-    } else {
+    } else if (r.cls == 1) {
       h->acc.stream_launches += 1;
       h->acc.stream_ms += ms;
       h->acc.stream_bytes += r.amount;
+    } else {
+      h->acc.aux_launches += 1;
+      h->acc.aux_ms += ms;
+      h->acc.aux_bytes += r.amount;
     }
     h->ev_pool.push_back(r.a);
     h->ev_pool.push_back(r.b);
@@ -649,7 +653,7 @@ muon_status run(muon_handle* h, const Call& c) {
 
   // algorithmic byte counts for the profile
   double el_ns = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
-  double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}};
+  double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_dup[2] = {0, 0};
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
     const double el = (double)m.rows * m.cols;
@@ -663,7 +667,10 @@ muon_status run(muon_handle* h, const Call& c) {
     // prologue bytes: read the source, write the iterate and its transpose
     const double pro = el * esz(m.ns_t) + 2.0 * m.s_pad * (double)m.L_pad * esz(m.ns_t);
     b_pro[0][m.ns_t] += pro;
-    if (m.aurora) b_pro[1][m.ns_t] += pro;
+    if (m.aurora) {
+      b_pro[1][m.ns_t] += pro;
+      b_dup[m.ns_t] += (double)m.s * m.L * esz(m.ns_t);   // one read of U
+    }
   }
   (void)el_all;
 
@@ -720,7 +727,7 @@ muon_status run(muon_handle* h, const Call& c) {
     for (int t = 0; t < 2; ++t) {
       const HostList& L = P->prologue[g][t];
       if (L.nblk == 0) continue;
-      ProfScope ps(h, 1, b_pro[g][t]);
+      ProfScope ps(h, 2, b_pro[g][t]);
       CHECK_LAUNCH(h, launch_prologue(t, D, dev_list(*P, L), L.nblk, upd ? 1 : 0, st));
     }
     for (int k = 0; k < cfg.ns_steps; ++k) {
@@ -738,10 +745,10 @@ muon_status run(muon_handle* h, const Call& c) {
       for (int t = 0; t < 2; ++t) {
         const HostList& L = P->dupdate[t];
         if (L.nblk == 0) continue;
-        ProfScope ps(h, 1, 0);
+        ProfScope ps(h, 2, b_dup[t]);
         CHECK_LAUNCH(h, launch_aurora_dupdate(t, D, dev_list(*P, L), L.nblk, fin, cfg.pp_eps, cfg.pp_beta, st));
       }
-      ProfScope ps(h, 1, 0);
+      ProfScope ps(h, 2, 0);
       CHECK_LAUNCH(h, launch_aurora_scale(D, dev_list(*P, P->ascale), P->ascale.nblk, cfg.ns_eps, st));
     }
   }
