@@ -140,6 +140,9 @@ typedef struct {
   double  gemm_ms;            /* summed event time of those launches */
   double  gemm_counted_flop;  /* 4 s^2 L + 2 s^3 per iteration per matrix (s <= L) */
   double  gemm_executed_flop; /* flops the tiles actually issue (symmetric tiles skipped) */
+  double  gemm_algorithmic_flop; /* flops the products need: the upper half of each symmetric
+                                    result, no padding (3 s^2 L + (4 r - 3) s^3 per block of r
+                                    iterations) */
   int64_t stream_launches;    /* bandwidth-bound launches of the step itself: momentum and
                                  norms, power iteration, tail (and the latency kernels between) */
   double  stream_ms;

@@ -67,6 +67,7 @@ class MuonProfile(ctypes.Structure):
     _fields_ = [("gemm_launches", ctypes.c_int64), ("gemm_ms", ctypes.c_double),
                 ("gemm_counted_flop", ctypes.c_double),
                 ("gemm_executed_flop", ctypes.c_double),
+                ("gemm_algorithmic_flop", ctypes.c_double),
                 ("stream_launches", ctypes.c_int64), ("stream_ms", ctypes.c_double),
                 ("stream_bytes", ctypes.c_double), ("aux_launches", ctypes.c_int64),
                 ("aux_ms", ctypes.c_double), ("aux_bytes", ctypes.c_double)]
@@ -329,6 +330,10 @@ def muon_update(grads: Sequence[torch.Tensor], momenta: Sequence[torch.Tensor],
     Momenta and weights are updated in place; update_out[i], when given,
     receives the update after the floor and before the learning rate.
     """
+    _update("muon_update", grads, momenta, weights, cfg, update_out, handle)
+
+
+def _update(name, grads, momenta, weights, cfg, update_out, handle):
     grads = list(grads)
     momenta = list(momenta)
     n = len(grads)
@@ -344,7 +349,8 @@ def muon_update(grads: Sequence[torch.Tensor], momenta: Sequence[torch.Tensor],
     m = _array([_desc(t, "momentum") for t in momenta])
     w = _array([_desc(t, "weight") for t in weights]) if weights is not None else None
     u = _array([_desc(t, "update_out") for t in update_out]) if update_out is not None else None
-    h._check(h._lib.muon_update(h.ptr, n, g, m, w, u, ctypes.byref(cfg) if cfg is not None else None))
+    fn = getattr(h._lib, name)
+    h._check(fn(h.ptr, n, g, m, w, u, ctypes.byref(cfg) if cfg is not None else None))
 
 
 def check_update_args(grads, momenta, weights=None, update_out=None, cfg=None) -> tuple[int, str]:

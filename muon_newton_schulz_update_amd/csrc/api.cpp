@@ -37,13 +37,13 @@
 namespace muon {
 
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
-                          float ca, float cb, float cc, int variant, int tile, hipStream_t st);
+                          int roles, float ca, float cb, float cc, int variant, int tile, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  int sgd, hipStream_t st);
 hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st);
 hipError_t launch_norms_scalars(DevMat* m, LaunchList L, int nblk, float ns_eps, int init_power, hipStream_t st);
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st);
-hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, int fin, float pp_eps, float pp_beta,
+hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, float pp_eps, float pp_beta,
                                  hipStream_t st);
 hipError_t launch_aurora_scale(DevMat* m, LaunchList L, int nblk, float ns_eps, hipStream_t st);
 hipError_t launch_power_matvec(const DevMat* m, LaunchList L, int nblk, int steps, int final_pass, hipStream_t st);
@@ -53,10 +53,9 @@ hipError_t launch_power_fused(int ns_t, const DevMat* m, LaunchList L, int nblk,
 hipError_t launch_power_wsum(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_normalize(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_sigma(DevMat* m, LaunchList L, int nblk, float contra, hipStream_t st);
-hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, int fin, hipStream_t st);
+hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, hipStream_t st);
 hipError_t launch_tail_finalize(DevMat* m, LaunchList L, int nblk, float target_uw, hipStream_t st);
-hipError_t launch_tail_apply(const DevMat* m, LaunchList L, int nblk, int fin, float lr, int copy_only,
-                             hipStream_t st);
+hipError_t launch_tail_apply(const DevMat* m, LaunchList L, int nblk, float lr, int copy_only, hipStream_t st);
 
 namespace {
 
@@ -75,17 +74,59 @@ struct MatInfo {
   int user;                  // index in the caller's batch
   int rows, cols, s, L, s_pad, L_pad;
   bool tall, square, aurora, eq_short;
+  int block;                 // Newton-Schulz iterations per block (1 for squares)
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv, wband;
-  size_t o_xn, o_x[2], o_xt[2], o_a, o_b, o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
+  size_t o_xn, o_x[2], o_xt[2], o_sq[SQ_COUNT], o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
       o_pwpart, o_tailpart, o_linepart, o_scal, o_ist;
 };
+
+// Newton-Schulz iterations per block of a rectangular matrix. A block stays
+// on the short side until its last product, so it needs 3 s^2 L + (4 r - 3)
+// s^3 flops for r iterations instead of r (3 s^2 L + s^3); a square matrix
+// gains nothing and keeps one iteration per block, and so does a short side
+// below kBlockMinShort (its products are few tiles, bound by launch count).
+// Within a block, Q = B'_{r-1} ... B'_0 has eigenvalues prod_j f(sigma_j),
+// f(sigma) = a + b sigma^2 + c sigma^4; stored in bf16, its entries carry
+// rounding relative to its largest eigenvalue, so the directions with the
+// smallest lose (max f / min f)^r of their precision. The block length is
+// the largest r <= kDefaultBlock with that ratio at most kMaxBlockSpread over
+// sigma in [0, 1] (the page's polynomial: ratio 2, r = 4; the classic one,
+// 3.4445 / 0.701 = 4.9, gets r = 1). MUON_NS_BLOCK (1..8, read when a plan is
+// built) forces a length for every rectangular matrix.
+constexpr int kDefaultBlock = 4;
+constexpr double kMaxBlockSpread = 16.0;
+constexpr int kBlockMinShort = 512;
 
 // The fused power pass takes matrices up to kFusedCols columns whose rows are
 // whole 16-byte chunks of the NS type (it loads 8-element chunks only); it
 // depends on the matrix alone, never on the rest of the batch.
 inline bool fused_power(const MatInfo& m) {
   return m.cols <= kFusedCols && ((size_t)m.cols * (m.ns_t == DT_BF16 ? 2 : 4)) % 16 == 0;
+}
+
+// Matrices of one pass group launch together when they share a block length:
+// class 0 holds the one-iteration blocks, class 1 the longer ones.
+inline int block_class(const MatInfo& m) { return m.block > 1 ? 1 : 0; }
+
+// Block length for the rectangular matrices of a call (see kDefaultBlock);
+// *forced is set when MUON_NS_BLOCK gives it.
+int rect_block(const muon_config& cfg, bool* forced) {
+  *forced = false;
+  if (const char* v = getenv("MUON_NS_BLOCK")) {
+    *forced = true;
+    return std::min(8, std::max(1, atoi(v)));
+  }
+  double lo = 1e300, hi = 0;
+  for (int i = 0; i <= 1000; ++i) {
+    const double x = i / 1000.0, x2 = x * x;
+    const double f = fabs((double)cfg.ns_a + (double)cfg.ns_b * x2 + (double)cfg.ns_c * x2 * x2);
+    lo = std::min(lo, f);
+    hi = std::max(hi, f);
+  }
+  if (!(lo > 0) || hi / lo <= 1.0) return lo > 0 ? kDefaultBlock : 1;
+  const int r = (int)floor(log(kMaxBlockSpread) / log(hi / lo) + 1e-9);
+  return std::min(kDefaultBlock, std::max(1, r));
 }
 
 // Host copy of one LaunchList: offset of its int arrays in the meta buffer.
@@ -101,8 +142,11 @@ struct GemmList {
   int n = 0;
   int tile = kTile;                 // output tile edge of its items (256, or 128 for small launches)
   size_t off = 0;                   // byte offset of TileItem array in meta
-  double counted = 0, executed = 0; // flops
+  double counted_iter = 0;          // 4 s^2 L + 2 s^3 summed over its matrices: one standard iteration
+  double executed = 0;              // flops the tiles of one launch issue (padding, whole diagonal tiles)
+  double algorithmic = 0;           // flops one launch needs (upper half of a symmetric result)
 };
+enum { LIST_GRAM = 0, LIST_SQ = 1, LIST_BX = 2 };   // tile lists: Gram, short-side products, X' = Q X
 
 // A product launch with fewer 256-tiles than this uses 128-tiles: with one
 // 256-tile workgroup per CU such a launch is a few rounds of workgroups and
@@ -126,7 +170,8 @@ struct Plan {
   HostList matvec_w, rmatvec_w;           // X v + X^T u for matrices wider than kFusedCols
   HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
   HostList dupdate[2];      // [ns_t]
-  GemmList gemm[2][2][3];   // [group][ns_t][mode]
+  GemmList gemm[2][2][2][3];   // [pass group][block class][ns_t][list]
+  int block = kDefaultBlock;    // iterations per block of a rectangular matrix
   // device meta: DevMat array followed by the list arrays
   std::vector<uint8_t> meta_host;  // list part (static)
   size_t meta_devmat_bytes = 0;
@@ -136,11 +181,11 @@ struct Plan {
   uint64_t last_use = 0;
 };
 
-std::string plan_key(int kind, int pp, bool wide_rows, int n, const muon_matrix* in) {
+std::string plan_key(int kind, int pp, bool wide_rows, int block, bool forced, int n, const muon_matrix* in) {
   std::string k;
   k.reserve(16 + n * 12);
   char buf[64];
-  snprintf(buf, sizeof(buf), "%d/%d/%d/%d|", kind, pp, (int)wide_rows, n);
+  snprintf(buf, sizeof(buf), "%d/%d/%d/%d/%d/%d|", kind, pp, (int)wide_rows, block, (int)forced, n);
   k += buf;
   for (int i = 0; i < n; ++i) {
     snprintf(buf, sizeof(buf), "%lld,%lld,%d;", (long long)in[i].rows, (long long)in[i].cols, (int)in[i].dtype);
@@ -152,7 +197,7 @@ std::string plan_key(int kind, int pp, bool wide_rows, int n, const muon_matrix*
 struct ProfRec {
   hipEvent_t a, b;
   int cls;  // 0 gemm, 1 stream, 2 aux (prologue, D update)
-  double amount, amount2;
+  double amount, amount2, amount3;
 };
 
 }  // namespace
@@ -223,9 +268,11 @@ void add_gemm(std::vector<uint8_t>& meta, GemmList& G, std::vector<TileItem>& it
 // and the inputs' shapes and element types (exactly what plan_key holds):
 // caller pointers, strides, weights and outputs go into the per-call
 // descriptors.
-std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int n, const muon_matrix* in) {
+std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int block, bool forced, int n,
+                                 const muon_matrix* in) {
   auto P = std::make_unique<Plan>();
   P->kind = kind;
+  P->block = block;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -259,8 +306,17 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int n, const 
     m.o_x[1] = take(nsl);
     m.o_xt[0] = take(nsl);
     m.o_xt[1] = take(nsl);
-    m.o_a = take((size_t)m.s_pad * m.s_pad * e);
-    m.o_b = take((size_t)m.s_pad * m.s_pad * e);
+    m.block = m.square || (!forced && m.s < kBlockMinShort) ? 1 : P->block;
+    const size_t ssq = (size_t)m.s_pad * m.s_pad * e;
+    m.o_sq[SQ_A] = take(ssq);
+    m.o_sq[SQ_B] = take(ssq);
+    if (m.block > 1) {
+      m.o_sq[SQ_T] = take(ssq);
+      m.o_sq[SQ_Q0] = take(ssq);
+      m.o_sq[SQ_Q1] = take(ssq);
+    } else {   // one iteration per block: B'_0 is the only factor (Q0 = B); T and Q1 unused
+      m.o_sq[SQ_T] = m.o_sq[SQ_Q0] = m.o_sq[SQ_Q1] = m.o_sq[SQ_B];
+    }
     m.o_rowpart = take((size_t)m.rows * m.n_seg * 4);
     m.o_colpart = take(m.rows < m.cols ? (size_t)m.n_rt * m.cols * 4 : 4);
     m.o_rowsq = take((size_t)m.rows * 4);
@@ -369,68 +425,74 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int n, const 
       if (P->mats[i].aurora) { ms.push_back(i); bl.push_back(1); }
     add_list(meta, P->ascale, ms, bl);
   }
-  // Newton-Schulz tile lists: longest reduction first (LPT); within a matrix,
-  // tiles sharing a tile row are consecutive.
+  // Newton-Schulz tile lists, one set per (pass group, block class, NS type):
+  // the Gram (s x s upper tiles, K = L), the short-side products (s x s upper
+  // tiles, K = s; shared by GM_SQ and GM_SYM) and X' = Q X (s x L, K = s).
+  // Longest reduction first (LPT); within a matrix, tiles sharing a tile row
+  // are consecutive.
   int force_tile = 0;
   if (const char* v = getenv("MUON_NS_TILE")) force_tile = atoi(v) == 128 ? 128 : atoi(v) == 256 ? 256 : 0;
   for (int g = 0; g < 2; ++g)
-    for (int t = 0; t < 2; ++t)
-      for (int mode = 0; mode < 3; ++mode) {
-        std::vector<int> order;
-        for (int i = 0; i < nm; ++i) {
-          const MatInfo& m = P->mats[i];
-          if (m.ns_t != t || (g == 1 && !m.aurora)) continue;
-          order.push_back(i);
-        }
-        auto kdim = [&](int i) {
-          const MatInfo& m = P->mats[i];
-          return mode == GM_GRAM ? m.L_pad : m.s_pad;
-        };
-        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kdim(a) > kdim(b); });
-        std::vector<TileItem> items;
-        GemmList& G = P->gemm[g][t][mode];
-        long n256 = 0;
-        for (int i : order) {
-          const long ts = P->mats[i].s_pad / kTile, tl = P->mats[i].L_pad / kTile;
-          n256 += mode == GM_BX ? ts * tl : ts * (ts + 1) / 2;
-        }
-        G.tile = n256 < kSmallLaunchTiles ? 128 : kTile;
-        if (force_tile) G.tile = force_tile;
-        const int tile = G.tile;
-        for (int i : order) {
-          const MatInfo& m = P->mats[i];
-          const int ts = m.s_pad / tile, tl = m.L_pad / tile;
-          const double s = m.s, L = m.L;
-          const int tcols = mode == GM_BX ? tl : ts;
-          // Super-tiles of kSuperM x kSuperN tiles, row-major inside and
-          // across: one super-tile is one XCD's wave of workgroups, so its
-          // tiles share kSuperM row panels and kSuperN column panels in L2.
-          for (int a0 = 0; a0 < ts; a0 += kSuperM)
-            for (int b0 = 0; b0 < tcols; b0 += kSuperN)
-              for (int a = a0; a < std::min(ts, a0 + kSuperM); ++a)
-                for (int b = b0; b < std::min(tcols, b0 + kSuperN); ++b) {
-                  if (mode != GM_BX && b < a) continue;   // symmetric: upper tiles only
-                  items.push_back(TileItem{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
-                }
-          if (mode == GM_BX) {
-            G.counted += 2.0 * s * s * L;
-            G.executed += 2.0 * ts * tl * tile * (double)tile * m.s_pad;
-          } else {
-            const double K = mode == GM_GRAM ? m.L_pad : m.s_pad;
-            G.counted += mode == GM_GRAM ? 2.0 * s * s * L : 2.0 * s * s * s;
-            G.executed += 2.0 * (ts * (ts + 1) / 2) * tile * (double)tile * K;
+    for (int c = 0; c < 2; ++c)
+      for (int t = 0; t < 2; ++t)
+        for (int li = 0; li < 3; ++li) {
+          std::vector<int> order;
+          for (int i = 0; i < nm; ++i) {
+            const MatInfo& m = P->mats[i];
+            if (m.ns_t != t || (g == 1 && !m.aurora) || block_class(m) != c) continue;
+            order.push_back(i);
           }
+          auto kdim = [&](int i) {
+            const MatInfo& m = P->mats[i];
+            return li == LIST_GRAM ? m.L_pad : m.s_pad;
+          };
+          std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kdim(a) > kdim(b); });
+          std::vector<TileItem> items;
+          GemmList& G = P->gemm[g][c][t][li];
+          long n256 = 0;
+          for (int i : order) {
+            const long ts = P->mats[i].s_pad / kTile, tl = P->mats[i].L_pad / kTile;
+            n256 += li == LIST_BX ? ts * tl : ts * (ts + 1) / 2;
+          }
+          G.tile = n256 < kSmallLaunchTiles ? 128 : kTile;
+          if (force_tile) G.tile = force_tile;
+          const int tile = G.tile;
+          for (int i : order) {
+            const MatInfo& m = P->mats[i];
+            const int ts = m.s_pad / tile, tl = m.L_pad / tile;
+            const double s = m.s, L = m.L;
+            const int tcols = li == LIST_BX ? tl : ts;
+            // Super-tiles of kSuperM x kSuperN tiles, row-major inside and
+            // across: one super-tile is one XCD's wave of workgroups, so its
+            // tiles share kSuperM row panels and kSuperN column panels in L2.
+            for (int a0 = 0; a0 < ts; a0 += kSuperM)
+              for (int b0 = 0; b0 < tcols; b0 += kSuperN)
+                for (int a = a0; a < std::min(ts, a0 + kSuperM); ++a)
+                  for (int b = b0; b < std::min(tcols, b0 + kSuperN); ++b) {
+                    if (li != LIST_BX && b < a) continue;   // symmetric: upper tiles only
+                    items.push_back(TileItem{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
+                  }
+            // one standard iteration of this matrix, in the counted convention
+            G.counted_iter += 4.0 * s * s * L + 2.0 * s * s * s;
+            if (li == LIST_BX) {
+              G.algorithmic += 2.0 * s * s * L;
+              G.executed += 2.0 * ts * tl * tile * (double)tile * m.s_pad;
+            } else {
+              const double K = li == LIST_GRAM ? m.L_pad : m.s_pad;
+              G.algorithmic += li == LIST_GRAM ? s * s * L : s * s * s;   // the upper half of a symmetric result
+              G.executed += 2.0 * (ts * (ts + 1) / 2) * tile * (double)tile * K;
+            }
+          }
+          add_gemm(meta, G, items);
         }
-        add_gemm(meta, G, items);
-      }
   return P;
 }
 
-LaunchList dev_list(const Plan& P, const HostList& L) {
+LaunchList dev_list(const uint8_t* meta, const HostList& L) {
   LaunchList d;
   d.n = L.n;
-  d.off = (const int32_t*)((const uint8_t*)P.meta_dev + L.off_off);
-  d.mat = (const int32_t*)((const uint8_t*)P.meta_dev + L.off_mat);
+  d.off = (const int32_t*)(meta + L.off_off);
+  d.mat = (const int32_t*)(meta + L.off_mat);
   return d;
 }
 
@@ -517,11 +579,13 @@ struct ProfScope {
   muon_handle* h;
   ProfRec r{};
   bool on;
-  ProfScope(muon_handle* hh, int cls, double amount, double amount2 = 0) : h(hh), on(hh->prof) {
+  ProfScope(muon_handle* hh, int cls, double amount, double amount2 = 0, double amount3 = 0)
+      : h(hh), on(hh->prof) {
     if (!on) return;
     r.cls = cls;
     r.amount = amount;
     r.amount2 = amount2;
+    r.amount3 = amount3;
     r.a = pool_event(h);
     r.b = pool_event(h);
     if (!r.a || !r.b) { on = false; return; }
@@ -544,6 +608,7 @@ muon_status drain_profile(muon_handle* h) {
       h->acc.gemm_ms += ms;
       h->acc.gemm_counted_flop += r.amount;
       h->acc.gemm_executed_flop += r.amount2;
+      h->acc.gemm_algorithmic_flop += r.amount3;
     } else if (r.cls == 1) {
       h->acc.stream_launches += 1;
       h->acc.stream_ms += ms;
@@ -583,7 +648,9 @@ muon_status run(muon_handle* h, const Call& c) {
   const muon_config& cfg = c.cfg;
   const int pp = c.kind == KIND_NS ? 0 : cfg.pp_iterations;
   const bool wide_rows = (cfg.flags & MUON_FLAG_WIDE_ROWS) != 0;
-  const std::string key = plan_key(c.kind, pp, wide_rows, c.n, c.in);
+  bool forced = false;
+  const int block = rect_block(cfg, &forced);
+  const std::string key = plan_key(c.kind, pp, wide_rows, block, forced, c.n, c.in);
   auto it = h->plans.find(key);
   Plan* P;
   if (it == h->plans.end()) {
@@ -596,7 +663,7 @@ muon_status run(muon_handle* h, const Call& c) {
       if (victim->second->meta_dev) HIP_TRY(h, hipFree(victim->second->meta_dev));
       h->plans.erase(victim);
     }
-    auto p = build_plan(c.kind, pp, wide_rows, c.n, c.in);
+    auto p = build_plan(c.kind, pp, wide_rows, block, forced, c.n, c.in);
     P = p.get();
     h->plans.emplace(key, std::move(p));
   } else {
@@ -608,9 +675,10 @@ muon_status run(muon_handle* h, const Call& c) {
   if (rc) return rc;
   rc = ensure_meta(h, *P);
   if (rc) return rc;
+  uint8_t* ws = (uint8_t*)h->ws;
+  uint8_t* meta = (uint8_t*)P->meta_dev;
 
   // descriptors
-  uint8_t* ws = (uint8_t*)h->ws;
   std::vector<DevMat> dm(P->mats.size());
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
@@ -634,7 +702,8 @@ muon_status run(muon_handle* h, const Call& c) {
     d.xn = c.kind == KIND_UPDATE ? ws + m.o_xn : nullptr;
     d.x[0] = ws + m.o_x[0]; d.x[1] = ws + m.o_x[1];
     d.xt[0] = ws + m.o_xt[0]; d.xt[1] = ws + m.o_xt[1];
-    d.a = ws + m.o_a; d.b = ws + m.o_b;
+    for (int r = 0; r < SQ_COUNT; ++r) d.sq[r] = ws + m.o_sq[r];
+    d.fin = ((cfg.ns_steps + m.block - 1) / m.block) & 1;   // blocks per pass, mod 2
     d.rowpart = (float*)(ws + m.o_rowpart); d.colpart = (float*)(ws + m.o_colpart);
     d.rowsq = (float*)(ws + m.o_rowsq); d.colsq = (float*)(ws + m.o_colsq);
     d.rho = (float*)(ws + m.o_rho); d.dvec = (float*)(ws + m.o_dvec);
@@ -646,7 +715,7 @@ muon_status run(muon_handle* h, const Call& c) {
   rc = upload_devmat(h, *P, dm);
   if (rc) return rc;
 
-  DevMat* D = (DevMat*)P->meta_dev;
+  DevMat* D = (DevMat*)meta;
   hipStream_t st = h->stream;
   const bool upd = c.kind == KIND_UPDATE;
   const bool contra = upd && cfg.contra != 0.f;
@@ -677,13 +746,13 @@ muon_status run(muon_handle* h, const Call& c) {
   // 1. momentum/Nesterov (or input) + norms
   {
     ProfScope ps(h, 1, b_mom);
-    CHECK_LAUNCH(h, launch_momentum_stats(D, dev_list(*P, P->stream), P->stream.nblk, upd ? 1 : 0, cfg.mu,
+    CHECK_LAUNCH(h, launch_momentum_stats(D, dev_list(meta, P->stream), P->stream.nblk, upd ? 1 : 0, cfg.mu,
                                           cfg.nesterov, (cfg.flags & MUON_FLAG_SGD_MOMENTUM) ? 1 : 0, st));
   }
   {
     ProfScope ps(h, 1, 0);
-    CHECK_LAUNCH(h, launch_norms_lines(D, dev_list(*P, P->lines), P->lines.nblk, cfg.pp_eps, st));
-    CHECK_LAUNCH(h, launch_norms_scalars(D, dev_list(*P, P->permat), P->permat.nblk, cfg.ns_eps, contra ? 1 : 0,
+    CHECK_LAUNCH(h, launch_norms_lines(D, dev_list(meta, P->lines), P->lines.nblk, cfg.pp_eps, st));
+    CHECK_LAUNCH(h, launch_norms_scalars(D, dev_list(meta, P->permat), P->permat.nblk, cfg.ns_eps, contra ? 1 : 0,
                                          st));
   }
   // 2. power iteration
@@ -693,80 +762,108 @@ muon_status run(muon_handle* h, const Call& c) {
         const HostList& F = P->fused[t];
         if (!F.nblk) continue;
         ProfScope ps(h, 1, el_fused[t]);
-        CHECK_LAUNCH(h, launch_power_fused(t, D, dev_list(*P, F), F.nblk, cfg.power_steps, F.max_cols, st));
+        CHECK_LAUNCH(h, launch_power_fused(t, D, dev_list(meta, F), F.nblk, cfg.power_steps, F.max_cols, st));
       }
       if (P->matvec_w.nblk) {
         {
           ProfScope ps(h, 1, el_wide);
-          CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(*P, P->matvec_w), P->matvec_w.nblk, cfg.power_steps, 0,
+          CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec_w), P->matvec_w.nblk, cfg.power_steps, 0,
                                               st));
         }
         ProfScope ps(h, 1, el_wide);
-        CHECK_LAUNCH(h, launch_power_rmatvec(D, dev_list(*P, P->rmatvec_w), P->rmatvec_w.nblk, cfg.power_steps,
+        CHECK_LAUNCH(h, launch_power_rmatvec(D, dev_list(meta, P->rmatvec_w), P->rmatvec_w.nblk, cfg.power_steps,
                                              st));
       }
       {
         ProfScope ps(h, 1, 0);
-        CHECK_LAUNCH(h, launch_power_wsum(D, dev_list(*P, P->colblk), P->colblk.nblk, cfg.power_steps, st));
-        CHECK_LAUNCH(h, launch_power_normalize(D, dev_list(*P, P->permat), P->permat.nblk, cfg.power_steps, st));
+        CHECK_LAUNCH(h, launch_power_wsum(D, dev_list(meta, P->colblk), P->colblk.nblk, cfg.power_steps, st));
+        CHECK_LAUNCH(h, launch_power_normalize(D, dev_list(meta, P->permat), P->permat.nblk, cfg.power_steps, st));
       }
     }
     {
       ProfScope ps(h, 1, el_ns);
-      CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(*P, P->matvec), P->matvec.nblk, cfg.power_steps, 1, st));
+      CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec), P->matvec.nblk, cfg.power_steps, 1, st));
     }
     {
       ProfScope ps(h, 1, 0);
-      CHECK_LAUNCH(h, launch_power_sigma(D, dev_list(*P, P->permat), P->permat.nblk, cfg.contra, st));
+      CHECK_LAUNCH(h, launch_power_sigma(D, dev_list(meta, P->permat), P->permat.nblk, cfg.contra, st));
     }
   }
-  // 3. Newton-Schulz passes
-  const int fin = cfg.ns_steps & 1;
+  // 3. Newton-Schulz passes. Per pass group, block class and type, the
+  // iterations run in blocks of r (see ns_gemm.hip): A = X X^T; for each j,
+  // B'_j = a I + b A + c A^2 (into Q0 when j = 0), Q <- B'_j Q, and unless j
+  // is the block's last, A <- B'_j (B'_j A); then X' = Q X.
   for (int p = 0; p < P->passes; ++p) {
     const int g = p == 0 ? 0 : 1;
     for (int t = 0; t < 2; ++t) {
       const HostList& L = P->prologue[g][t];
       if (L.nblk == 0) continue;
       ProfScope ps(h, 2, b_pro[g][t]);
-      CHECK_LAUNCH(h, launch_prologue(t, D, dev_list(*P, L), L.nblk, upd ? 1 : 0, st));
+      CHECK_LAUNCH(h, launch_prologue(t, D, dev_list(meta, L), L.nblk, upd ? 1 : 0, st));
     }
-    for (int k = 0; k < cfg.ns_steps; ++k) {
-      const int cur = k & 1;
-      for (int mode = 0; mode < 3; ++mode)
-        for (int t = 0; t < 2; ++t) {
-          const GemmList& G = P->gemm[g][t][mode];
-          if (G.n == 0) continue;
-          ProfScope ps(h, 0, G.counted, G.executed);
-          CHECK_LAUNCH(h, launch_ns_gemm(t, D, (const TileItem*)((uint8_t*)P->meta_dev + G.off), G.n, mode, cur,
-                                         cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, G.tile, st));
+    const int last_pass = p + 1 == P->passes ? NS_LAST_PASS : 0;
+    for (int c = 0; c < 2; ++c)
+      for (int t = 0; t < 2; ++t) {
+        const GemmList* GL = P->gemm[g][c][t];
+        if (GL[LIST_GRAM].n == 0) continue;
+        const int r = c == 0 ? 1 : P->block;
+        auto gemm = [&](int li, int mode, int cur, int roles, double counted) -> muon_status {
+          const GemmList& G = GL[li];
+          ProfScope ps(h, 0, counted, G.executed, G.algorithmic);
+          CHECK_LAUNCH(h, launch_ns_gemm(t, D, (const TileItem*)(meta + G.off), G.n, mode, cur,
+                                         roles, cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, G.tile, st));
+          return MUON_OK;
+        };
+        int cur = 0;
+        for (int k = 0; k < cfg.ns_steps; cur ^= 1) {
+          const int rr = std::min(r, cfg.ns_steps - k);
+          k += rr;
+          muon_status e = gemm(LIST_GRAM, GM_GRAM, cur, ns_roles(0, 0, SQ_A), 0.0);
+          for (int j = 0; !e && j < rr; ++j) {
+            const int bj = j == 0 ? SQ_Q0 : SQ_B;   // B'_0 is Q_1 itself
+            e = gemm(LIST_SQ, GM_SQ, cur, ns_roles(SQ_A, SQ_A, bj), 0.0);
+            if (!e && j >= 1)
+              e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(SQ_B, (j - 1) & 1 ? SQ_Q1 : SQ_Q0, j & 1 ? SQ_Q1 : SQ_Q0),
+                       0.0);
+            if (!e && j + 1 < rr) {
+              e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_A, SQ_T), 0.0);
+              if (!e) e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_T, SQ_A), 0.0);
+            }
+          }
+          if (!e) {
+            const int roles = ns_roles((rr - 1) & 1 ? SQ_Q1 : SQ_Q0, 0, 0) |
+                              (k == cfg.ns_steps ? NS_LAST_BX | last_pass : 0);
+            e = gemm(LIST_BX, GM_BX, cur, roles, rr * GL[LIST_BX].counted_iter);
+          }
+          if (e) return e;
         }
-    }
+      }
     if (p + 1 < P->passes) {
       for (int t = 0; t < 2; ++t) {
         const HostList& L = P->dupdate[t];
         if (L.nblk == 0) continue;
         ProfScope ps(h, 2, b_dup[t]);
-        CHECK_LAUNCH(h, launch_aurora_dupdate(t, D, dev_list(*P, L), L.nblk, fin, cfg.pp_eps, cfg.pp_beta, st));
+        CHECK_LAUNCH(h, launch_aurora_dupdate(t, D, dev_list(meta, L), L.nblk, cfg.pp_eps, cfg.pp_beta, st));
       }
       ProfScope ps(h, 2, 0);
-      CHECK_LAUNCH(h, launch_aurora_scale(D, dev_list(*P, P->ascale), P->ascale.nblk, cfg.ns_eps, st));
+      CHECK_LAUNCH(h, launch_aurora_scale(D, dev_list(meta, P->ascale), P->ascale.nblk, cfg.ns_eps, st));
     }
   }
   // 4. tail
   if (upd) {
     {
       ProfScope ps(h, 1, b_tail_r);
-      CHECK_LAUNCH(h, launch_tail_reduce(D, dev_list(*P, P->stream), P->stream.nblk, fin, st));
+      CHECK_LAUNCH(h, launch_tail_reduce(D, dev_list(meta, P->stream), P->stream.nblk, st));
     }
     {
       ProfScope ps(h, 1, 0);
-      CHECK_LAUNCH(h, launch_tail_finalize(D, dev_list(*P, P->permat), P->permat.nblk, cfg.target_uw, st));
+      CHECK_LAUNCH(h, launch_tail_finalize(D, dev_list(meta, P->permat), P->permat.nblk, cfg.target_uw, st));
     }
     ProfScope ps(h, 1, b_tail_a);
-    CHECK_LAUNCH(h, launch_tail_apply(D, dev_list(*P, P->stream), P->stream.nblk, fin, cfg.lr, 0, st));
+    CHECK_LAUNCH(h, launch_tail_apply(D, dev_list(meta, P->stream), P->stream.nblk, cfg.lr, 0, st));
   } else {
     ProfScope ps(h, 1, b_tail_a);
-    CHECK_LAUNCH(h, launch_tail_apply(D, dev_list(*P, P->stream), P->stream.nblk, fin, 0.f, 1, st));
+    CHECK_LAUNCH(h, launch_tail_apply(D, dev_list(meta, P->stream), P->stream.nblk, 0.f, 1, st));
   }
   if (h->prof && h->recs.size() > 200000) return drain_profile(h);
   return MUON_OK;
@@ -841,7 +938,11 @@ extern "C" muon_status muon_reserve(muon_handle* h, int n, const muon_matrix* sh
   }
   size_t need = 0;
   for (int kind = 0; kind < 3; ++kind) {
-    auto P = build_plan(kind, 2, false, n, shapes);
+    bool forced = false;
+    muon_config dflt;
+    muon_config_default(&dflt);
+    const int block = rect_block(dflt, &forced);
+    auto P = build_plan(kind, 2, false, block, forced, n, shapes);
     need = std::max(need, P->ws_bytes);
   }
   return ensure_workspace(h, need);

@@ -6,7 +6,8 @@
 //   xt[2]   L_pad x s_pad, ld = s_pad: its transpose, written by the same
 //           epilogue, so every product of the iteration reads both operands
 //           with the reduction index contiguous ("NT" form)
-//   a, b    s_pad x s_pad: Gram A = X X^T and B = b A + c A^2
+//   sq[5]   s_pad x s_pad: the short-side matrices of a block of iterations
+//           (roles SQ_A .. SQ_Q1 below)
 //   float vectors and partial-sum buffers (see DevMat)
 // s = min(rows, cols) (the short side), L = max(rows, cols); both padded up to
 // a multiple of the 256-wide tile. Padding is zero and stays exactly zero
@@ -49,6 +50,33 @@ enum IState : int {
   IS_COUNT = 4
 };
 
+// Matrix-core products. Every product reads two row-major operands with the
+// reduction index contiguous (C[m][n] = sum_k P[m][k] Q[n][k]):
+//   GM_GRAM  A = X X^T            (P = Q = x[cur])          upper tiles, mirrored
+//   GM_SQ    B' = b A + c A A + a I (P = Q = sq[rp])        upper tiles, mirrored
+//   GM_SYM   C = P Q              (sq[rp], sq[rq]; both symmetric and
+//                                  commuting, so C is too)  upper tiles, mirrored
+//   GM_BX    X' = P X             (P = sq[rp], Q = xt[cur]) writes X' and X'^T
+enum GemmMode : int { GM_GRAM = 0, GM_SQ = 1, GM_SYM = 2, GM_BX = 3 };
+
+// Roles of the short-side buffers DevMat::sq.
+enum SqRole : int {
+  SQ_A = 0,    // A_j, the Gram of the block's iterate, advanced in place
+  SQ_B,        // B'_j = a I + b A_j + c A_j^2 (j >= 1)
+  SQ_T,        // B'_j A_j
+  SQ_Q0,       // Q_j = B'_{j-1} ... B'_0, ping-pong (B'_0 itself is written here)
+  SQ_Q1,
+  SQ_COUNT
+};
+
+// Launch flags of GM_BX (in the roles word, bits 12 and 13): the last X' = Q X
+// of a pass writes only the orientation its reader uses; which one depends
+// on whether this is the matrix's last pass (the last Aurora pass, or the
+// only pass of a matrix without the preconditioner).
+constexpr int NS_LAST_BX = 1 << 12;
+constexpr int NS_LAST_PASS = 1 << 13;
+inline constexpr int ns_roles(int rp, int rq, int rd) { return rp | (rq << 4) | (rd << 8); }
+
 struct DevMat {
   // caller buffers
   const void* g;  int64_t ld_g;  int32_t dt_g;   // grad or polar input
@@ -61,7 +89,7 @@ struct DevMat {
   int32_t square;
   int32_t aurora;   // diagonal preconditioner (on the long side unless eq_short)
   int32_t eq_short; // aurora on a wide matrix's own rows (the short side)
-  int32_t ns_t;     // DT_F32 or DT_BF16: type of xn, x, xt, a, b
+  int32_t ns_t;     // DT_F32 or DT_BF16: type of xn, x, xt, sq
   int32_t n_rt, n_ct;   // ceil(rows / kStreamRows), ceil(cols / kStreamCols)
   int32_t n_seg;        // ceil(cols / kSegCols): streaming tiles are n_rt x n_seg
   int32_t n_rmv;        // partial w rows of the power step: ceil(rows / kRmvRows), fused: ceil(rows / kFusedPart)
@@ -70,8 +98,9 @@ struct DevMat {
   void* xn;
   void* x[2];
   void* xt[2];
-  void* a;
-  void* b;
+  void* sq[SQ_COUNT];   // short-side matrices by role (a matrix with one-iteration blocks aliases SQ_Q0 to SQ_B
+                        // and leaves SQ_T, SQ_Q1 unused)
+  int32_t fin;          // x[fin] / xt[fin] holds the result of the last pass (blocks per pass, mod 2)
   float* rowpart;   // rows x n_seg   : row sums of squares per tile segment
   float* colpart;   // n_rt x cols    : column sums of squares per row tile
   float* rowsq;     // rows
@@ -104,6 +133,6 @@ struct LaunchList {
   const int32_t* mat;   // n
 };
 
-enum GemmMode : int { GM_GRAM = 0, GM_SQ = 1, GM_BX = 2 };
+
 
 }  // namespace muon

@@ -1,17 +1,22 @@
 // Newton-Schulz matrix-core engine for gfx950.
 //
-// One iteration of the quintic Newton-Schulz map (Aurora record page,
-// www.xxmr.cn/news/295280, section 源码实现: X <- a X + (b A + c A^2) X with
-// A = X X^T, X normalised first) is three products, each a launch over every
-// matrix of a batch:
+// The quintic Newton-Schulz map (Aurora record page, www.xxmr.cn/news/295280,
+// section 源码实现: X <- a X + (b A + c A^2) X with A = X X^T, X normalised
+// first) runs as products, each a launch over every matrix of a batch:
 //   GM_GRAM  A  = X X^T                  (s x s, K = L)  upper tiles only, mirrored
 //   GM_SQ    B' = b A + c A A^T + a I     (s x s, K = s)  upper tiles only, mirrored
-//   GM_BX    X' = B' X                   (s x L, K = s)  writes X' and X'^T
-// (B' X equals a X + (b A + c A^2) X; adding a on the diagonal of B in the
-// second product's epilogue turns the third into a plain product.) X^T is
-// kept beside X, written by the third product's epilogue, so all three read
-// both operands with the reduction index contiguous:
-// C[m][n] = sum_k P[m][k] Q[n][k].
+//   GM_SYM   C  = P Q (symmetric P, Q)   (s x s, K = s)  upper tiles only, mirrored
+//   GM_BX    X' = P X                    (s x L, K = s)  writes X' and X'^T
+// One iteration is GRAM, SQ, then BX with P = B' (B' X equals a X + (b A +
+// c A^2) X; adding a on the diagonal of B in the second product's epilogue
+// turns the third into a plain product). A block of r iterations of a
+// rectangular matrix stays on the short side until its last step: every A_j
+// and B'_j is a polynomial in A_0, so they commute, A_{j+1} = B'_j A_j B'_j
+// (two GM_SYM products) and X_{j+r} = Q X_j with Q = B'_{r-1} ... B'_0 (GM_SYM
+// products, then one GM_BX), which needs 3 s^2 L + (4 r - 3) s^3 flops
+// instead of r (3 s^2 L + s^3). X^T is kept beside X, written by the BX
+// epilogue, so every product reads both operands with the reduction index
+// contiguous: C[m][n] = sum_k P[m][k] Q[n][k].
 //
 // Tiling: 256 x 256 output tile per workgroup. Default layout: 8 waves in
 // 4 x 2, each wave 64 x 128 (2 x 4 MFMA 32x32 blocks, accumulators in
@@ -117,6 +122,12 @@ template <> struct Elem<__bf16> {
     for (int e = 0; e < 8; ++e) q[e] = f2bf(v[e]);
     *(u16x8_t*)((unsigned short*)p + i) = q;
   }
+  // elements e in [lo, hi) of the 8 only
+  __device__ static void st8_part(void* p, size_t i, const float v[8], int lo, int hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e >= lo && e < hi) ((unsigned short*)p)[i + e] = f2bf(v[e]);
+  }
 };
 template <> struct Elem<float> {
   static constexpr int kPerChunk = 4;
@@ -138,7 +149,13 @@ template <> struct Elem<float> {
     *(f32x4_t*)((float*)p + i) = (f32x4_t){v[0], v[1], v[2], v[3]};
     *(f32x4_t*)((float*)p + i + 4) = (f32x4_t){v[4], v[5], v[6], v[7]};
   }
+  __device__ static void st8_part(void* p, size_t i, const float v[8], int lo, int hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e >= lo && e < hi) ((float*)p)[i + e] = v[e];
+  }
 };
+
 
 }  // namespace
 
@@ -147,10 +164,14 @@ template <> struct Elem<float> {
 // b % 8. Items are dealt to XCDs in runs of `group` consecutive items (one
 // super-tile of the planner's raster, whose tiles share operand panels), so a
 // run executes together on one XCD and reuses its L2.
+// roles: the roles in DevMat::sq of operand P (bits 0-3), operand Q (bits
+// 4-7) and the output (bits 8-11); GM_BX only: bit 12 = the last product of a pass,
+// bit 13 = that pass is the last Aurora pass (NS_LAST_BX, NS_LAST_PASS).
 template <typename T, int mode, int S, int WM, int WN, int TILE>
 __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(const DevMat* __restrict__ mats,
                                                              const TileItem* __restrict__ items, int n_items,
-                                                             int group, int cur, float ca, float cb, float cc) {
+                                                             int group, int cur, int roles, float ca, float cb,
+                                                             float cc) {
   constexpr int NW = WM * WN;                // waves per workgroup
   constexpr int MI = TILE / WM / 32;         // 32x32 blocks per wave, down
   constexpr int NI = TILE / WN / 32;         // 32x32 blocks per wave, across
@@ -174,6 +195,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   const int wm = wave / WN, wn = wave % WN;
   const int sp = M.s_pad, Lp = M.L_pad;
 
+  const int role_p = roles & 15, role_q = (roles >> 4) & 15, role_o = (roles >> 8) & 15, last = (roles >> 12) & 3;
   const T *P, *Q;
   int ld, K;
   if constexpr (mode == GM_GRAM) {
@@ -182,12 +204,16 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     Q = x + (size_t)it.tn * TILE * Lp;
     ld = Lp; K = Lp;
   } else if constexpr (mode == GM_SQ) {
-    const T* a = (const T*)M.a;
+    const T* a = (const T*)M.sq[role_p];
     P = a + (size_t)it.tm * TILE * sp;
     Q = a + (size_t)it.tn * TILE * sp;
     ld = sp; K = sp;
+  } else if constexpr (mode == GM_SYM) {
+    P = (const T*)M.sq[role_p] + (size_t)it.tm * TILE * sp;
+    Q = (const T*)M.sq[role_q] + (size_t)it.tn * TILE * sp;
+    ld = sp; K = sp;
   } else {
-    P = (const T*)M.b + (size_t)it.tm * TILE * sp;
+    P = (const T*)M.sq[role_p] + (size_t)it.tm * TILE * sp;
     Q = (const T*)M.xt[cur] + (size_t)it.tn * TILE * sp;
     ld = sp; K = sp;
   }
@@ -218,7 +244,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // count, and with it every wait, stays the same); both operands' fragments
   // are read from the first panel's slot.
   const int ext = (int)((int64_t)TILE * ld * sizeof(T));
-  const bool same = (mode != GM_BX) && (it.tm == it.tn);
+  const bool same = (mode == GM_GRAM || mode == GM_SQ) && (it.tm == it.tn);
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void*)P, (short)0, ext, 0x00020000);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Q, (short)0, same ? 0 : ext, 0x00020000);
 
@@ -354,14 +380,29 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   void* out;
   void* outT;
   int ldo, ldt;
-  if constexpr (mode == GM_GRAM) {
-    out = M.a; outT = M.a; ldo = sp; ldt = sp;
-  } else if constexpr (mode == GM_SQ) {
-    out = M.b; outT = M.b; ldo = sp; ldt = sp;
-  } else {
+  bool write_o = true, write_t;
+  if constexpr (mode == GM_BX) {
     out = M.x[cur ^ 1]; outT = M.xt[cur ^ 1]; ldo = Lp; ldt = sp;
+    // the last product of a pass writes only the orientation read next: the
+    // D update reads the long-side lines (rows of X'^T; rows of X' when the
+    // wide matrix is equilibrated on its rows), the tail reads the storage
+    // orientation (X'^T for a tall matrix, X' otherwise)
+    write_t = true;
+    if (last & 1) {
+      if ((last & 2) || !M.aurora) { write_t = M.tall != 0; write_o = !write_t; }   // this matrix's last pass
+      else { write_o = M.eq_short != 0; write_t = !write_o; }
+    }
+  } else {
+    out = M.sq[role_o]; outT = out; ldo = sp; ldt = sp;
+    write_t = it.tm != it.tn;
   }
-  const bool write_t = (mode == GM_BX) || (it.tm != it.tn);
+  // A GM_SYM result is symmetric only in exact arithmetic (C[m][n] and C[n][m]
+  // come from different products), so its diagonal tiles keep the upper
+  // triangle and write the lower one as its mirror: the stored matrix is then
+  // the mirrored upper triangle whatever the tile size, as for off-diagonal
+  // tiles.
+  const bool diag_sym = mode == GM_SYM && it.tm == it.tn;
+  if (diag_sym) write_t = true;
   __syncthreads();   // every wave is done with the slots
   if constexpr (sizeof(T) == 2 && mode != GM_SQ) {
     // bf16 outputs that are the accumulators rounded: each wave stages its
@@ -393,14 +434,24 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         }
     wave_lds_sync();
     // row-major: 8 consecutive columns of one row per lane
+    if (write_o) {
 #pragma unroll
-    for (int kk = 0; kk < TR * TC / 8 / 64; ++kk) {
-      const int q = kk * 64 + lane;
-      const int r = q / (TC / 8), c8 = (q % (TC / 8)) * 8;
-      u16x8_t v;
+      for (int kk = 0; kk < TR * TC / 8 / 64; ++kk) {
+        const int q = kk * 64 + lane;
+        const int r = q / (TC / 8), c8 = (q % (TC / 8)) * 8;
+        u16x8_t v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = st[sidx(r, c8 + e)];
-      *(u16x8_t*)((unsigned short*)out + (size_t)(row0 + r) * ldo + col0 + c8) = v;
+        for (int e = 0; e < 8; ++e) v[e] = st[sidx(r, c8 + e)];
+        unsigned short* dst = (unsigned short*)out + (size_t)(row0 + r) * ldo + col0 + c8;
+        const int d = (col0 + c8) - (row0 + r);   // element e is upper when d + e >= 0
+        if (!diag_sym || d >= 0) {
+          *(u16x8_t*)dst = v;
+        } else if (d > -8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (d + e >= 0) dst[e] = v[e];
+        }
+      }
     }
     if (write_t) {
       // transposed: 8 consecutive rows of one column per lane, a column's
@@ -410,7 +461,17 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         const int q = kk * 64 + lane;
         const int c = q / (TR / 8), r8 = (q % (TR / 8)) * 8;
         const u16x8_t v = *(const u16x8_t*)(st + sidx(r8, c));
-        *(u16x8_t*)((unsigned short*)outT + (size_t)(col0 + c) * ldt + row0 + r8) = v;
+        unsigned short* dst = (unsigned short*)outT + (size_t)(col0 + c) * ldt + row0 + r8;
+        // the mirror of source element (row0 + r8 + e, col0 + c): only from
+        // the strict upper triangle on a GM_SYM diagonal tile
+        const int d = (col0 + c) - (row0 + r8);   // element e qualifies when e < d
+        if (!diag_sym || d >= 8) {
+          *(u16x8_t*)dst = v;
+        } else if (d > 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < d) dst[e] = v[e];
+        }
       }
     }
     return;
@@ -428,7 +489,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
       for (int kk = 0; kk < KK; ++kk) {
         const int q = kk * 64 + lane;
         const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
-        araw[kk] = Elem<T>::ldraw(M.a, (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8);
+        araw[kk] = Elem<T>::ldraw(M.sq[role_p], (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8);
       }
     }
 #pragma unroll
@@ -454,7 +515,11 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = buf[rr * kPitch + c8 + e];
       }
-      Elem<T>::st8(out, idx, v);
+      if (write_o) {
+        const int d = (col0 + c8) - (row0 + mi * 32 + rr);   // upper when d + e >= 0
+        if (!diag_sym || d >= 0) Elem<T>::st8(out, idx, v);
+        else if (d > -8) Elem<T>::st8_part(out, idx, v, -d, 8);
+      }
       if (mode == GM_SQ && write_t) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) buf[rr * kPitch + c8 + e] = v[e];
@@ -469,7 +534,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = buf[(rc + e) * kPitch + c1];
-        Elem<T>::st8(outT, (size_t)(col0 + c1) * ldt + row0 + mi * 32 + rc, v);
+        const size_t tidx = (size_t)(col0 + c1) * ldt + row0 + mi * 32 + rc;
+        const int d = (col0 + c1) - (row0 + mi * 32 + rc);   // mirror of a strict-upper source when e < d
+        if (!diag_sym || d >= 8) Elem<T>::st8(outT, tidx, v);
+        else if (d > 0) Elem<T>::st8_part(outT, tidx, v, 0, d);
       }
     }
     wave_lds_sync();
@@ -486,7 +554,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
 // The third product always writes X'^T beside X' (the next iteration's
 // product, the preconditioner update and the output read it).
 hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, int n_items, int mode, int cur,
-                          float ca, float cb, float cc, int variant, int tile, hipStream_t st) {
+                          int roles, float ca, float cb, float cc, int variant, int tile, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
   if (tile != 256 && tile != 128) return hipErrorInvalidValue;
   const int group = 32;   // one super-tile of the planner's raster per XCD wave
@@ -494,12 +562,13 @@ hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, i
   const dim3 grid(per_xcd_groups * group * 8);
 #define NS_LAUNCH(T, MODE, WM, WN, TL)                                                                            \
   hipLaunchKernelGGL((k_ns_gemm<T, MODE, 5, WM, WN, TL>), grid, dim3(WM * WN * 64), 0, st, mats, items, n_items, \
-                     group, cur, ca, cb, cc)
-#define NS_MODES(T, WM, WN, TL)                             \
-  do {                                                      \
-    if (mode == GM_GRAM) NS_LAUNCH(T, GM_GRAM, WM, WN, TL); \
-    else if (mode == GM_SQ) NS_LAUNCH(T, GM_SQ, WM, WN, TL); \
-    else NS_LAUNCH(T, GM_BX, WM, WN, TL);                   \
+                     group, cur, roles, ca, cb, cc)
+#define NS_MODES(T, WM, WN, TL)                               \
+  do {                                                        \
+    if (mode == GM_GRAM) NS_LAUNCH(T, GM_GRAM, WM, WN, TL);   \
+    else if (mode == GM_SQ) NS_LAUNCH(T, GM_SQ, WM, WN, TL);  \
+    else if (mode == GM_SYM) NS_LAUNCH(T, GM_SYM, WM, WN, TL); \
+    else NS_LAUNCH(T, GM_BX, WM, WN, TL);                     \
   } while (0)
   if (ns_t == DT_BF16) {
     if (tile == 128) NS_MODES(__bf16, 2, 2, 128);

@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void k_prologue(const DevMat* __restrict__ mat
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mats, LaunchList L,
-                                                        int fin, float pp_eps, float pp_beta) {
+                                                        float pp_eps, float pp_beta) {
   __shared__ float red[4];
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
   const int len = M.eq_short ? M.L : M.s;     // entries per line
   float contrib = 0.f;
   if (l < nl) {
-    const void* ut = M.eq_short ? M.x[fin] : M.xt[fin];
+    const void* ut = M.eq_short ? M.x[M.fin] : M.xt[M.fin];
     const size_t row = (size_t)l * (M.eq_short ? M.L_pad : M.s_pad);
     float s = 0.f;
     // entries past len are zero padding (a line holds a multiple of 256)
@@ -963,9 +963,9 @@ __global__ __launch_bounds__(256) void k_power_sigma(DevMat* __restrict__ mats, 
 // wide/square (ld L_pad), xt[fin] for tall (ld s_pad). U rows are padded to
 // a multiple of 256 with zeros, so U chunks are always read whole.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ const void* u_ptr(const DevMat& M, int fin, int64_t* ld) {
-  if (M.tall) { *ld = M.s_pad; return M.xt[fin]; }
-  *ld = M.L_pad; return M.x[fin];
+__device__ __forceinline__ const void* u_ptr(const DevMat& M, int64_t* ld) {
+  if (M.tall) { *ld = M.s_pad; return M.xt[M.fin]; }
+  *ld = M.L_pad; return M.x[M.fin];
 }
 
 // The U, X and W rows r..r+R-1 at column c: vector loads of all three
@@ -1014,7 +1014,7 @@ __device__ __forceinline__ void tail_load_part(const DevMat& M, const void* U, i
 
 // Partial sums per streaming tile: ||U||^2, ||U - kappa X||^2, ||W||^2.
 template <typename T, typename TW>
-__device__ __forceinline__ void tail_reduce_body(const DevMat& M, int local, int fin, float (*red)[4]) {
+__device__ __forceinline__ void tail_reduce_body(const DevMat& M, int local, float (*red)[4]) {
   constexpr int R = kWaveRows;
   const int tr = local / M.n_seg, sg = local % M.n_seg;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1022,7 +1022,7 @@ __device__ __forceinline__ void tail_reduce_body(const DevMat& M, int local, int
   const int r = tr * kStreamRows + w * R;
   const int nr = max(0, min(R, M.rows - r));
   int64_t ldu;
-  const void* U = u_ptr(M, fin, &ldu);
+  const void* U = u_ptr(M, &ldu);
   const float kappa = M.scal[SC_KAPPA];
   const bool use_x = kappa != 0.f, has_w = M.w != nullptr;
   const int nv = max(0, min(8, M.cols - c));
@@ -1085,11 +1085,11 @@ __device__ __forceinline__ void tail_reduce_body(const DevMat& M, int local, int
     }                                                                               \
   } while (0)
 
-__global__ __launch_bounds__(256) void k_tail_reduce(const DevMat* __restrict__ mats, LaunchList L, int fin) {
+__global__ __launch_bounds__(256) void k_tail_reduce(const DevMat* __restrict__ mats, LaunchList L) {
   __shared__ float red[3][4];
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  TAIL_DISPATCH(tail_reduce_body, M, local, fin, red);
+  TAIL_DISPATCH(tail_reduce_body, M, local, red);
 }
 
 // alpha = ||U|| / max(||U - kappa X||, 1e-10) * sqrt(max(1, rows/cols)),
@@ -1127,7 +1127,7 @@ __global__ __launch_bounds__(256) void k_tail_finalize(DevMat* __restrict__ mats
 // V = alpha (U - kappa X); update_out <- V; W <- W - lr V.
 // copy_only: V = U (the polar entry points' output copy).
 template <typename T, typename TW>
-__device__ __forceinline__ void tail_apply_body(const DevMat& M, int local, int fin, float lr, int copy_only) {
+__device__ __forceinline__ void tail_apply_body(const DevMat& M, int local, float lr, int copy_only) {
   constexpr int R = kWaveRows;
   const int tr = local / M.n_seg, sg = local % M.n_seg;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1136,7 +1136,7 @@ __device__ __forceinline__ void tail_apply_body(const DevMat& M, int local, int 
   const int nr = max(0, min(R, M.rows - r));
   if (c >= M.cols || nr == 0) return;
   int64_t ldu;
-  const void* U = u_ptr(M, fin, &ldu);
+  const void* U = u_ptr(M, &ldu);
   const float kappa = copy_only ? 0.f : M.scal[SC_KAPPA];
   const float alpha = copy_only ? 1.f : M.scal[SC_ALPHA];
   const bool use_x = kappa != 0.f, has_w = M.w != nullptr, has_o = M.uo != nullptr;
@@ -1182,11 +1182,11 @@ __device__ __forceinline__ void tail_apply_body(const DevMat& M, int local, int 
   }
 }
 
-__global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ mats, LaunchList L, int fin,
-                                                    float lr, int copy_only) {
+__global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ mats, LaunchList L, float lr,
+                                                    int copy_only) {
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  TAIL_DISPATCH(tail_apply_body, M, local, fin, lr, copy_only);
+  TAIL_DISPATCH(tail_apply_body, M, local, lr, copy_only);
 }
 
 // ---------------------------------------------------------------------------
@@ -1215,10 +1215,10 @@ hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, in
   else LAUNCH(k_prologue<float>, nblk, m, L, use_xn);
   return hipGetLastError();
 }
-hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, int fin, float pp_eps,
-                                 float pp_beta, hipStream_t st) {
-  if (ns_t == DT_BF16) LAUNCH(k_aurora_dupdate<__bf16>, nblk, m, L, fin, pp_eps, pp_beta);
-  else LAUNCH(k_aurora_dupdate<float>, nblk, m, L, fin, pp_eps, pp_beta);
+hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, float pp_eps, float pp_beta,
+                                 hipStream_t st) {
+  if (ns_t == DT_BF16) LAUNCH(k_aurora_dupdate<__bf16>, nblk, m, L, pp_eps, pp_beta);
+  else LAUNCH(k_aurora_dupdate<float>, nblk, m, L, pp_eps, pp_beta);
   return hipGetLastError();
 }
 hipError_t launch_aurora_scale(DevMat* m, LaunchList L, int nblk, float ns_eps, hipStream_t st) {
@@ -1254,17 +1254,16 @@ hipError_t launch_power_sigma(DevMat* m, LaunchList L, int nblk, float contra, h
   LAUNCH(k_power_sigma, nblk, m, L, contra);
   return hipGetLastError();
 }
-hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, int fin, hipStream_t st) {
-  LAUNCH(k_tail_reduce, nblk, m, L, fin);
+hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, hipStream_t st) {
+  LAUNCH(k_tail_reduce, nblk, m, L);
   return hipGetLastError();
 }
 hipError_t launch_tail_finalize(DevMat* m, LaunchList L, int nblk, float target_uw, hipStream_t st) {
   LAUNCH(k_tail_finalize, nblk, m, L, target_uw);
   return hipGetLastError();
 }
-hipError_t launch_tail_apply(const DevMat* m, LaunchList L, int nblk, int fin, float lr, int copy_only,
-                             hipStream_t st) {
-  LAUNCH(k_tail_apply, nblk, m, L, fin, lr, copy_only);
+hipError_t launch_tail_apply(const DevMat* m, LaunchList L, int nblk, float lr, int copy_only, hipStream_t st) {
+  LAUNCH(k_tail_apply, nblk, m, L, lr, copy_only);
   return hipGetLastError();
 }
 
