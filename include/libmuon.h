@@ -59,7 +59,8 @@ typedef enum {
   MUON_ERR_SHAPE_MISMATCH = -3,   /* grad/momentum/weight/out shapes differ, ld < cols, limits */
   MUON_ERR_ALLOC = -4,            /* device workspace allocation failed */
   MUON_ERR_HIP = -5,              /* a HIP runtime call failed */
-  MUON_ERR_NO_DEVICE = -6         /* no usable gfx950 device */
+  MUON_ERR_NO_DEVICE = -6,        /* no usable gfx950 device */
+  MUON_ERR_TOO_LARGE = -7         /* muon_update_static: the batch does not fit the static scratch */
 } muon_status_code;
 typedef int muon_status;
 
@@ -296,6 +297,29 @@ muon_status aurora_orthogonalize(muon_handle* handle, int n,
 muon_status muon_update(muon_handle* handle, int n, const muon_matrix* grad,
                         const muon_matrix* momentum, const muon_matrix* weight,
                         const muon_matrix* update_out, const muon_config* cfg);
+
+/*
+ * muon_update_static — muon_update for callers that cannot allocate device
+ * memory during the call: code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid allocation. Same arguments, rules,
+ * validation, kernels and results as muon_update (bitwise), but the call
+ * allocates nothing: its workspace and launch tables live in a file-scope
+ * device array of 64 MiB per device (held until the process ends; its
+ * address is taken once per device by muon_create, and a pinned 1 MiB table
+ * stage is allocated there too), and no profiling events are recorded.
+ *   Limit: the batch's workspace plus its launch tables must fit the 64 MiB
+ *   (for example one 1024 x 3072 bf16 matrix, or a few 768 x 768 ones, with
+ *   tables within 1 MiB); larger batches return MUON_ERR_TOO_LARGE with a
+ *   message giving the bytes needed, before anything is enqueued.
+ *   Sharing: every static call on a device uses that device's one array and
+ *   leaves its contents there (nothing in it needs clearing: every call
+ *   writes each part before reading it). Static calls that can overlap on
+ *   one device (other handles, other streams) race: order them, e.g. on one
+ *   stream.
+ */
+muon_status muon_update_static(muon_handle* handle, int n, const muon_matrix* grad,
+                               const muon_matrix* momentum, const muon_matrix* weight,
+                               const muon_matrix* update_out, const muon_config* cfg);
 
 /*
  * Profiling of the library's own launches (for roofline reporting): when

@@ -26,7 +26,7 @@ __all__ = [
     "MuonConfig", "MuonProfile", "LibMuonError", "Handle", "load_library",
     "library_path", "default_config", "classic_config", "momentum_warmup", "make_config", "ns_polar",
     "aurora_orthogonalize", "muon_update", "check_update_args",
-    "check_polar_args", "get_handle", "STATUS", "MUON_FLAG_SGD_MOMENTUM", "MUON_FLAG_WIDE_ROWS",
+    "check_polar_args", "get_handle", "STATUS", "muon_update_static", "MUON_FLAG_SGD_MOMENTUM", "MUON_FLAG_WIDE_ROWS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +39,7 @@ MUON_FLAG_WIDE_ROWS = 0x2       # Aurora on a wide matrix's own rows
 STATUS = {
     0: "MUON_OK", -1: "MUON_ERR_INVALID_ARG", -2: "MUON_ERR_UNSUPPORTED_DTYPE",
     -3: "MUON_ERR_SHAPE_MISMATCH", -4: "MUON_ERR_ALLOC", -5: "MUON_ERR_HIP",
-    -6: "MUON_ERR_NO_DEVICE",
+    -6: "MUON_ERR_NO_DEVICE", -7: "MUON_ERR_TOO_LARGE",
 }
 
 
@@ -126,6 +126,9 @@ def load_library() -> ctypes.CDLL:
             "muon_update": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, P(MuonMatrix),
                                            P(MuonMatrix), P(MuonMatrix), P(MuonMatrix),
                                            P(MuonConfig)]),
+            "muon_update_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, P(MuonMatrix),
+                                                  P(MuonMatrix), P(MuonMatrix), P(MuonMatrix),
+                                                  P(MuonConfig)]),
             "muon_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
             "muon_profile_reset": (ctypes.c_int, [ctypes.c_void_p]),
             "muon_profile_read": (ctypes.c_int, [ctypes.c_void_p, P(MuonProfile)]),
@@ -351,6 +354,17 @@ def _update(name, grads, momenta, weights, cfg, update_out, handle):
     u = _array([_desc(t, "update_out") for t in update_out]) if update_out is not None else None
     fn = getattr(h._lib, name)
     h._check(fn(h.ptr, n, g, m, w, u, ctypes.byref(cfg) if cfg is not None else None))
+
+
+def muon_update_static(grads: Sequence[torch.Tensor], momenta: Sequence[torch.Tensor],
+                       weights: Sequence[torch.Tensor | None] | None = None,
+                       cfg: MuonConfig | None = None,
+                       update_out: Sequence[torch.Tensor | None] | None = None,
+                       handle: Handle | None = None) -> None:
+    """`muon_update` through libmuon's `muon_update_static`: the call itself
+    allocates no device memory (its workspace is the library's static
+    per-device scratch, 64 MiB), for batches that fit it."""
+    _update("muon_update_static", grads, momenta, weights, cfg, update_out, handle)
 
 
 def check_update_args(grads, momenta, weights=None, update_out=None, cfg=None) -> tuple[int, str]:

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmuon.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["ns_gemm.hip", "stream_kernels.hip"]
+DEVICE_SOURCES = ["ns_gemm.hip", "stream_kernels.hip", "static_scratch.hip"]
 HOST_SOURCES = ["api.cpp", "validate.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

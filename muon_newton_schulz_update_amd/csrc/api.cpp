@@ -56,6 +56,12 @@ hipError_t launch_power_sigma(DevMat* m, LaunchList L, int nblk, float contra, h
 hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, hipStream_t st);
 hipError_t launch_tail_finalize(DevMat* m, LaunchList L, int nblk, float target_uw, hipStream_t st);
 hipError_t launch_tail_apply(const DevMat* m, LaunchList L, int nblk, float lr, int copy_only, hipStream_t st);
+size_t static_scratch_bytes();
+hipError_t static_scratch_address(int dev, void** out);
+
+// Pinned staging for the launch tables of muon_update_static, allocated with
+// the handle: the largest table set a static call may upload.
+constexpr size_t kStaticStageBytes = size_t(1) << 20;
 
 namespace {
 
@@ -215,6 +221,12 @@ struct muon_handle {
   size_t pinned_bytes = 0;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
+  // muon_update_static: the device's static scratch and the handle's table staging
+  void* scratch = nullptr;
+  void* static_stage = nullptr;
+  hipEvent_t static_done = nullptr;
+  bool static_pending = false;
+  bool in_static = false;    // inside muon_update_static: no profiling events
   std::string err;
   // profiling
   bool prof = false;
@@ -580,7 +592,7 @@ struct ProfScope {
   ProfRec r{};
   bool on;
   ProfScope(muon_handle* hh, int cls, double amount, double amount2 = 0, double amount3 = 0)
-      : h(hh), on(hh->prof) {
+      : h(hh), on(hh->prof && !hh->in_static) {
     if (!on) return;
     r.cls = cls;
     r.amount = amount;
@@ -644,7 +656,9 @@ struct Call {
     if (e_ != hipSuccess) return set_err((h), MUON_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(e_)); \
   } while (0)
 
-muon_status run(muon_handle* h, const Call& c) {
+// use_static: the workspace and the launch tables go to the device's static
+// scratch (muon_update_static): no allocation, no profiling events.
+muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   const muon_config& cfg = c.cfg;
   const int pp = c.kind == KIND_NS ? 0 : cfg.pp_iterations;
   const bool wide_rows = (cfg.flags & MUON_FLAG_WIDE_ROWS) != 0;
@@ -671,12 +685,28 @@ muon_status run(muon_handle* h, const Call& c) {
   }
   P->last_use = ++h->tick;
   if (P->mats.empty()) return MUON_OK;
-  muon_status rc = ensure_workspace(h, P->ws_bytes);
-  if (rc) return rc;
-  rc = ensure_meta(h, *P);
-  if (rc) return rc;
-  uint8_t* ws = (uint8_t*)h->ws;
-  uint8_t* meta = (uint8_t*)P->meta_dev;
+  muon_status rc = MUON_OK;
+  uint8_t* ws;
+  uint8_t* meta;
+  if (use_static) {
+    const size_t meta_off = align_up(P->ws_bytes);
+    const size_t need = meta_off + P->meta_host.size();
+    if (need > static_scratch_bytes() || P->meta_host.size() > kStaticStageBytes)
+      return set_err(h, MUON_ERR_TOO_LARGE,
+                     "muon_update_static: the batch needs " + std::to_string(need) + " bytes of device scratch (" +
+                         std::to_string(P->meta_host.size()) + " of launch tables); the static scratch holds " +
+                         std::to_string(static_scratch_bytes()) + " bytes and " + std::to_string(kStaticStageBytes) +
+                         " of tables");
+    ws = (uint8_t*)h->scratch;
+    meta = ws + meta_off;
+  } else {
+    rc = ensure_workspace(h, P->ws_bytes);
+    if (rc) return rc;
+    rc = ensure_meta(h, *P);
+    if (rc) return rc;
+    ws = (uint8_t*)h->ws;
+    meta = (uint8_t*)P->meta_dev;
+  }
 
   // descriptors
   std::vector<DevMat> dm(P->mats.size());
@@ -712,8 +742,23 @@ muon_status run(muon_handle* h, const Call& c) {
     d.linepart = (float*)(ws + m.o_linepart);
     d.scal = (float*)(ws + m.o_scal); d.ist = (int32_t*)(ws + m.o_ist);
   }
-  rc = upload_devmat(h, *P, dm);
-  if (rc) return rc;
+  if (use_static) {
+    // the whole table set (descriptors, then the lists) through the pinned
+    // stage; the previous static upload from it must have been read
+    if (h->static_pending) {
+      HIP_TRY(h, hipEventSynchronize(h->static_done));
+      h->static_pending = false;
+    }
+    uint8_t* stage = (uint8_t*)h->static_stage;
+    memcpy(stage, P->meta_host.data(), P->meta_host.size());
+    memcpy(stage, dm.data(), dm.size() * sizeof(DevMat));
+    HIP_TRY(h, hipMemcpyAsync(meta, stage, P->meta_host.size(), hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipEventRecord(h->static_done, h->stream));
+    h->static_pending = true;
+  } else {
+    rc = upload_devmat(h, *P, dm);
+    if (rc) return rc;
+  }
 
   DevMat* D = (DevMat*)meta;
   hipStream_t st = h->stream;
@@ -865,7 +910,7 @@ muon_status run(muon_handle* h, const Call& c) {
     ProfScope ps(h, 1, b_tail_a);
     CHECK_LAUNCH(h, launch_tail_apply(D, dev_list(meta, P->stream), P->stream.nblk, 0.f, 1, st));
   }
-  if (h->prof && h->recs.size() > 200000) return drain_profile(h);
+  if (!use_static && h->prof && h->recs.size() > 200000) return drain_profile(h);
   return MUON_OK;
 }
 
@@ -898,6 +943,20 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
     delete h;
     return MUON_ERR_HIP;
   }
+  // set-up of muon_update_static: the device address of this device's static
+  // scratch (looked up once per device), the table staging and its event
+  if (static_scratch_address(dev, &h->scratch) != hipSuccess ||
+      hipEventCreateWithFlags(&h->static_done, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    muon_destroy(h);
+    return MUON_ERR_HIP;
+  }
+  if (hipHostMalloc(&h->static_stage, kStaticStageBytes, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    h->static_stage = nullptr;
+    muon_destroy(h);
+    return MUON_ERR_ALLOC;
+  }
   *out = h;
   return MUON_OK;
 }
@@ -910,6 +969,8 @@ extern "C" muon_status muon_destroy(muon_handle* h) {
   if (h->ws) (void)hipFree(h->ws);
   if (h->pinned) (void)hipHostFree(h->pinned);
   if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+  if (h->static_done) (void)hipEventDestroy(h->static_done);
+  if (h->static_stage) (void)hipHostFree(h->static_stage);
   for (auto& r : h->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (auto e : h->ev_pool) (void)hipEventDestroy(e);
   delete h;
@@ -979,6 +1040,22 @@ extern "C" muon_status muon_update(muon_handle* h, int n, const muon_matrix* gra
   h->err.clear();
   Call c{KIND_UPDATE, n, grad, momentum, weight, update_out, resolve_cfg(cfg)};
   return run(h, c);
+}
+
+extern "C" muon_status muon_update_static(muon_handle* h, int n, const muon_matrix* grad,
+                                          const muon_matrix* momentum, const muon_matrix* weight,
+                                          const muon_matrix* update_out, const muon_config* cfg) {
+  if (!h) return MUON_ERR_INVALID_ARG;
+  char msg[256];
+  const int rc = check_update(n, grad, momentum, weight, update_out, cfg, msg, sizeof(msg));
+  if (rc) return set_err(h, rc, msg);
+  h->err.clear();
+  if (!h->scratch || !h->static_stage) return set_err(h, MUON_ERR_HIP, "static scratch not set up");
+  Call c{KIND_UPDATE, n, grad, momentum, weight, update_out, resolve_cfg(cfg)};
+  h->in_static = true;
+  const muon_status r = run(h, c, true);
+  h->in_static = false;
+  return r;
 }
 
 extern "C" muon_status muon_profile_enable(muon_handle* h, int enable) {
