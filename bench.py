@@ -351,7 +351,7 @@ def main() -> int:
             "frac": round(achieved / peak, 4),
             # the byte-counter record was taken on the Aurora step's launches
             "traffic": measured_traffic(a.workload) if a.recipe == "aurora" else None,
-            "kernel": "k_ns_gemm (A = XX^T, B' = bA + cA^2 + aI, X' = B'X launches together)",
+            "kernel": "k_ns_gemm (A = XX^T, B' = bA + cA^2 + aI, short-side products, X' = QX launches together)",
             "flops": "algorithmic flops of the products run: symmetric halves once, no padding",
             "algorithmic_tflop_per_step": round(p["gemm_algorithmic_flop"] / a.steps / 1e12, 3),
             "standard_iteration_tflops": round(standard, 2),
