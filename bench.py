@@ -240,6 +240,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-launch event timing")
     ap.add_argument("--no-clocks", action="store_true", help="do not sample GPU clocks with the SMI tool")
+    ap.add_argument("--fp8-gram", action="store_true",
+                    help="research option, not the headline: the first Gram of each pass on fp8 operands "
+                         "(MUON_FLAG_FP8_GRAM); the line's dtype says so")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -261,6 +264,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     w = gen.WORKLOADS[a.workload]
     cfg = mu.make_config(a.recipe, **dict(w.config))
+    if a.fp8_gram:
+        cfg.flags |= mu.MUON_FLAG_FP8_GRAM
     log(f"[bench] generating {a.workload}: {len(w.shapes)} matrices")
     grads, moms, weights = gen.make_batch(a.workload, dev)
     torch.cuda.synchronize()
@@ -327,7 +332,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.grad_dtype == torch.bfloat16 else "f32",
+        "dtype": ("bf16" if w.grad_dtype == torch.bfloat16 else "f32") + ("+fp8 first Gram" if a.fp8_gram else ""),
         "data": "synthetic",
         "config": {"workload": a.workload, "recipe": a.recipe, "matrices": len(shapes), "matrix_params": params,
                    "counted_ns_tflop_per_step": round(flops / 1e12, 3),

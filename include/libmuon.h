@@ -130,10 +130,24 @@ typedef struct {
  * matrices are unaffected. Since such a polar factor's rows are already
  * orthonormal, later passes move D only where Newton-Schulz has not
  * converged; pp_iterations 1 is row-normalise-then-polar on the rows.
+ *
+ * MUON_FLAG_FP8_GRAM — lower-precision Newton-Schulz, a research option (not
+ * from the pages, which run the optimizer's products in their training
+ * precision; the 3.8B page uses FP8 only for the model's GEMMs, in its
+ * post-mortem). For bf16 matrices that run Newton-Schulz in blocks
+ * (rectangular, short side >= 512), the first Gram of each pass, A = X0 X0^T
+ * with K = the long side, reads an fp8 (OCP e4m3) copy of X0 written by the
+ * pass prologue with a per-matrix power-of-two scale q (q |X0| <= 448,
+ * bounded by the largest equilibrated line or row norm), runs on the fp8
+ * matrix cores and divides by q^2 in its epilogue. The sums over the long
+ * side average the operands' rounding: measured error stays at the bf16
+ * path's level (about 5e-3 relative Frobenius). Later Grams, the short-side
+ * products and X' = Q X stay bf16 (fp8 there costs 1e-2 to 5e-2).
  */
 #define MUON_FLAG_SGD_MOMENTUM 0x1u
 #define MUON_FLAG_WIDE_ROWS    0x2u
-#define MUON_FLAG_ALL          0x3u
+#define MUON_FLAG_FP8_GRAM     0x4u
+#define MUON_FLAG_ALL          0x7u
 
 /* Per-kernel-class timing gathered when profiling is on (see muon_profile_*). */
 typedef struct {

@@ -80,10 +80,11 @@ struct MatInfo {
   int user;                  // index in the caller's batch
   int rows, cols, s, L, s_pad, L_pad;
   bool tall, square, aurora, eq_short;
+  bool f8;                   // the first Gram of each pass on fp8 operands (MUON_FLAG_FP8_GRAM)
   int block;                 // Newton-Schulz iterations per block (1 for squares)
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv, wband;
-  size_t o_xn, o_x[2], o_xt[2], o_sq[SQ_COUNT], o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
+  size_t o_xn, o_x[2], o_xt[2], o_x8, o_sq[SQ_COUNT], o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
       o_pwpart, o_tailpart, o_linepart, o_scal, o_ist;
 };
 
@@ -178,6 +179,7 @@ struct Plan {
   HostList dupdate[2];      // [ns_t]
   GemmList gemm[2][2][2][3];   // [pass group][block class][ns_t][list]
   int block = kDefaultBlock;    // iterations per block of a rectangular matrix
+  bool fp8 = false;             // MUON_FLAG_FP8_GRAM: the class-1 bf16 matrices' first Gram is fp8
   // device meta: DevMat array followed by the list arrays
   std::vector<uint8_t> meta_host;  // list part (static)
   size_t meta_devmat_bytes = 0;
@@ -187,11 +189,12 @@ struct Plan {
   uint64_t last_use = 0;
 };
 
-std::string plan_key(int kind, int pp, bool wide_rows, int block, bool forced, int n, const muon_matrix* in) {
+std::string plan_key(int kind, int pp, bool wide_rows, bool fp8, int block, bool forced, int n,
+                     const muon_matrix* in) {
   std::string k;
   k.reserve(16 + n * 12);
-  char buf[64];
-  snprintf(buf, sizeof(buf), "%d/%d/%d/%d/%d/%d|", kind, pp, (int)wide_rows, block, (int)forced, n);
+  char buf[80];
+  snprintf(buf, sizeof(buf), "%d/%d/%d/%d/%d/%d/%d|", kind, pp, (int)wide_rows, (int)fp8, block, (int)forced, n);
   k += buf;
   for (int i = 0; i < n; ++i) {
     snprintf(buf, sizeof(buf), "%lld,%lld,%d;", (long long)in[i].rows, (long long)in[i].cols, (int)in[i].dtype);
@@ -280,11 +283,12 @@ void add_gemm(std::vector<uint8_t>& meta, GemmList& G, std::vector<TileItem>& it
 // and the inputs' shapes and element types (exactly what plan_key holds):
 // caller pointers, strides, weights and outputs go into the per-call
 // descriptors.
-std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int block, bool forced, int n,
+std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int block, bool forced, int n,
                                  const muon_matrix* in) {
   auto P = std::make_unique<Plan>();
   P->kind = kind;
   P->block = block;
+  P->fp8 = fp8;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -314,11 +318,15 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int block, bo
     const size_t e = esz(m.ns_t);
     const size_t nsl = (size_t)m.s_pad * m.L_pad * e;
     m.o_xn = kind == KIND_UPDATE ? take((size_t)m.rows * m.cols * e) : 0;
+    m.block = m.square || (!forced && m.s < kBlockMinShort) ? 1 : P->block;
+    // fp8 first Gram: bf16 matrices that run blocks (their first Gram is the
+    // long K = L product whose sums average the operands' rounding)
+    m.f8 = fp8 && m.ns_t == DT_BF16 && m.block > 1;
+    m.o_x8 = m.f8 ? take((size_t)m.s_pad * m.L_pad) : 0;
     m.o_x[0] = take(nsl);
     m.o_x[1] = take(nsl);
     m.o_xt[0] = take(nsl);
     m.o_xt[1] = take(nsl);
-    m.block = m.square || (!forced && m.s < kBlockMinShort) ? 1 : P->block;
     const size_t ssq = (size_t)m.s_pad * m.s_pad * e;
     m.o_sq[SQ_A] = take(ssq);
     m.o_sq[SQ_B] = take(ssq);
@@ -341,8 +349,10 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, int block, bo
     m.o_pwpart = take(kind == KIND_UPDATE ? (size_t)cdiv(m.rows, fused_power(m) ? kFusedPart : kRmvRows) *
                                                 m.cols * 4
                                           : 4);
-    m.o_tailpart = take(std::max((size_t)m.n_rt * m.n_seg * 4, (size_t)cdiv(m.L, 4)) * 4);
-    m.o_linepart = take((size_t)2 * line_blocks(m.rows, m.cols) * 4);
+    // tail partials (4 per streaming tile); the D update's per-block sums and maxima
+    m.o_tailpart = take(std::max((size_t)m.n_rt * m.n_seg * 4, (size_t)2 * cdiv(m.L, 4)) * 4);
+    // per line block: row-sum total, (D rho)^2 total, largest line norm^2
+    m.o_linepart = take((size_t)3 * line_blocks(m.rows, m.cols) * 4);
     m.o_scal = take(SC_COUNT * 4);
     m.o_ist = take(IS_COUNT * 4);
     if (m.aurora) P->any_aurora = true;
@@ -662,9 +672,10 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   const muon_config& cfg = c.cfg;
   const int pp = c.kind == KIND_NS ? 0 : cfg.pp_iterations;
   const bool wide_rows = (cfg.flags & MUON_FLAG_WIDE_ROWS) != 0;
+  const bool fp8 = (cfg.flags & MUON_FLAG_FP8_GRAM) != 0;
   bool forced = false;
   const int block = rect_block(cfg, &forced);
-  const std::string key = plan_key(c.kind, pp, wide_rows, block, forced, c.n, c.in);
+  const std::string key = plan_key(c.kind, pp, wide_rows, fp8, block, forced, c.n, c.in);
   auto it = h->plans.find(key);
   Plan* P;
   if (it == h->plans.end()) {
@@ -677,7 +688,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
       if (victim->second->meta_dev) HIP_TRY(h, hipFree(victim->second->meta_dev));
       h->plans.erase(victim);
     }
-    auto p = build_plan(c.kind, pp, wide_rows, block, forced, c.n, c.in);
+    auto p = build_plan(c.kind, pp, wide_rows, fp8, block, forced, c.n, c.in);
     P = p.get();
     h->plans.emplace(key, std::move(p));
   } else {
@@ -733,6 +744,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     d.x[0] = ws + m.o_x[0]; d.x[1] = ws + m.o_x[1];
     d.xt[0] = ws + m.o_xt[0]; d.xt[1] = ws + m.o_xt[1];
     for (int r = 0; r < SQ_COUNT; ++r) d.sq[r] = ws + m.o_sq[r];
+    d.x8 = m.f8 ? ws + m.o_x8 : nullptr;
     d.fin = ((cfg.ns_steps + m.block - 1) / m.block) & 1;   // blocks per pass, mod 2
     d.rowpart = (float*)(ws + m.o_rowpart); d.colpart = (float*)(ws + m.o_colpart);
     d.rowsq = (float*)(ws + m.o_rowsq); d.colsq = (float*)(ws + m.o_colsq);
@@ -852,10 +864,13 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         const GemmList* GL = P->gemm[g][c][t];
         if (GL[LIST_GRAM].n == 0) continue;
         const int r = c == 0 ? 1 : P->block;
-        auto gemm = [&](int li, int mode, int cur, int roles, double counted) -> muon_status {
+        // the first Gram of the pass reads the prologue's fp8 copy of X0 when
+        // this class's matrices have one (all or none: bf16 with blocks)
+        const bool f8 = c == 1 && t == DT_BF16 && P->fp8;
+        auto gemm = [&](int li, int mode, int cur, int roles, double counted, int et) -> muon_status {
           const GemmList& G = GL[li];
           ProfScope ps(h, 0, counted, G.executed, G.algorithmic);
-          CHECK_LAUNCH(h, launch_ns_gemm(t, D, (const TileItem*)(meta + G.off), G.n, mode, cur,
+          CHECK_LAUNCH(h, launch_ns_gemm(et, D, (const TileItem*)(meta + G.off), G.n, mode, cur,
                                          roles, cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, G.tile, st));
           return MUON_OK;
         };
@@ -863,22 +878,22 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         for (int k = 0; k < cfg.ns_steps; cur ^= 1) {
           const int rr = std::min(r, cfg.ns_steps - k);
           k += rr;
-          muon_status e = gemm(LIST_GRAM, GM_GRAM, cur, ns_roles(0, 0, SQ_A), 0.0);
+          muon_status e = gemm(LIST_GRAM, GM_GRAM, cur, ns_roles(0, 0, SQ_A), 0.0, f8 && k == rr ? DT_F8 : t);
           for (int j = 0; !e && j < rr; ++j) {
             const int bj = j == 0 ? SQ_Q0 : SQ_B;   // B'_0 is Q_1 itself
-            e = gemm(LIST_SQ, GM_SQ, cur, ns_roles(SQ_A, SQ_A, bj), 0.0);
+            e = gemm(LIST_SQ, GM_SQ, cur, ns_roles(SQ_A, SQ_A, bj), 0.0, t);
             if (!e && j >= 1)
               e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(SQ_B, (j - 1) & 1 ? SQ_Q1 : SQ_Q0, j & 1 ? SQ_Q1 : SQ_Q0),
-                       0.0);
+                       0.0, t);
             if (!e && j + 1 < rr) {
-              e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_A, SQ_T), 0.0);
-              if (!e) e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_T, SQ_A), 0.0);
+              e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_A, SQ_T), 0.0, t);
+              if (!e) e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_T, SQ_A), 0.0, t);
             }
           }
           if (!e) {
             const int roles = ns_roles((rr - 1) & 1 ? SQ_Q1 : SQ_Q0, 0, 0) |
                               (k == cfg.ns_steps ? NS_LAST_BX | last_pass : 0);
-            e = gemm(LIST_BX, GM_BX, cur, roles, rr * GL[LIST_BX].counted_iter);
+            e = gemm(LIST_BX, GM_BX, cur, roles, rr * GL[LIST_BX].counted_iter, t);
           }
           if (e) return e;
         }
@@ -1003,7 +1018,7 @@ extern "C" muon_status muon_reserve(muon_handle* h, int n, const muon_matrix* sh
     muon_config dflt;
     muon_config_default(&dflt);
     const int block = rect_block(dflt, &forced);
-    auto P = build_plan(kind, 2, false, block, forced, n, shapes);
+    auto P = build_plan(kind, 2, false, false, block, forced, n, shapes);
     need = std::max(need, P->ws_bytes);
   }
   return ensure_workspace(h, need);

@@ -27,7 +27,8 @@ constexpr int kRmvRows = 256;     // rows per tile of the X^T u kernel (and the 
 constexpr int kFusedCols = 12288; // widest matrix the fused X^T X v pass takes (its v sits in LDS)
 constexpr int kFusedPart = 64;    // rows per partial w of the fused pass (fixed: results do not depend on batching)
 
-enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+// Element types; DT_F8 (OCP e4m3) only names the fp8 form of a Gram launch.
+enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F8 = 2 };
 
 // Per-matrix scalar slots (fp32) in DevMat::scal.
 enum Scalar : int {
@@ -40,6 +41,8 @@ enum Scalar : int {
   SC_KAPPA,        // (contra / 2) / max(sigma, 1e-7)
   SC_ALPHA,        // final scale of (U - kappa X)
   SC_PNORM,        // ||w|| of the last power step
+  SC_F8Q,          // power-of-two scale q of the pass's fp8 copy of X0 (|q X0| <= 448)
+  SC_F8INV2,       // 1 / q^2: undoes the scale in the fp8 Gram's epilogue
   SC_COUNT = 16
 };
 
@@ -98,6 +101,8 @@ struct DevMat {
   void* xn;
   void* x[2];
   void* xt[2];
+  void* x8;         // fp8 q X0 for the first Gram, or null: L_pad/64 panels of s_pad x 64 bytes (column c of
+                    // row r at ((c/64) s_pad + r) 64 + c%64), written by the pass prologue
   void* sq[SQ_COUNT];   // short-side matrices by role (a matrix with one-iteration blocks aliases SQ_Q0 to SQ_B
                         // and leaves SQ_T, SQ_Q1 unused)
   int32_t fin;          // x[fin] / xt[fin] holds the result of the last pass (blocks per pass, mod 2)
@@ -111,8 +116,9 @@ struct DevMat {
   float* pv;        // cols : v
   float* pwpart;    // n_rmv x cols : partial w per row band
   float* tailpart;  // n_rt * n_seg * 4 : partial tail sums per streaming tile
-  float* linepart;  // 2 * (ceil(rows/256) + (rows < cols ? ceil(cols/256) : 0)): per-block norm
-                    // partials of the line sums; reused for the blocks of ||w||^2
+  float* linepart;  // 3 * (ceil(rows/256) + (rows < cols ? ceil(cols/256) : 0)): per-block norm
+                    // partials of the line sums and the largest line norm^2; reused for the blocks
+                    // of ||w||^2
   float* scal;      // SC_COUNT
   int32_t* ist;     // IS_COUNT
 };

@@ -53,6 +53,13 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// fp8 (OCP e4m3) operand element: the type tag of the Gram's fp8 form.
+struct F8 {
+  uint8_t v;
+};
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -129,6 +136,10 @@ template <> struct Elem<__bf16> {
       if (e >= lo && e < hi) ((unsigned short*)p)[i + e] = f2bf(v[e]);
   }
 };
+template <> struct Elem<F8> {
+  static constexpr int kPerChunk = 16;         // fp8 per 16-byte chunk
+  typedef i32x8_t Frag;                        // 32 fp8 (two chunks) per lane per MFMA
+};
 template <> struct Elem<float> {
   static constexpr int kPerChunk = 4;
   typedef f32x4_t Frag;                        // four MFMA operands (4 consecutive k) per lane
@@ -177,8 +188,13 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   constexpr int NI = TILE / WN / 32;         // 32x32 blocks per wave, across
   constexpr int kOpBytes = TILE * kRowBytes; // one operand of one stage (one LDS slot)
   constexpr int LPO = TILE / 8 / NW;         // direct loads per wave per operand per stage
-  constexpr int kMfmaStep = MI * NI * (sizeof(T) == 2 ? 1 : 4);   // MFMAs per k-step
-  constexpr int kReadStep = MI + NI;                              // LDS reads per k-step
+  constexpr bool kF8 = sizeof(T) == 1;       // fp8 operands (GM_GRAM only), bf16 output
+  // k-steps per stage: 16 bf16, 4 fp32 (four 32x32x2 MFMAs) or 64 fp8 of K per
+  // lane pair, so a 128-byte stage row is 4, 4 or 2 k-steps
+  constexpr int KS = kF8 ? 2 : 4;
+  constexpr int kMfmaStep = MI * NI * (sizeof(T) == 4 ? 4 : 1);   // MFMAs per k-step
+  constexpr int kReadStep = (MI + NI) * (kF8 ? 2 : 1);            // LDS reads per k-step
+  static_assert(!kF8 || mode == GM_GRAM, "fp8 operands are for the Gram");
   // S operand slots; after the K loop the same memory stages the epilogue
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * kOpBytes];
   static_assert(S * kOpBytes >= NW * kSlabBytes, "epilogue staging fits in the slots");
@@ -199,10 +215,20 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   const T *P, *Q;
   int ld, K;
   if constexpr (mode == GM_GRAM) {
-    const T* x = (const T*)M.x[cur];
-    P = x + (size_t)it.tm * TILE * Lp;
-    Q = x + (size_t)it.tn * TILE * Lp;
-    ld = Lp; K = Lp;
+    if constexpr (kF8) {
+      // the fp8 copy of X0 (first Gram of a pass) is stored in panels of 64
+      // columns, each s_pad x 64 bytes: a tile's rows start at row tm*TILE of
+      // panel 0, row pitch 64 bytes
+      const T* x = (const T*)M.x8;
+      P = x + (size_t)it.tm * TILE * 64;
+      Q = x + (size_t)it.tn * TILE * 64;
+      ld = 64; K = Lp;
+    } else {
+      const T* x = (const T*)M.x[cur];
+      P = x + (size_t)it.tm * TILE * Lp;
+      Q = x + (size_t)it.tn * TILE * Lp;
+      ld = Lp; K = Lp;
+    }
   } else if constexpr (mode == GM_SQ) {
     const T* a = (const T*)M.sq[role_p];
     P = a + (size_t)it.tm * TILE * sp;
@@ -232,9 +258,17 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // physical chunk p%8 of it. Physical chunk c' of row r holds logical chunk
   // c' ^ ((r >> 1) & 7); for these rows that term is (4 w + p/16) % 8, so a
   // lane needs one 32-bit byte offset for the whole K loop.
+  // fp8 panels: logical chunks 0-3 of a stage row lie in panel 2 ks, chunks
+  // 4-7 in panel 2 ks + 1 (pstride bytes further), so the per-lane offset
+  // still holds for the whole K loop and a stage advances two panels.
   const int prow = 8 * wave + (lane >> 3);
-  const uint32_t lane_off = (uint32_t)(((int64_t)prow * ld + ((lane & 7) ^ ((prow >> 1) & 7)) * CPR) * sizeof(T));
+  const int lchunk = (lane & 7) ^ ((prow >> 1) & 7);
+  const int pstride = kF8 ? sp * 64 : 0;   // bytes per fp8 panel
+  const uint32_t lane_off =
+      kF8 ? (uint32_t)(prow * 64 + (lchunk & 3) * 16 + (lchunk >> 2) * pstride)
+          : (uint32_t)(((int64_t)prow * ld + lchunk * CPR) * sizeof(T));
   const int rstep = (int)((int64_t)8 * NW * ld * sizeof(T));
+  const int kstride = kF8 ? 2 * pstride : kRowBytes;   // bytes from one K stage to the next
   // Buffer resources over the two operand panels. Every read stays inside
   // its panel: the K offset travels in the scalar offset and stages past the
   // end of K are clamped. On a diagonal tile of the two symmetric products
@@ -243,7 +277,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // count, each of its loads fails the check and fetches nothing (the issue
   // count, and with it every wait, stays the same); both operands' fragments
   // are read from the first panel's slot.
-  const int ext = (int)((int64_t)TILE * ld * sizeof(T));
+  const int ext = kF8 ? (Lp / 64 - 1) * pstride + TILE * 64 : (int)((int64_t)TILE * ld * sizeof(T));
   const bool same = (mode == GM_GRAM || mode == GM_SQ) && (it.tm == it.tn);
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void*)P, (short)0, ext, 0x00020000);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Q, (short)0, same ? 0 : ext, 0x00020000);
@@ -258,27 +292,52 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
 #pragma unroll
     for (int i = 0; i < LPO; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds((o & 1) ? rq : rp, LDS_PTR(sm + (NW * i + wave) * 1024), 16,
-                                               lane_off, ks * kRowBytes + i * rstep, 0, 0);
+                                               lane_off, ks * kstride + i * rstep, 0, 0);
   };
 
   // Fragments: lane l reads tile row (block base + l%32), logical chunk
-  // 2 s + l/32 of the stage (8 bf16 or 4 fp32 consecutive k) for k-step s.
+  // 2 s + l/32 of the stage (8 bf16 or 4 fp32 consecutive k) for k-step s;
+  // fp8: chunks 4 s + 2 (l/32) and the next one (32 consecutive k). The
+  // matrix cores pair A and B elements by the same lane half and register
+  // position, so any layout both operands share gives the same sums.
   typedef typename Elem<T>::Frag Frag;
   Frag fa[2][MI], fb[2][NI];
   const int lr = lane & 31;
   auto read_frags = [&](int pslot, int qslot, int s, int buf) {
     const uint8_t* sa = smem + pslot * kOpBytes;
     const uint8_t* sb = same ? sa : smem + qslot * kOpBytes;
-    const int ph = ((2 * s + (lane >> 5)) ^ ((lr >> 1) & 7)) * 16;
+    if constexpr (kF8) {
+      const int c0 = 4 * s + 2 * (lane >> 5);
+      const int ph0 = (c0 ^ ((lr >> 1) & 7)) * 16, ph1 = ((c0 + 1) ^ ((lr >> 1) & 7)) * 16;
+      auto frag = [&](const uint8_t* row) {
+        const u32x4_t lo = *(const u32x4_t*)(row + ph0), hi = *(const u32x4_t*)(row + ph1);
+        return (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                         (int)hi[3]};
+      };
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      fa[buf][mi] = *(const Frag*)(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes + ph);
+      for (int mi = 0; mi < MI; ++mi) fa[buf][mi] = frag(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes);
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-      fb[buf][ni] = *(const Frag*)(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
+      for (int ni = 0; ni < NI; ++ni) fb[buf][ni] = frag(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes);
+    } else {
+      const int ph = ((2 * s + (lane >> 5)) ^ ((lr >> 1) & 7)) * 16;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        fa[buf][mi] = *(const Frag*)(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes + ph);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        fb[buf][ni] = *(const Frag*)(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
+    }
   };
   auto mfmas = [&](int buf) {
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (kF8) {
+      // e4m3 operands (format 0), unit block scales (E8M0 127 = 1.0)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[buf][mi], fb[buf][ni], acc[mi][ni], 0, 0,
+                                                                        0, 127, 0, 127);
+    } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -321,9 +380,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // slots of stage k (ps, qs) and of stage k+1 (pn, qn)
   int ps = 0, qs = 1, pn = 2 % S, qn = 3 % S;
   for (int k = 0; k < nk - 1; ++k) {
-    // k-steps 0-2, each with the next k-step's fragments read between its MFMAs
+    // all k-steps but the last, each with the next k-step's fragments read
+    // between its MFMAs
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
+    for (int s = 0; s < KS - 1; ++s) {
       read_frags(ps, qs, s + 1, (s + 1) & 1);
       mfmas(s & 1);
       spread(kReadStep, 0);
@@ -335,7 +395,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     wait_vm<(S - 4) * LPO>();
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // k-step 3: the refill of the freed slots with operand stages 2k+S and
+    // the last k-step: the refill of the freed slots with operand stages 2k+S and
     // 2k+S+1 (longest latency first), then the next stage's first fragments.
     // With 256-tiles it runs at raised wave priority: a wave still in it
     // outranks the waves of its SIMD that have moved on to the next stage, so
@@ -356,11 +416,11 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     qn = (qn + 2 >= S) ? qn + 2 - S : qn + 2;
   }
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
+  for (int s = 0; s < KS - 1; ++s) {
     read_frags(ps, qs, s + 1, (s + 1) & 1);
     mfmas(s & 1);
   }
-  mfmas(1);
+  mfmas(1);   // KS is even: the last k-step's fragments are in buffer 1
   wait_vm<0>();
   // Keep every MFMA above this point and give the last ones time to write
   // their accumulators before the epilogue reads them through inline asm
@@ -404,7 +464,9 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   const bool diag_sym = mode == GM_SYM && it.tm == it.tn;
   if (diag_sym) write_t = true;
   __syncthreads();   // every wave is done with the slots
-  if constexpr (sizeof(T) == 2 && mode != GM_SQ) {
+  // the fp8 Gram's products carry the square of the operand scale q
+  const float oscale = kF8 ? M.scal[SC_F8INV2] : 1.f;
+  if constexpr ((sizeof(T) == 2 || kF8) && mode != GM_SQ) {
     // bf16 outputs that are the accumulators rounded: each wave stages its
     // whole (MI*32) x (NI*32) tile at once, rounded, column-major (a column's
     // rows contiguous), so a lane's four consecutive-row accumulators go in
@@ -426,10 +488,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         for (int g = 0; g < 4; ++g) {
           const int col = ni * 32 + (lane & 31);
           const int row = mi * 32 + 8 * g + 4 * (lane >> 5);   // rows row..row+3: registers 4g..4g+3
-          const unsigned int lo = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g])) |
-                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 1])) << 16);
-          const unsigned int hi = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 2])) |
-                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 3])) << 16);
+          const unsigned int lo = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g]) * oscale) |
+                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 1]) * oscale) << 16);
+          const unsigned int hi = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 2]) * oscale) |
+                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 3]) * oscale) << 16);
           *(u32x2_t*)(st + sidx(row, col)) = (u32x2_t){lo, hi};
         }
     wave_lds_sync();
@@ -476,71 +538,73 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     }
     return;
   }
-  // 32-row fp32 slabs; the second product's A values for a slab are loaded
-  // before the slab is staged, so their latency overlaps the staging
-  float* buf = (float*)(smem + wave * kSlabBytes);
-  constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
-  constexpr int KK = SC / 16;                // 8-column chunks per lane per slab
+  if constexpr (!kF8) {
+    // 32-row fp32 slabs; the second product's A values for a slab are loaded
+    // before the slab is staged, so their latency overlaps the staging
+    float* buf = (float*)(smem + wave * kSlabBytes);
+    constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
+    constexpr int KK = SC / 16;                // 8-column chunks per lane per slab
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    typename Elem<T>::Raw araw[mode == GM_SQ ? KK : 1];
-    if constexpr (mode == GM_SQ) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int q = kk * 64 + lane;
-        const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
-        araw[kk] = Elem<T>::ldraw(M.sq[role_p], (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8);
-      }
-    }
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        buf[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + ni * 32 + (lane & 31)] = agpr_read(acc[mi][ni][r]);
-    wave_lds_sync();
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int q = kk * 64 + lane;
-      const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
-      float v[8];
-      const size_t idx = (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8;
+    for (int mi = 0; mi < MI; ++mi) {
+      typename Elem<T>::Raw araw[mode == GM_SQ ? KK : 1];
       if constexpr (mode == GM_SQ) {
-        // B' = b A + c A^2 + a I
-        float av[8];
-        Elem<T>::cvt(araw[kk], av);
-        const int dg = (row0 + mi * 32 + rr) - (col0 + c8);   // the diagonal is at e = dg
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = cc * buf[rr * kPitch + c8 + e] + cb * av[e] + (e == dg ? ca : 0.f);
-      } else {
+        for (int kk = 0; kk < KK; ++kk) {
+          const int q = kk * 64 + lane;
+          const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
+          araw[kk] = Elem<T>::ldraw(M.sq[role_p], (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8);
+        }
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = buf[rr * kPitch + c8 + e];
-      }
-      if (write_o) {
-        const int d = (col0 + c8) - (row0 + mi * 32 + rr);   // upper when d + e >= 0
-        if (!diag_sym || d >= 0) Elem<T>::st8(out, idx, v);
-        else if (d > -8) Elem<T>::st8_part(out, idx, v, -d, 8);
-      }
-      if (mode == GM_SQ && write_t) {
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) buf[rr * kPitch + c8 + e] = v[e];
-      }
-    }
-    if (write_t) {
+        for (int r = 0; r < 16; ++r)
+          buf[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + ni * 32 + (lane & 31)] = agpr_read(acc[mi][ni][r]);
       wave_lds_sync();
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int q = kk * 64 + lane;
-        const int c1 = q >> 2, rc = (q & 3) * 8;
+        const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
         float v[8];
+        const size_t idx = (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8;
+        if constexpr (mode == GM_SQ) {
+          // B' = b A + c A^2 + a I
+          float av[8];
+          Elem<T>::cvt(araw[kk], av);
+          const int dg = (row0 + mi * 32 + rr) - (col0 + c8);   // the diagonal is at e = dg
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = buf[(rc + e) * kPitch + c1];
-        const size_t tidx = (size_t)(col0 + c1) * ldt + row0 + mi * 32 + rc;
-        const int d = (col0 + c1) - (row0 + mi * 32 + rc);   // mirror of a strict-upper source when e < d
-        if (!diag_sym || d >= 8) Elem<T>::st8(outT, tidx, v);
-        else if (d > 0) Elem<T>::st8_part(outT, tidx, v, 0, d);
+          for (int e = 0; e < 8; ++e) v[e] = cc * buf[rr * kPitch + c8 + e] + cb * av[e] + (e == dg ? ca : 0.f);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = buf[rr * kPitch + c8 + e];
+        }
+        if (write_o) {
+          const int d = (col0 + c8) - (row0 + mi * 32 + rr);   // upper when d + e >= 0
+          if (!diag_sym || d >= 0) Elem<T>::st8(out, idx, v);
+          else if (d > -8) Elem<T>::st8_part(out, idx, v, -d, 8);
+        }
+        if (mode == GM_SQ && write_t) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) buf[rr * kPitch + c8 + e] = v[e];
+        }
       }
+      if (write_t) {
+        wave_lds_sync();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const int q = kk * 64 + lane;
+          const int c1 = q >> 2, rc = (q & 3) * 8;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = buf[(rc + e) * kPitch + c1];
+          const size_t tidx = (size_t)(col0 + c1) * ldt + row0 + mi * 32 + rc;
+          const int d = (col0 + c1) - (row0 + mi * 32 + rc);   // mirror of a strict-upper source when e < d
+          if (!diag_sym || d >= 8) Elem<T>::st8(outT, tidx, v);
+          else if (d > 0) Elem<T>::st8_part(outT, tidx, v, 0, d);
+        }
+      }
+      wave_lds_sync();
     }
-    wave_lds_sync();
   }
 }
 
@@ -570,7 +634,13 @@ hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, i
     else if (mode == GM_SYM) NS_LAUNCH(T, GM_SYM, WM, WN, TL); \
     else NS_LAUNCH(T, GM_BX, WM, WN, TL);                     \
   } while (0)
-  if (ns_t == DT_BF16) {
+  if (ns_t == DT_F8) {
+    // fp8 operands: the Gram only
+    if (mode != GM_GRAM) return hipErrorInvalidValue;
+    if (tile == 128) NS_LAUNCH(F8, GM_GRAM, 2, 2, 128);
+    else if (variant == 1) NS_LAUNCH(F8, GM_GRAM, 2, 2, 256);
+    else NS_LAUNCH(F8, GM_GRAM, 4, 2, 256);
+  } else if (ns_t == DT_BF16) {
     if (tile == 128) NS_MODES(__bf16, 2, 2, 128);
     else if (variant == 1) NS_MODES(__bf16, 2, 2, 256);
     else NS_MODES(__bf16, 4, 2, 256);

@@ -40,6 +40,7 @@ __device__ __forceinline__ float bf2f(unsigned short h) { return __uint_as_float
 
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 #define GLOBAL_AS __attribute__((address_space(1)))
 // Loads and stores through global address-space pointers (all buffers here
@@ -152,6 +153,44 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   float t = 0.f;
   for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
   return t;
+}
+
+// Block maximum (256 threads); result valid in every thread.
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// float -> OCP e4m3 (bias 7, no infinities, largest finite 448), round to
+// nearest even, magnitudes clamped to 448. Subnormals are m 2^-9 (m < 8);
+// m reaching 8 carries into the smallest normal, whose code is also 8.
+__device__ __forceinline__ unsigned int f2e4m3(float x) {
+  const unsigned int sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  unsigned int code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal range
+    code = (unsigned int)rintf(a * 512.f);   // 0 .. 8
+  } else {
+    unsigned int u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);        // round the mantissa to 3 bits, ties to even
+    code = ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);   // exponent - 127 + 7
+  }
+  return sign | code;
+}
+
+// Power-of-two scale for the fp8 copy of X0, from an upper bound on |X0|:
+// the largest q = 2^e with q * bound <= 448 (1 when the bound is 0).
+__device__ __forceinline__ float f8_scale(float bound) {
+  if (!(bound > 0.f)) return 1.f;
+  const float e = fminf(fmaxf(floorf(log2f(448.f / bound)), -100.f), 100.f);
+  return exp2f(e);
 }
 
 // Sum of n floats p[0], p[stride], ..., in index order, eight loads at a time.
@@ -334,11 +373,17 @@ __global__ __launch_bounds__(256) void k_norms_lines(DevMat* __restrict__ mats, 
     gst<float>(M.dvec + i, d);
     ypart = (d * rho) * (d * rho);
   }
+  // the largest squared norm among the lines that bound every element of
+  // X0 / scale: the equilibrated lines (D_l rho_l)^2, or the storage rows
+  float mpart = M.aurora ? ypart : (rowline && i < M.rows ? tpart : 0.f);
   tpart = block_sum(tpart, red);
   ypart = block_sum(ypart, red);
+  mpart = block_max(mpart, red);
   if (threadIdx.x == 0) {
+    const int nlb = nrb + (wide ? (M.cols + 255) / 256 : 0);
     gst<float>(M.linepart + 2 * local, tpart);
     gst<float>(M.linepart + 2 * local + 1, ypart);
+    gst<float>(M.linepart + 2 * nlb + local, mpart);
   }
 }
 
@@ -352,21 +397,27 @@ __global__ __launch_bounds__(256) void k_norms_scalars(DevMat* __restrict__ mats
   const int t = threadIdx.x;
   const int nrb = (M.rows + 255) / 256;
   const int nlb = nrb + (M.rows < M.cols ? (M.cols + 255) / 256 : 0);
-  float tot = 0.f, ysq = 0.f;
+  float tot = 0.f, ysq = 0.f, mx = 0.f;
   for (int b = t; b < nlb; b += 256) {
     tot += gld<float>(M.linepart + 2 * b);
     ysq += gld<float>(M.linepart + 2 * b + 1);
+    mx = fmaxf(mx, gld<float>(M.linepart + 2 * nlb + b));
   }
   tot = block_sum(tot, red);
   ysq = block_sum(ysq, red);
+  mx = block_max(mx, red);
   if (!M.aurora) ysq = tot;
   if (init_power) {
     const float v0 = 1.f / sqrtf((float)M.cols);
     for (int c = t; c < M.cols; c += 256) gst<float>(M.pv + c, v0);
   }
   if (t == 0) {
+    const float scale = 1.f / (sqrtf(ysq) + ns_eps);
+    const float q = f8_scale(scale * sqrtf(mx));   // every element of X0 is at most scale * sqrt(mx)
     M.scal[SC_XNORM2] = tot;
-    M.scal[SC_SCALE] = 1.f / (sqrtf(ysq) + ns_eps);
+    M.scal[SC_SCALE] = scale;
+    M.scal[SC_F8Q] = q;
+    M.scal[SC_F8INV2] = 1.f / (q * q);
     M.scal[SC_SIGMA] = 0.f;
     M.scal[SC_KAPPA] = 0.f;
     M.ist[IS_PSTEPS] = 0;
@@ -392,6 +443,17 @@ __device__ __forceinline__ void prologue_body(const DevMat& M, int local, const 
   const int br = (local / ntc) * 64, bc = (local % ntc) * 64;
   const bool vs = aligned16(src, lds, dts);
   const float scale = M.scal[SC_SCALE];
+  // the fp8 copy of x[0] for the first Gram (x8 is null when not wanted), in
+  // panels of 64 columns of s_pad x 64 bytes: a 64 x 64 tile is 4 KB of
+  // contiguous bytes
+  uint8_t* x8 = (uint8_t*)M.x8;
+  const float q8 = M.scal[SC_F8Q];
+  auto put8 = [&](int r, int c, const float v[8]) {   // x[0](r, c .. c + 7), c % 8 == 0
+    u32x2_t w;
+    w[0] = f2e4m3(v[0] * q8) | (f2e4m3(v[1] * q8) << 8) | (f2e4m3(v[2] * q8) << 16) | (f2e4m3(v[3] * q8) << 24);
+    w[1] = f2e4m3(v[4] * q8) | (f2e4m3(v[5] * q8) << 8) | (f2e4m3(v[6] * q8) << 16) | (f2e4m3(v[7] * q8) << 24);
+    gst<u32x2_t>(x8 + ((size_t)(c >> 6) * M.s_pad + r) * 64 + (c & 63), w);
+  };
   // direct frame: wide -> x[0] (ld L_pad); tall -> xt[0] (ld s_pad)
   void* dir = M.tall ? M.xt[0] : M.x[0];
   void* tra = M.tall ? M.x[0] : M.xt[0];
@@ -447,6 +509,7 @@ __device__ __forceinline__ void prologue_body(const DevMat& M, int local, const 
       tile[i][j + e] = v[e];
     }
     Ty<T>::st(dir, (size_t)rr[h] * ld_dir + cc[h], v);
+    if (x8 && !M.tall) put8(rr[h], cc[h], v);
   }
   __syncthreads();
 #pragma unroll
@@ -457,6 +520,7 @@ __device__ __forceinline__ void prologue_body(const DevMat& M, int local, const 
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tile[i0 + e][jc];
     Ty<T>::st(tra, (size_t)(bc + jc) * ld_tra + br + i0, v);
+    if (x8 && M.tall) put8(bc + jc, br + i0, v);
   }
 }
 
@@ -490,7 +554,7 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
   const int l = local * 4 + w;
   const int nl = M.eq_short ? M.s : M.L;      // equilibrated lines
   const int len = M.eq_short ? M.L : M.s;     // entries per line
-  float contrib = 0.f;
+  float contrib = 0.f;   // (D_l rho_l)^2 of this wave's line
   if (l < nl) {
     const void* ut = M.eq_short ? M.x[M.fin] : M.xt[M.fin];
     const size_t row = (size_t)l * (M.eq_short ? M.L_pad : M.s_pad);
@@ -525,7 +589,11 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
   }
   if (lane == 0) red[w] = contrib;
   __syncthreads();
-  if (threadIdx.x == 0) M.tailpart[local] = red[0] + red[1] + red[2] + red[3];
+  if (threadIdx.x == 0) {
+    const int nb = (nl + 3) / 4;   // blocks of this launch for the matrix
+    M.tailpart[local] = red[0] + red[1] + red[2] + red[3];
+    M.tailpart[nb + local] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
 }
 
 __global__ __launch_bounds__(256) void k_aurora_scale(DevMat* __restrict__ mats, LaunchList L, float ns_eps) {
@@ -533,10 +601,20 @@ __global__ __launch_bounds__(256) void k_aurora_scale(DevMat* __restrict__ mats,
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   const int nb = ((M.eq_short ? M.s : M.L) + 3) / 4;   // blocks of k_aurora_dupdate
-  float s = 0.f;
-  for (int i = threadIdx.x; i < nb; i += 256) s += gld<float>(M.tailpart + i);
+  float s = 0.f, mx = 0.f;
+  for (int i = threadIdx.x; i < nb; i += 256) {
+    s += gld<float>(M.tailpart + i);
+    mx = fmaxf(mx, gld<float>(M.tailpart + nb + i));
+  }
   s = block_sum(s, red);
-  if (threadIdx.x == 0) M.scal[SC_SCALE] = 1.f / (sqrtf(s) + ns_eps);
+  mx = block_max(mx, red);
+  if (threadIdx.x == 0) {
+    const float scale = 1.f / (sqrtf(s) + ns_eps);
+    const float q = f8_scale(scale * sqrtf(mx));
+    M.scal[SC_SCALE] = scale;
+    M.scal[SC_F8Q] = q;
+    M.scal[SC_F8INV2] = 1.f / (q * q);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -646,6 +646,44 @@ def test_aurora_wide_rows_option(dev, dtype, tol):
         check_update(f"wide_rows[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], cfg, tol)
 
 
+def test_fp8_first_gram_option(dev):
+    """MUON_FLAG_FP8_GRAM (research option): the first Gram of each pass of
+    bf16 matrices that run blocks reads an fp8 copy of X0. Against the oracle
+    at the bf16 bar (row norms too); against the same call without the option
+    it differs (fp8 was used) by about the bf16 rounding level; fp32 and
+    square matrices, which do not take it, are bitwise unchanged."""
+    say("fp8 first Gram option")
+    shapes = [(600, 2048), (2048, 600), (520, 1030), (512, 512)]
+    cfg8 = mu.make_config(flags=mu.MUON_FLAG_FP8_GRAM)
+    cfg0 = mu.default_config()
+    mats = [gen.custom_matrix(sh, 2900 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3, mom_sd=1e-3,
+                              weight_dtype=torch.bfloat16) for i, sh in enumerate(shapes)]
+    mats.append(gen.custom_matrix((300, 700), 2950, dev))          # fp32: not taken
+    G, M0, W0, M8, V8, W8 = run_update(dev, mats, cfg8)
+    _, _, _, M0b, V0, W0b = run_update(dev, mats, cfg0)
+    for i, sh in enumerate(shapes + [(300, 700)]):
+        tol = BF16_TOL if i < len(shapes) else FP32_TOL
+        check_update(f"fp8gram[{sh}]", G[i], M0[i], W0[i], M8[i], V8[i], W8[i], cfg8, tol,
+                     ROW_TOL if i < len(shapes) else None)
+        d = rel(f64(V8[i]), f64(V0[i]))
+        say(f"  {sh}: rel(fp8 option vs without) = {d:.2e}")
+        if i < 3:
+            assert 0 < d < 2e-2, (sh, d)
+        else:
+            assert torch.equal(V8[i], V0[i]), sh                 # square / fp32: unchanged
+    for name, fn, ref in (("ns_polar", mu.ns_polar, lambda x: O.newton_schulz(x)),
+                          ("aurora", mu.aurora_orthogonalize, lambda x: O.aurora_orthogonalize(x))):
+        xs = [gen.custom_matrix(sh, 2960 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3)[0]
+              for i, sh in enumerate(shapes[:3])]
+        outs = fn(xs, [torch.empty(x.shape, device=dev) for x in xs], cfg=cfg8)
+        torch.cuda.synchronize()
+        for x, o in zip(xs, outs):
+            want = ref(f64(x))
+            e, r = rel(f64(o), want), row_agree(f64(o), want)
+            say(f"  {name} {tuple(x.shape)} fp8 first Gram: rel={e:.2e} rows={r:.2e}")
+            assert e <= BF16_TOL and r <= ROW_TOL
+
+
 def test_overlapping_rows_rejected(dev):
     """An expanded momentum (stride(0) = 0: every row the same memory) is
     rejected before anything is enqueued and stays untouched."""
