@@ -285,12 +285,12 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // Operand stage o is P (o even) or Q (o odd) of stage o/2; it goes to
   // slot o % S. Stages past the end of K are clamped to the last one: an
   // L2-resident re-read into a slot nobody reads again, which keeps every
-  // wait below the same.
-  auto issue = [&](int slot, int o) {
+  // wait below the same. issue() takes loads [i0, i1) of this wave's LPO.
+  auto issue = [&](int slot, int o, int i0, int i1) {
     const int ks = min(o >> 1, nk - 1);
     uint8_t* sm = smem + slot * kOpBytes;
 #pragma unroll
-    for (int i = 0; i < LPO; ++i)
+    for (int i = i0; i < i1; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds((o & 1) ? rq : rp, LDS_PTR(sm + (NW * i + wave) * 1024), 16,
                                                lane_off, ks * kstride + i * rstep, 0, 0);
   };
@@ -371,43 +371,61 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     }
   };
 
-  // Prologue: fill every slot, wait for stage 0, read its first k-step.
+  // Refill schedule. After the barrier of stage k the slots of stage k are
+  // free; the last k-step refills one of them with operand stage 2k + S
+  // (needed at the next barrier), and the first two k-steps of stage k + 1
+  // load operand stage 2k + S + 1 into the other, in halves (needed one
+  // barrier later). Issuing all of a stage's refill at once, eight 1 KB
+  // loads per wave from all eight waves, held waves in load issue while
+  // their k-step had 256 cycles of matrix work (3-7 % per product).
+  // Prologue: operand stages 0 .. S-2 (stage S-1 is the first deferred
+  // half-refill); wait for stage 0, read its first k-step.
 #pragma unroll
-  for (int o = 0; o < S; ++o) issue(o, o);
-  wait_vm<(S - 2) * LPO>();
+  for (int o = 0; o < S - 1; ++o) issue(o, o, 0, LPO);
+  wait_vm<(S - 3) * LPO>();
   ring_barrier();
   read_frags(0, 1, 0, 0);
   // slots of stage k (ps, qs) and of stage k+1 (pn, qn)
   int ps = 0, qs = 1, pn = 2 % S, qn = 3 % S;
+  constexpr int NDS = KS - 1 < 2 ? KS - 1 : 2;   // k-steps that carry the deferred refill
   for (int k = 0; k < nk - 1; ++k) {
     // all k-steps but the last, each with the next k-step's fragments read
-    // between its MFMAs
+    // between its MFMAs; the first NDS also issue part of operand stage
+    // 2k + S - 1 into the slot freed at the previous barrier (the slot after
+    // stage k + 1's two)
+    const int dslot = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s) {
-      read_frags(ps, qs, s + 1, (s + 1) & 1);
-      mfmas(s & 1);
-      spread(kReadStep, 0);
+      if (s < NDS) {
+        issue(dslot, 2 * k + S - 1, s * LPO / NDS, (s + 1) * LPO / NDS);
+        read_frags(ps, qs, s + 1, (s + 1) & 1);
+        mfmas(s & 1);
+        spread(kReadStep + LPO / NDS, LPO / NDS);
+      } else {
+        read_frags(ps, qs, s + 1, (s + 1) & 1);
+        mfmas(s & 1);
+        spread(kReadStep, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // stage k+1 has landed for every wave (only the S - 4 most recent
-    // operand stages may be in flight); stage k's slots are free
+    // stage k+1 has landed for every wave (only the deferred operand stage,
+    // the S - 4 most recent, may be in flight); stage k's slots are free
     wait_lgkm0();
     wait_vm<(S - 4) * LPO>();
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // the last k-step: the refill of the freed slots with operand stages 2k+S and
-    // 2k+S+1 (longest latency first), then the next stage's first fragments.
+    // the last k-step: the refill of one freed slot with operand stage 2k+S,
+    // then the next stage's first fragments.
     // With 256-tiles it runs at raised wave priority: a wave still in it
     // outranks the waves of its SIMD that have moved on to the next stage, so
     // the waves reach the next barrier closer together (1-1.2 % faster on the
     // 3072-row products). 128-tiles, two workgroups per CU, keep the default.
     if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(2);
     __builtin_amdgcn_sched_barrier(0);
-    issue(ps, 2 * k + S);
-    issue(qs, 2 * k + S + 1);
+    issue(ps, 2 * k + S, 0, LPO);
     read_frags(pn, qn, 0, 0);
     mfmas(1);
-    spread(2 * LPO + kReadStep, 2 * LPO);
+    spread(LPO + kReadStep, LPO);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
