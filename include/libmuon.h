@@ -27,7 +27,9 @@
  *  - Errors: no exception crosses the ABI. Calls return a muon_status; a
  *    negative value is an error. All arguments are validated on the host
  *    before anything is enqueued: on any error nothing is enqueued and no
- *    caller buffer is touched. muon_last_error() gives a message.
+ *    caller buffer is touched. muon_last_error() gives a message. (With
+ *    MUON_FLAG_CHECK_FINITE a read-only device pass also checks the input
+ *    values; a non-finite one is reported the same way, no buffer written.)
  *  - Asynchrony: compute calls enqueue on the handle's stream and return.
  *    Inputs must stay valid and unmodified until that stream reaches the
  *    work. Device faults surface as MUON_ERR_HIP on a later call or on the
@@ -60,7 +62,8 @@ typedef enum {
   MUON_ERR_ALLOC = -4,            /* device workspace allocation failed */
   MUON_ERR_HIP = -5,              /* a HIP runtime call failed */
   MUON_ERR_NO_DEVICE = -6,        /* no usable gfx950 device */
-  MUON_ERR_TOO_LARGE = -7         /* muon_update_static: the batch does not fit the static scratch */
+  MUON_ERR_TOO_LARGE = -7,        /* muon_update_static: the batch does not fit the static scratch */
+  MUON_ERR_NONFINITE = -8         /* MUON_FLAG_CHECK_FINITE: an input element is NaN or Inf */
 } muon_status_code;
 typedef int muon_status;
 
@@ -143,11 +146,24 @@ typedef struct {
  * side average the operands' rounding: measured error stays at the bf16
  * path's level (about 5e-3 relative Frobenius). Later Grams, the short-side
  * products and X' = Q X stay bf16 (fp8 there costs 1e-2 to 5e-2).
+ *
+ * MUON_FLAG_CHECK_FINITE — an input check for callers that want a NaN or
+ * Inf to stop the step instead of spreading through it (the pages define
+ * no such check; without the flag a non-finite input gives non-finite
+ * results for its matrix only). Before anything is written, one read-only
+ * pass over every matrix's grad (the polar input), momentum and weight
+ * looks for NaN or Inf; the call then waits for that pass on its stream
+ * (the one case where a compute call synchronises). If any element is not
+ * finite the call returns MUON_ERR_NONFINITE, names the first such matrix
+ * in muon_last_error(), and leaves every caller buffer as it was;
+ * otherwise the step runs as without the flag, with bitwise-equal results.
+ * Costs one read of the inputs and the synchronisation.
  */
 #define MUON_FLAG_SGD_MOMENTUM 0x1u
 #define MUON_FLAG_WIDE_ROWS    0x2u
 #define MUON_FLAG_FP8_GRAM     0x4u
-#define MUON_FLAG_ALL          0x7u
+#define MUON_FLAG_CHECK_FINITE 0x8u
+#define MUON_FLAG_ALL          0xFu
 
 /* Per-kernel-class timing gathered when profiling is on (see muon_profile_*). */
 typedef struct {

@@ -27,7 +27,7 @@ __all__ = [
     "library_path", "default_config", "classic_config", "momentum_warmup", "make_config", "ns_polar",
     "aurora_orthogonalize", "muon_update", "check_update_args",
     "check_polar_args", "get_handle", "STATUS", "muon_update_static", "MUON_FLAG_SGD_MOMENTUM", "MUON_FLAG_WIDE_ROWS",
-    "MUON_FLAG_FP8_GRAM",
+    "MUON_FLAG_FP8_GRAM", "MUON_FLAG_CHECK_FINITE",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,10 +38,11 @@ MUON_F32, MUON_BF16 = 0, 1
 MUON_FLAG_SGD_MOMENTUM = 0x1    # classic recipe's SGD momentum (buf = mu buf + G)
 MUON_FLAG_WIDE_ROWS = 0x2       # Aurora on a wide matrix's own rows
 MUON_FLAG_FP8_GRAM = 0x4        # fp8 operands for the first Gram of each pass (research option)
+MUON_FLAG_CHECK_FINITE = 0x8    # refuse (MUON_ERR_NONFINITE, nothing written) inputs with a NaN or Inf
 STATUS = {
     0: "MUON_OK", -1: "MUON_ERR_INVALID_ARG", -2: "MUON_ERR_UNSUPPORTED_DTYPE",
     -3: "MUON_ERR_SHAPE_MISMATCH", -4: "MUON_ERR_ALLOC", -5: "MUON_ERR_HIP",
-    -6: "MUON_ERR_NO_DEVICE", -7: "MUON_ERR_TOO_LARGE",
+    -6: "MUON_ERR_NO_DEVICE", -7: "MUON_ERR_TOO_LARGE", -8: "MUON_ERR_NONFINITE",
 }
 
 

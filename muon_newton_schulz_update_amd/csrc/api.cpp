@@ -40,6 +40,7 @@ hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, i
                           int roles, float ca, float cb, float cc, int variant, int tile, hipStream_t st);
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  int sgd, hipStream_t st);
+hipError_t launch_check_finite(DevMat* m, LaunchList L, int nblk, int upd, hipStream_t st);
 hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st);
 hipError_t launch_norms_scalars(DevMat* m, LaunchList L, int nblk, float ns_eps, int init_power, hipStream_t st);
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st);
@@ -221,6 +222,7 @@ struct muon_handle {
   std::map<std::string, std::unique_ptr<muon::Plan>> plans;
   uint64_t tick = 0;
   void* pinned = nullptr;
+  int32_t* bad_host = nullptr;   // pinned, kMaxBatch flags: the input check's per-matrix results
   size_t pinned_bytes = 0;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -800,6 +802,23 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   }
   (void)el_all;
 
+  // 0. optional input check: read-only, before anything is written; the
+  // flags come back into pinned host memory and the call waits for them
+  if ((cfg.flags & MUON_FLAG_CHECK_FINITE) && !P->mats.empty()) {
+    const size_t nm = P->mats.size();
+    CHECK_LAUNCH(h, launch_check_finite(D, dev_list(meta, P->stream), P->stream.nblk, upd ? 1 : 0, st));
+    HIP_TRY(h, hipMemcpy2DAsync(h->bad_host, sizeof(int32_t), &D[0].bad, sizeof(DevMat), sizeof(int32_t), nm,
+                                hipMemcpyDeviceToHost, st));
+    HIP_TRY(h, hipStreamSynchronize(st));
+    int first = -1;
+    for (size_t i = 0; i < nm; ++i)
+      if (h->bad_host[i] && (first < 0 || P->mats[i].user < first)) first = P->mats[i].user;
+    if (first >= 0)
+      return set_err(h, MUON_ERR_NONFINITE,
+                     "matrix " + std::to_string(first) + " of the batch has a NaN or Inf among its inputs" +
+                         (upd ? " (grad, momentum or weight)" : "") + "; nothing was written");
+  }
+
   // 1. momentum/Nesterov (or input) + norms
   {
     ProfScope ps(h, 1, b_mom);
@@ -972,6 +991,12 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
     muon_destroy(h);
     return MUON_ERR_ALLOC;
   }
+  if (hipHostMalloc((void**)&h->bad_host, kMaxBatch * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    h->bad_host = nullptr;
+    muon_destroy(h);
+    return MUON_ERR_ALLOC;
+  }
   *out = h;
   return MUON_OK;
 }
@@ -986,6 +1011,7 @@ extern "C" muon_status muon_destroy(muon_handle* h) {
   if (h->upload_done) (void)hipEventDestroy(h->upload_done);
   if (h->static_done) (void)hipEventDestroy(h->static_done);
   if (h->static_stage) (void)hipHostFree(h->static_stage);
+  if (h->bad_host) (void)hipHostFree(h->bad_host);
   for (auto& r : h->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (auto e : h->ev_pool) (void)hipEventDestroy(e);
   delete h;

@@ -106,6 +106,7 @@ struct DevMat {
   void* sq[SQ_COUNT];   // short-side matrices by role (a matrix with one-iteration blocks aliases SQ_Q0 to SQ_B
                         // and leaves SQ_T, SQ_Q1 unused)
   int32_t fin;          // x[fin] / xt[fin] holds the result of the last pass (blocks per pass, mod 2)
+  int32_t bad;          // 0 as uploaded; k_check_finite sets it when an input element is NaN or Inf
   float* rowpart;   // rows x n_seg   : row sums of squares per tile segment
   float* colpart;   // n_rt x cols    : column sums of squares per row tile
   float* rowsq;     // rows

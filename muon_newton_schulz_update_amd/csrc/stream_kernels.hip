@@ -334,6 +334,53 @@ __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Input check (MUON_FLAG_CHECK_FINITE), over the momentum pass's tiles: the
+// grad (the polar input), with upd the momentum, and the weight when there
+// is one. Reads only; a NaN or Inf anywhere in a matrix's inputs sets its
+// descriptor's flag (one atomic per wave that saw one).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void ld8_rt(const void* b, int dt, int64_t ld, int r, int c, int n, float v[8]) {
+  const size_t i = (size_t)r * ld + c;
+  if (n == 8 && aligned16(b, ld, dt)) {
+    if (dt == DT_BF16) Ty<__bf16>::cvt(Ty<__bf16>::ld(b, i), v);
+    else Ty<float>::cvt(Ty<float>::ld(b, i), v);
+  } else if (dt == DT_BF16) {
+    ld_part<__bf16>(b, i, n, v);
+  } else {
+    ld_part<float>(b, i, n, v);
+  }
+}
+__global__ __launch_bounds__(256) void k_check_finite(DevMat* __restrict__ mats, LaunchList L, int upd) {
+  int local;
+  DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  const int tr = local / M.n_seg, sg = local % M.n_seg;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = sg * kSegCols + lane * 8;
+  const int r0 = tr * kStreamRows + w * kWaveRows;
+  const int nv = max(0, min(8, M.cols - c));
+  bool ok = true;
+  for (int k = 0; k < kWaveRows; ++k) {
+    const int r = r0 + k;
+    const int n = r < M.rows ? nv : 0;   // n = 0 loads nothing
+    float v[8];
+    ld8_rt(M.g, M.dt_g, M.ld_g, r, c, n, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ok = ok && isfinite(v[e]);
+    if (upd) {
+      ld8_rt(M.m, DT_F32, M.ld_m, r, c, n, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ok = ok && isfinite(v[e]);
+    }
+    if (M.w) {
+      ld8_rt(M.w, M.dt_w, M.ld_w, r, c, n, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ok = ok && isfinite(v[e]);
+    }
+  }
+  if (__any(!ok) && lane == 0) atomicOr(&M.bad, 1);
+}
+
+// ---------------------------------------------------------------------------
 // Norms from the K1 partials, in two launches.
 // Lines: one thread per row (rowsq[r] = sum of the row's segment partials)
 // and, for wide matrices, per column (colsq[c] = sum over row tiles). A
@@ -1278,6 +1325,10 @@ __global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ m
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu,
                                  int nesterov, int sgd, hipStream_t st) {
   LAUNCH(k_momentum_stats, nblk, m, L, nesterov_pass, mu, nesterov, sgd);
+  return hipGetLastError();
+}
+hipError_t launch_check_finite(DevMat* m, LaunchList L, int nblk, int upd, hipStream_t st) {
+  LAUNCH(k_check_finite, nblk, m, L, upd);
   return hipGetLastError();
 }
 hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st) {

@@ -298,6 +298,7 @@ extern "C" const char* muon_status_string(muon_status s) {
     case MUON_ERR_HIP: return "MUON_ERR_HIP";
     case MUON_ERR_NO_DEVICE: return "MUON_ERR_NO_DEVICE";
     case MUON_ERR_TOO_LARGE: return "MUON_ERR_TOO_LARGE";
+    case MUON_ERR_NONFINITE: return "MUON_ERR_NONFINITE";
     default: return "MUON_ERR_UNKNOWN";
   }
 }

@@ -123,7 +123,7 @@ def test_update_validation(lib, case, code):
 @pytest.mark.parametrize("field,value", [
     ("ns_steps", 0), ("ns_steps", 65), ("pp_iterations", -1), ("pp_iterations", 9),
     ("mu", 1.5), ("mu", -0.1), ("nesterov", 2), ("power_steps", 0), ("pp_eps", 0.0),
-    ("target_uw", -1.0), ("flags", 8), ("flags", 0x80000000), ("lr", float("nan")), ("ns_a", float("inf")),
+    ("target_uw", -1.0), ("flags", 16), ("flags", 0x80000000), ("lr", float("nan")), ("ns_a", float("inf")),
 ])
 def test_config_validation(lib, field, value):
     cfg = mu.default_config()

@@ -475,6 +475,70 @@ def test_entry_points_reject_shared_buffers(dev):
         check_update(f"slices[{i}]", gi, mi, wi, M[i], V[i], W[i], mu.default_config(), FP32_TOL)
 
 
+def same_bits(a, b):
+    """Bitwise equality (torch.equal is False wherever a NaN sits)."""
+    it = {2: torch.int16, 4: torch.int32}[a.element_size()]
+    return a.dtype == b.dtype and torch.equal(a.view(it), b.view(it))
+
+
+def test_check_finite_flag(dev):
+    """MUON_FLAG_CHECK_FINITE: a NaN or Inf in any input (grad, momentum or
+    weight of an update; the input of a polar call) makes the call return
+    MUON_ERR_NONFINITE naming the first such matrix, with every caller buffer
+    as it was; the handle stays usable. Clean inputs give the same bits as
+    without the flag. Without the flag a non-finite input reaches only its
+    own matrix: the others keep the bits of a clean run."""
+    say("non-finite input check")
+    shapes = [(300, 700), (640, 257), (256, 256), (33, 517)]
+    base = [gen.custom_matrix(sh, 3100 + i, dev, grad_dtype=torch.bfloat16 if i % 2 else torch.float32,
+                              weight_dtype=torch.bfloat16 if i % 2 else torch.float32)
+            for i, sh in enumerate(shapes)]
+    cfg0 = mu.default_config()
+    cfgc = mu.make_config(flags=mu.MUON_FLAG_CHECK_FINITE)
+    _, _, _, Mr, Vr, Wr = run_update(dev, base, cfg0)
+    _, _, _, Mc, Vc, Wc = run_update(dev, base, cfgc)
+    for i in range(len(shapes)):
+        assert torch.equal(Mc[i], Mr[i]) and torch.equal(Vc[i], Vr[i]) and torch.equal(Wc[i], Wr[i]), i
+    # one bad element per case: (matrix, which input, row, col, value); the
+    # last rows and columns of ragged matrices and a misaligned view included
+    cases = [(1, "g", 639, 256, float("nan")), (0, "m", 0, 0, float("inf")),
+             (3, "w", 32, 516, float("-inf")), (2, "g", 128, 77, float("nan"))]
+    for mi, which, r, c, val in cases:
+        mats = [(g.clone(), m.clone(), w.clone()) for g, m, w in base]
+        k = {"g": 0, "m": 1, "w": 2}[which]
+        mats[mi][k][r, c] = val
+        if mi == 2:   # the grad through a view with a 2-element offset (not 16-byte aligned)
+            pad = torch.zeros((256, 258), device=dev, dtype=mats[2][0].dtype)
+            pad[:, 2:] = mats[2][0]
+            mats[2] = (pad[:, 2:], mats[2][1], mats[2][2])
+        before = [(g.clone(), m.clone(), w.clone()) for g, m, w in mats]
+        V = [torch.full(g.shape, 7.0, device=dev) for g, _, _ in mats]
+        with pytest.raises(mu.LibMuonError) as ei:
+            mu.muon_update([g for g, _, _ in mats], [m for _, m, _ in mats], [w for _, _, w in mats], cfgc,
+                           update_out=V)
+        torch.cuda.synchronize()
+        assert ei.value.status == -8 and f"matrix {mi} " in str(ei.value), (which, str(ei.value))
+        for (g, m, w), (g0, m0, w0), v in zip(mats, before, V):
+            assert same_bits(g, g0) and same_bits(m, m0) and same_bits(w, w0) and bool((v == 7.0).all())
+        say(f"  {which}[{mi}] ({r}, {c}) = {val}: refused, nothing written")
+    # polar input
+    xs = [gen.custom_matrix(sh, 3150 + i, dev)[0] for i, sh in enumerate(shapes[:2])]
+    xs[1][5, 250] = float("nan")
+    outs = [torch.full(x.shape, 3.0, device=dev) for x in xs]
+    with pytest.raises(mu.LibMuonError) as ei:
+        mu.ns_polar(xs, outs, cfg=cfgc)
+    torch.cuda.synchronize()
+    assert ei.value.status == -8 and "matrix 1 " in str(ei.value)
+    assert all(bool((o == 3.0).all()) for o in outs)
+    # the handle still works; without the flag the NaN stays in its matrix
+    mats = [(g.clone(), m.clone(), w.clone()) for g, m, w in base]
+    mats[1][0][10, 10] = float("nan")
+    _, _, _, Mn, Vn, Wn = run_update(dev, mats, cfg0)
+    assert not bool(torch.isfinite(Vn[1]).all())
+    for i in (0, 2, 3):
+        assert torch.equal(Mn[i], Mr[i]) and torch.equal(Vn[i], Vr[i]) and torch.equal(Wn[i], Wr[i]), i
+
+
 def test_update_single_fp32_256x1024(dev):
     say("muon_update single_fp32_256x1024")
     g, m, w = gen.make_matrix(gen.WORKLOADS["single_fp32_256x1024"], 0, dev)
