@@ -355,7 +355,7 @@ def main() -> int:
             "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             # the byte-counter record was taken on the Aurora step's launches
-            "traffic": measured_traffic(a.workload) if a.recipe == "aurora" else None,
+            "traffic": measured_traffic(a.workload) if a.recipe == "aurora" and not a.fp8_gram else None,
             "kernel": "k_ns_gemm (A = XX^T, B' = bA + cA^2 + aI, short-side products, X' = QX launches together)",
             "flops": "algorithmic flops of the products run: symmetric halves once, no padding",
             "algorithmic_tflop_per_step": round(p["gemm_algorithmic_flop"] / a.steps / 1e12, 3),
