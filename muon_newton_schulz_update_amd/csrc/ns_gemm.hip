@@ -378,11 +378,27 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // barrier later). Issuing all of a stage's refill at once, eight 1 KB
   // loads per wave from all eight waves, held waves in load issue while
   // their k-step had 256 cycles of matrix work (3-7 % per product).
+  // With 256-tiles (one workgroup per CU, stages long enough to cover the
+  // latency) the next-barrier stage is split too: its first half in the last
+  // k-step, its second half in k-step 0 of the next stage, the deferred stage
+  // in k-steps 1 and 2 - two loads per k-step throughout (a further 0.8 % on
+  // the 3.8B set). 128-tiles, whose short stages leave less time for that
+  // second half, keep the whole next-barrier stage in the last k-step (the
+  // even split made them 6 % slower).
   // Prologue: operand stages 0 .. S-2 (stage S-1 is the first deferred
-  // half-refill); wait for stage 0, read its first k-step.
+  // refill; with the even split, stage S-2's second half is iteration 0's);
+  // wait for stage 0, read its first k-step.
+  constexpr bool kEven = TILE == 256 && KS == 4;
+  if constexpr (kEven) {
 #pragma unroll
-  for (int o = 0; o < S - 1; ++o) issue(o, o, 0, LPO);
-  wait_vm<(S - 3) * LPO>();
+    for (int o = 0; o < S - 2; ++o) issue(o, o, 0, LPO);
+    issue(S - 2, S - 2, 0, LPO / 2);
+    wait_vm<(S - 4) * LPO + LPO / 2>();
+  } else {
+#pragma unroll
+    for (int o = 0; o < S - 1; ++o) issue(o, o, 0, LPO);
+    wait_vm<(S - 3) * LPO>();
+  }
   ring_barrier();
   read_frags(0, 1, 0, 0);
   // slots of stage k (ps, qs) and of stage k+1 (pn, qn)
@@ -396,7 +412,15 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     const int dslot = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s) {
-      if (s < NDS) {
+      if constexpr (kEven) {
+        // k-step 0: second half of operand stage 2k + S - 2 (slot qn);
+        // k-steps 1, 2: operand stage 2k + S - 1 in halves (slot dslot)
+        if (s == 0) issue(qn, 2 * k + S - 2, LPO / 2, LPO);
+        else issue(dslot, 2 * k + S - 1, (s - 1) * LPO / 2, s * LPO / 2);
+        read_frags(ps, qs, s + 1, (s + 1) & 1);
+        mfmas(s & 1);
+        spread(kReadStep + LPO / 2, LPO / 2);
+      } else if (s < NDS) {
         issue(dslot, 2 * k + S - 1, s * LPO / NDS, (s + 1) * LPO / NDS);
         read_frags(ps, qs, s + 1, (s + 1) & 1);
         mfmas(s & 1);
@@ -422,10 +446,17 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     // 3072-row products). 128-tiles, two workgroups per CU, keep the default.
     if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(2);
     __builtin_amdgcn_sched_barrier(0);
-    issue(ps, 2 * k + S, 0, LPO);
-    read_frags(pn, qn, 0, 0);
-    mfmas(1);
-    spread(LPO + kReadStep, LPO);
+    if constexpr (kEven) {
+      issue(ps, 2 * k + S, 0, LPO / 2);
+      read_frags(pn, qn, 0, 0);
+      mfmas(1);
+      spread(LPO / 2 + kReadStep, LPO / 2);
+    } else {
+      issue(ps, 2 * k + S, 0, LPO);
+      read_frags(pn, qn, 0, 0);
+      mfmas(1);
+      spread(LPO + kReadStep, LPO);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
