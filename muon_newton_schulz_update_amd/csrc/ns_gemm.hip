@@ -35,12 +35,16 @@
 // stage feeds the matrix cores the next stage and half of the one after
 // stream in. A stage is four k-steps; each step's fragments are read between
 // the previous step's MFMAs. The workgroup barrier sits before the last step,
-// so matrix-core work continues across it, and the refill of the two freed
-// slots and the next stage's first fragments are issued between that last
-// step's MFMAs. LDS rows are XOR-swizzled in 16-byte chunks so fragment reads
-// are conflict-free.
+// so matrix-core work continues across it. The two slots it frees are
+// refilled over the following k-steps, a few loads per step between the
+// MFMAs (the schedule is next to the K loop): issuing a whole stage's loads
+// at once held waves in load issue while their step had little matrix work.
+// LDS rows are XOR-swizzled in 16-byte chunks so fragment reads are
+// conflict-free.
 // bf16 runs v_mfma_f32_32x32x16_bf16 (fp32 accumulation); fp32 runs
-// v_mfma_f32_32x32x2f32 on the same tiles.
+// v_mfma_f32_32x32x2f32 on the same tiles; the optional fp8 first Gram runs
+// v_mfma_scale_f32_32x32x64_f8f6f4 on an e4m3 copy of X0 stored in panels of
+// 64 columns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
