@@ -339,6 +339,39 @@ def test_engine_tile_sizes(dev, tile, monkeypatch):
         h.close()
 
 
+def test_engine_layouts_and_tiles_agree_bitwise(dev, monkeypatch):
+    """Every output element's K sum runs inside one wave in the same k
+    order whatever the workgroup layout or tile edge, so the 4-wave
+    128 x 128 layout (MUON_NS_VARIANT=1), forced 256-tiles and forced
+    128-tiles give the default's bits exactly: a check of each refill
+    schedule (the 256-tile one, with four or eight loads per operand and
+    wave, and the 128-tile one) against the others. Rectangular matrices
+    with blocks (s >= 512) and squares, bf16 and fp32, in one update."""
+    say("engine layouts and tile edges agree bitwise")
+    mats = [gen.custom_matrix(sh, 1350 + i, dev, grad_dtype=dt, weight_dtype=dt)
+            for i, (sh, dt) in enumerate([((600, 1300), torch.bfloat16), ((1300, 520), torch.bfloat16),
+                                          ((512, 512), torch.bfloat16), ((300, 700), torch.float32),
+                                          ((520, 1030), torch.float32)])]
+    results = {}
+    for name, env in (("default", {}), ("4-wave 256", {"MUON_NS_VARIANT": "1", "MUON_NS_TILE": "256"}),
+                      ("8-wave 256", {"MUON_NS_TILE": "256"}), ("128", {"MUON_NS_TILE": "128"})):
+        for k in ("MUON_NS_VARIANT", "MUON_NS_TILE"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        h = mu.Handle(dev.index)
+        try:
+            results[name] = run_update(dev, mats, handle=h)[3:]
+        finally:
+            h.close()
+    base = results["default"]
+    for name, res in results.items():
+        for i in range(len(mats)):
+            for a, b in zip(res, base):
+                assert same_bits(a[i], b[i]), (name, i)
+        say(f"  {name}: bitwise equal to the default")
+
+
 @pytest.mark.parametrize("block", [1, 2, 3, 8])
 def test_engine_block_lengths(dev, block, monkeypatch):
     """Rectangular matrices run Newton-Schulz in blocks of iterations on the
