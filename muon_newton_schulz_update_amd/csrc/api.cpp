@@ -208,6 +208,7 @@ struct ProfRec {
   hipEvent_t a, b;
   int cls;  // 0 gemm, 1 stream, 2 aux (prologue, D update)
   double amount, amount2, amount3;
+  int count;  // launches between the two events (consecutive on the stream)
 };
 
 }  // namespace
@@ -610,6 +611,7 @@ struct ProfScope {
     r.amount = amount;
     r.amount2 = amount2;
     r.amount3 = amount3;
+    r.count = 1;
     r.a = pool_event(h);
     r.b = pool_event(h);
     if (!r.a || !r.b) { on = false; return; }
@@ -628,17 +630,17 @@ muon_status drain_profile(muon_handle* h) {
     float ms = 0.f;
     HIP_TRY(h, hipEventElapsedTime(&ms, r.a, r.b));
     if (r.cls == 0) {
-      h->acc.gemm_launches += 1;
+      h->acc.gemm_launches += r.count;
       h->acc.gemm_ms += ms;
       h->acc.gemm_counted_flop += r.amount;
       h->acc.gemm_executed_flop += r.amount2;
       h->acc.gemm_algorithmic_flop += r.amount3;
     } else if (r.cls == 1) {
-      h->acc.stream_launches += 1;
+      h->acc.stream_launches += r.count;
       h->acc.stream_ms += ms;
       h->acc.stream_bytes += r.amount;
     } else {
-      h->acc.aux_launches += 1;
+      h->acc.aux_launches += r.count;
       h->acc.aux_ms += ms;
       h->acc.aux_bytes += r.amount;
     }
@@ -831,39 +833,34 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     CHECK_LAUNCH(h, launch_norms_scalars(D, dev_list(meta, P->permat), P->permat.nblk, cfg.ns_eps, contra ? 1 : 0,
                                          st));
   }
-  // 2. power iteration
+  // 2. power iteration (profiled as one span: its launches are back to back)
   if (contra) {
+    ProfScope ps(h, 1, 0);
+    ps.r.count = 0;
     for (int r = 0; r <= cfg.power_steps; ++r) {
       for (int t = 0; t < 2; ++t) {
         const HostList& F = P->fused[t];
         if (!F.nblk) continue;
-        ProfScope ps(h, 1, el_fused[t]);
+        ps.r.amount += el_fused[t];
+        ps.r.count += 1;
         CHECK_LAUNCH(h, launch_power_fused(t, D, dev_list(meta, F), F.nblk, cfg.power_steps, F.max_cols, st));
       }
       if (P->matvec_w.nblk) {
-        {
-          ProfScope ps(h, 1, el_wide);
-          CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec_w), P->matvec_w.nblk, cfg.power_steps, 0,
-                                              st));
-        }
-        ProfScope ps(h, 1, el_wide);
+        ps.r.amount += 2 * el_wide;
+        ps.r.count += 2;
+        CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec_w), P->matvec_w.nblk, cfg.power_steps, 0,
+                                            st));
         CHECK_LAUNCH(h, launch_power_rmatvec(D, dev_list(meta, P->rmatvec_w), P->rmatvec_w.nblk, cfg.power_steps,
                                              st));
       }
-      {
-        ProfScope ps(h, 1, 0);
-        CHECK_LAUNCH(h, launch_power_wsum(D, dev_list(meta, P->colblk), P->colblk.nblk, cfg.power_steps, st));
-        CHECK_LAUNCH(h, launch_power_normalize(D, dev_list(meta, P->permat), P->permat.nblk, cfg.power_steps, st));
-      }
+      ps.r.count += 2;
+      CHECK_LAUNCH(h, launch_power_wsum(D, dev_list(meta, P->colblk), P->colblk.nblk, cfg.power_steps, st));
+      CHECK_LAUNCH(h, launch_power_normalize(D, dev_list(meta, P->permat), P->permat.nblk, cfg.power_steps, st));
     }
-    {
-      ProfScope ps(h, 1, el_ns);
-      CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec), P->matvec.nblk, cfg.power_steps, 1, st));
-    }
-    {
-      ProfScope ps(h, 1, 0);
-      CHECK_LAUNCH(h, launch_power_sigma(D, dev_list(meta, P->permat), P->permat.nblk, cfg.contra, st));
-    }
+    ps.r.amount += el_ns;
+    ps.r.count += 2;
+    CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec), P->matvec.nblk, cfg.power_steps, 1, st));
+    CHECK_LAUNCH(h, launch_power_sigma(D, dev_list(meta, P->permat), P->permat.nblk, cfg.contra, st));
   }
   // 3. Newton-Schulz passes. Per pass group, block class and type, the
   // iterations run in blocks of r (see ns_gemm.hip): A = X X^T; for each j,
@@ -886,9 +883,17 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         // the first Gram of the pass reads the prologue's fp8 copy of X0 when
         // this class's matrices have one (all or none: bf16 with blocks)
         const bool f8 = c == 1 && t == DT_BF16 && P->fp8;
+        // profiling: one event pair around this class's launches of the pass
+        // (they run back to back on the stream), with their flops and count
+        // summed; a pair per launch cost about 6 us each on the small sets
+        ProfScope ps(h, 0, 0.0, 0.0, 0.0);
+        ps.r.count = 0;
         auto gemm = [&](int li, int mode, int cur, int roles, double counted, int et) -> muon_status {
           const GemmList& G = GL[li];
-          ProfScope ps(h, 0, counted, G.executed, G.algorithmic);
+          ps.r.amount += counted;
+          ps.r.amount2 += G.executed;
+          ps.r.amount3 += G.algorithmic;
+          ps.r.count += 1;
           CHECK_LAUNCH(h, launch_ns_gemm(et, D, (const TileItem*)(meta + G.off), G.n, mode, cur,
                                          roles, cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, G.tile, st));
           return MUON_OK;

@@ -508,6 +508,42 @@ def test_entry_points_reject_shared_buffers(dev):
         check_update(f"slices[{i}]", gi, mi, wi, M[i], V[i], W[i], mu.default_config(), FP32_TOL)
 
 
+def test_profile_counts_and_flops(dev):
+    """The library's own profile (what bench.py's roofline divides): for a
+    256 x 256 bf16 square (one pass of 12 single iterations: GRAM, SQ, BX)
+    and a 600 x 2048 bf16 matrix (two Aurora passes of three 4-iteration
+    blocks: GRAM, 4 SQ, 9 SYM, BX), 36 + 90 engine launches, the algorithmic
+    flops 12 * 4 s^3 and 2 * 3 * (3 s^2 L + 13 s^3), the counted flops
+    (4 s^2 L + 2 s^3 per iteration and pass), positive times, and the
+    streaming bytes of the momentum pass; twice that after a second step."""
+    say("profile counts and flops")
+    mats = [gen.custom_matrix((256, 256), 3300, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16),
+            gen.custom_matrix((600, 2048), 3301, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16)]
+    h = mu.Handle(dev.index)
+    try:
+        h.profile_reset()
+        h.profile_enable(True)
+        run_update(dev, mats, handle=h)
+        p1 = h.profile_read()
+        run_update(dev, mats, handle=h)
+        p2 = h.profile_read()
+        h.profile_enable(False)
+    finally:
+        h.close()
+    sq, s, L = 256.0, 600.0, 2048.0
+    algo = 12 * 4 * sq ** 3 + 2 * 3 * (3 * s * s * L + 13 * s ** 3)
+    counted = 12 * (4 * sq ** 3 + 2 * sq ** 3) + 2 * 12 * (4 * s * s * L + 2 * s ** 3)
+    say(f"  launches {p1['gemm_launches']}, engine {p1['gemm_ms']:.3f} ms, stream {p1['stream_ms']:.3f} ms")
+    assert p1["gemm_launches"] == 36 + 90
+    assert p1["gemm_algorithmic_flop"] == pytest.approx(algo, rel=1e-12)
+    assert p1["gemm_counted_flop"] == pytest.approx(counted, rel=1e-12)
+    assert p1["gemm_ms"] > 0 and p1["stream_ms"] > 0 and p1["aux_ms"] > 0
+    assert p1["stream_bytes"] >= (256 * 256 + 600 * 2048) * (2 + 8 + 2)   # at least the momentum pass
+    assert p2["gemm_launches"] == 2 * p1["gemm_launches"]
+    assert p2["gemm_algorithmic_flop"] == pytest.approx(2 * algo, rel=1e-12)
+    assert p2["stream_bytes"] == pytest.approx(2 * p1["stream_bytes"], rel=1e-12)
+
+
 def same_bits(a, b):
     """Bitwise equality (torch.equal is False wherever a NaN sits)."""
     it = {2: torch.int16, 4: torch.int32}[a.element_size()]
