@@ -47,6 +47,7 @@
 // 64 columns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "muon_device.hpp"
 
@@ -527,6 +528,18 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // tiles.
   const bool diag_sym = mode == GM_SYM && it.tm == it.tn;
   if (diag_sym) write_t = true;
+  // the second product's first slab of A values, requested before the
+  // barrier (the waves that finish their K loop first wait there)
+  constexpr int kSC = NI * 32, kKK = kSC / 16;
+  typename Elem<std::conditional_t<kF8, __bf16, T>>::Raw apre[mode == GM_SQ && sizeof(T) != 1 ? kKK : 1];
+  if constexpr (mode == GM_SQ && sizeof(T) != 1) {
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+      const int q = kk * 64 + lane;
+      const int rr = q / (kSC / 8), c8 = (q % (kSC / 8)) * 8;
+      apre[kk] = Elem<T>::ldraw(M.sq[role_p], (size_t)(row0 + rr) * ldo + col0 + c8);
+    }
+  }
   __syncthreads();   // every wave is done with the slots
   // the fp8 Gram's products carry the square of the operand scale q
   const float oscale = kF8 ? M.scal[SC_F8INV2] : 1.f;
@@ -604,7 +617,9 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   }
   if constexpr (!kF8) {
     // 32-row fp32 slabs; the second product's A values for a slab are loaded
-    // before the slab is staged, so their latency overlaps the staging
+    // before the slab is staged, so their latency overlaps the staging (the
+    // first slab's before the barrier above, where the waves that finished
+    // their K loop early wait anyway: 0.3 % on the 3.8B set)
     float* buf = (float*)(smem + wave * kSlabBytes);
     constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
     constexpr int KK = SC / 16;                // 8-column chunks per lane per slab
@@ -612,8 +627,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     for (int mi = 0; mi < MI; ++mi) {
       typename Elem<T>::Raw araw[mode == GM_SQ ? KK : 1];
       if constexpr (mode == GM_SQ) {
+        static_assert(KK == kKK, "slab chunks");
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
+          if (mi == 0) { araw[kk] = apre[kk]; continue; }
           const int q = kk * 64 + lane;
           const int rr = q / (SC / 8), c8 = (q % (SC / 8)) * 8;
           araw[kk] = Elem<T>::ldraw(M.sq[role_p], (size_t)(row0 + mi * 32 + rr) * ldo + col0 + c8);
