@@ -262,6 +262,25 @@ muon_status muon_check_polar_args(int n, const muon_matrix* in,
                                   char* msg, int msg_len);
 
 /*
+ * Host-only consistency check of the launch plan a compute call would build
+ * for a batch (for tests and for debugging the planner; needs no device).
+ * kind: 0 muon_update, 1 ns_polar, 2 aurora_orthogonalize; only rows, cols
+ * and dtype of `shapes` are read; cfg may be NULL (defaults). It checks that
+ * every workspace region lies inside the workspace and overlaps no other;
+ * that every tile of every Newton-Schulz product list lies inside its
+ * matrix's padded tile grid and sits in the list of that matrix's pass,
+ * block length class and element type; that every tile a product needs is
+ * listed exactly once (the upper triangle of the symmetric products, the
+ * whole grid of X' = Q X); and that the streaming launch lists have
+ * consistent block offsets (the momentum pass's n_rt x n_seg tiles per
+ * matrix). Returns MUON_OK, or MUON_ERR_INVALID_ARG with the first violation
+ * in msg (NUL-terminated, at most msg_len bytes); shapes past the library's
+ * limits give MUON_ERR_SHAPE_MISMATCH.
+ */
+muon_status muon_debug_check_plan(int kind, int n, const muon_matrix* shapes,
+                                  const muon_config* cfg, char* msg, int msg_len);
+
+/*
  * Grow the workspace so that batches with these shapes and types run without
  * any further device allocation (so a timed or captured region allocates
  * nothing). Only rows, cols and dtype of `shapes` are read.

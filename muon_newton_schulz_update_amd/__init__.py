@@ -27,7 +27,7 @@ __all__ = [
     "library_path", "default_config", "classic_config", "momentum_warmup", "make_config", "ns_polar",
     "aurora_orthogonalize", "muon_update", "check_update_args",
     "check_polar_args", "get_handle", "STATUS", "muon_update_static", "MUON_FLAG_SGD_MOMENTUM", "MUON_FLAG_WIDE_ROWS",
-    "MUON_FLAG_FP8_GRAM", "MUON_FLAG_CHECK_FINITE",
+    "MUON_FLAG_FP8_GRAM", "MUON_FLAG_CHECK_FINITE", "debug_check_plan",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -122,6 +122,8 @@ def load_library() -> ctypes.CDLL:
             "muon_check_polar_args": (ctypes.c_int, [ctypes.c_int, P(MuonMatrix), P(MuonMatrix),
                                                      P(MuonConfig), ctypes.c_char_p, ctypes.c_int]),
             "muon_reserve": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, P(MuonMatrix)]),
+            "muon_debug_check_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, P(MuonMatrix), P(MuonConfig),
+                                                     ctypes.c_char_p, ctypes.c_int]),
             "ns_polar": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, P(MuonMatrix),
                                         P(MuonMatrix), P(MuonConfig)]),
             "aurora_orthogonalize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, P(MuonMatrix),
@@ -378,6 +380,19 @@ def check_update_args(grads, momenta, weights=None, update_out=None, cfg=None) -
     rc = lib.muon_check_update_args(len(grads), conv(grads), conv(momenta), conv(weights),
                                     conv(update_out), ctypes.byref(cfg) if cfg is not None else None,
                                     buf, 256)
+    return rc, buf.value.decode()
+
+
+def debug_check_plan(kind: str, shapes, cfg=None) -> tuple[int, str]:
+    """Host-only check of the launch plan for a batch (libmuon
+    `muon_debug_check_plan`; no device needed). kind: "update", "polar" or
+    "aurora"; shapes: (rows, cols, torch dtype) triples."""
+    lib = load_library()
+    descs = [MuonMatrix(None, r, c, c, MUON_BF16 if dt == torch.bfloat16 else MUON_F32) for r, c, dt in shapes]
+    buf = ctypes.create_string_buffer(512)
+    rc = lib.muon_debug_check_plan({"update": 0, "polar": 1, "aurora": 2}[kind], len(descs),
+                                   _array(descs) if descs else None,
+                                   ctypes.byref(cfg) if cfg is not None else None, buf, 512)
     return rc, buf.value.decode()
 
 

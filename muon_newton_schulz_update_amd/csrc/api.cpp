@@ -188,6 +188,7 @@ struct Plan {
   std::vector<DevMat> last_devmat;
   bool devmat_valid = false;
   uint64_t last_use = 0;
+  std::vector<std::pair<size_t, size_t>> regions;   // workspace (offset, bytes) handed out, for the plan check
 };
 
 std::string plan_key(int kind, int pp, bool wide_rows, bool fp8, int block, bool forced, int n,
@@ -296,6 +297,7 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
   auto take = [&](size_t bytes) {
     size_t o = off;
     off = align_up(off + std::max<size_t>(bytes, 1));
+    P->regions.emplace_back(o, bytes);
     return o;
   };
   for (int i = 0; i < n; ++i) {
@@ -953,6 +955,101 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   return MUON_OK;
 }
 
+// Host-only consistency check of a plan (muon_debug_check_plan): every
+// workspace region inside the workspace and disjoint from the others; every
+// product tile in bounds, in the list of its matrix's pass group, block class
+// and type, and every tile a product needs present exactly once; streaming
+// lists with consistent block offsets. Returns an empty string when the plan
+// passes, else the first violation.
+std::string check_plan(const Plan& P) {
+  char buf[256];
+  const int nm = (int)P.mats.size();
+  // workspace regions
+  std::vector<std::pair<size_t, size_t>> rg = P.regions;
+  std::sort(rg.begin(), rg.end());
+  for (size_t i = 0; i < rg.size(); ++i) {
+    if (rg[i].first + rg[i].second > P.ws_bytes) {
+      snprintf(buf, sizeof(buf), "workspace region at %zu (%zu bytes) ends past the workspace (%zu)", rg[i].first,
+               rg[i].second, P.ws_bytes);
+      return buf;
+    }
+    if (i && rg[i - 1].first + rg[i - 1].second > rg[i].first) {
+      snprintf(buf, sizeof(buf), "workspace regions at %zu and %zu overlap", rg[i - 1].first, rg[i].first);
+      return buf;
+    }
+  }
+  // streaming and vector lists: offsets from 0, non-decreasing, ending at nblk
+  auto list_ok = [&](const HostList& L, const char* name) -> std::string {
+    if (L.n == 0) return L.nblk == 0 ? "" : std::string(name) + ": blocks without matrices";
+    const int32_t* off = (const int32_t*)(P.meta_host.data() + L.off_off);
+    const int32_t* mat = (const int32_t*)(P.meta_host.data() + L.off_mat);
+    if (off[0] != 0 || off[L.n] != L.nblk) return std::string(name) + ": block offsets do not span the launch";
+    for (int i = 0; i < L.n; ++i)
+      if (off[i + 1] < off[i] || mat[i] < 0 || mat[i] >= nm) return std::string(name) + ": bad entry";
+    return "";
+  };
+  const std::pair<const HostList*, const char*> lists[] = {
+      {&P.stream, "stream"}, {&P.permat, "permat"}, {&P.lines, "lines"}, {&P.colblk, "colblk"},
+      {&P.matvec, "matvec"}, {&P.ascale, "ascale"}, {&P.fused[0], "fused"}, {&P.fused[1], "fused"},
+      {&P.matvec_w, "matvec_w"}, {&P.rmatvec_w, "rmatvec_w"}, {&P.prologue[0][0], "prologue"},
+      {&P.prologue[0][1], "prologue"}, {&P.prologue[1][0], "prologue"}, {&P.prologue[1][1], "prologue"},
+      {&P.dupdate[0], "dupdate"}, {&P.dupdate[1], "dupdate"}};
+  for (const auto& l : lists) {
+    std::string e = list_ok(*l.first, l.second);
+    if (!e.empty()) return e;
+  }
+  {
+    // the streaming tiles the kernels index: n_rt x n_seg per matrix
+    const int32_t* off = (const int32_t*)(P.meta_host.data() + P.stream.off_off);
+    const int32_t* mat = (const int32_t*)(P.meta_host.data() + P.stream.off_mat);
+    for (int i = 0; i < P.stream.n; ++i) {
+      const MatInfo& m = P.mats[mat[i]];
+      if (off[i + 1] - off[i] != m.n_rt * m.n_seg) return "stream: block count differs from the tile grid";
+    }
+  }
+  // product tile lists
+  for (int g = 0; g < 2; ++g)
+    for (int c = 0; c < 2; ++c)
+      for (int t = 0; t < 2; ++t)
+        for (int li = 0; li < 3; ++li) {
+          const GemmList& G = P.gemm[g][c][t][li];
+          const int tile = G.tile;
+          if (tile != 128 && tile != 256) return "product list with a bad tile edge";
+          std::vector<std::vector<uint8_t>> seen(nm);
+          const TileItem* it = (const TileItem*)(P.meta_host.data() + G.off);
+          for (int k = 0; k < G.n; ++k) {
+            const TileItem& x = it[k];
+            if (x.mat >= nm) return "product tile of an unknown matrix";
+            const MatInfo& m = P.mats[x.mat];
+            if (m.ns_t != t || (m.block > 1) != (c == 1) || (g == 1 && !m.aurora))
+              return "product tile in another class's list";
+            if (m.s_pad % 256 || m.L_pad % 256) return "padded extents not a multiple of 256";
+            const int ts = m.s_pad / tile, tcols = li == LIST_BX ? m.L_pad / tile : ts;
+            if (x.tm >= ts || x.tn >= tcols || (li != LIST_BX && x.tm > x.tn)) {
+              snprintf(buf, sizeof(buf), "tile (%d, %d) of matrix %d outside its %d x %d grid (list %d)", x.tm,
+                       x.tn, m.user, ts, tcols, li);
+              return buf;
+            }
+            if (seen[x.mat].empty()) seen[x.mat].assign((size_t)ts * tcols, 0);
+            if (seen[x.mat][(size_t)x.tm * tcols + x.tn]++) return "product tile listed twice";
+          }
+          for (int i = 0; i < nm; ++i) {
+            const MatInfo& m = P.mats[i];
+            const bool member = m.ns_t == t && (m.block > 1) == (c == 1) && (g == 0 || m.aurora);
+            const int ts = m.s_pad / tile, tcols = li == LIST_BX ? m.L_pad / tile : ts;
+            const size_t need = li == LIST_BX ? (size_t)ts * tcols : (size_t)ts * (ts + 1) / 2;
+            size_t have = 0;
+            for (uint8_t v : seen[i]) have += v;
+            if (member && have != need) {
+              snprintf(buf, sizeof(buf), "matrix %d: %zu of its %zu tiles in list %d", m.user, have, need, li);
+              return buf;
+            }
+            if (!member && have) return "tiles of a matrix that does not take part";
+          }
+        }
+  return "";
+}
+
 muon_config resolve_cfg(const muon_config* cfg) {
   muon_config c;
   if (cfg) c = *cfg; else muon_config_default(&c);
@@ -1033,6 +1130,28 @@ extern "C" muon_status muon_set_stream(muon_handle* h, void* stream) {
 }
 
 extern "C" const char* muon_last_error(const muon_handle* h) { return h ? h->err.c_str() : ""; }
+
+extern "C" muon_status muon_debug_check_plan(int kind, int n, const muon_matrix* shapes, const muon_config* cfg,
+                                             char* msg, int len) {
+  if (msg && len > 0) msg[0] = 0;
+  if (n < 0 || n > kMaxBatch || (n > 0 && !shapes) || kind < 0 || kind > 2) return MUON_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (shapes[i].rows < 0 || shapes[i].cols < 0 || shapes[i].rows > 65536 || shapes[i].cols > 65536 ||
+        std::min(shapes[i].rows, shapes[i].cols) > 16384 ||
+        (shapes[i].dtype != MUON_F32 && shapes[i].dtype != MUON_BF16))
+      return MUON_ERR_SHAPE_MISMATCH;
+  const muon_config c = resolve_cfg(cfg);
+  const int k = kind == 0 ? KIND_UPDATE : kind == 1 ? KIND_NS : KIND_AURORA;
+  const int pp = k == KIND_NS ? 0 : c.pp_iterations;
+  bool forced = false;
+  const int block = rect_block(c, &forced);
+  std::unique_ptr<Plan> P = build_plan(k, pp, (c.flags & MUON_FLAG_WIDE_ROWS) != 0,
+                                       (c.flags & MUON_FLAG_FP8_GRAM) != 0, block, forced, n, shapes);
+  const std::string e = check_plan(*P);
+  if (e.empty()) return MUON_OK;
+  if (msg && len > 0) snprintf(msg, (size_t)len, "%s", e.c_str());
+  return MUON_ERR_INVALID_ARG;
+}
 
 extern "C" muon_status muon_reserve(muon_handle* h, int n, const muon_matrix* shapes) {
   if (!h) return MUON_ERR_INVALID_ARG;
