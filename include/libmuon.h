@@ -224,13 +224,22 @@ const char* muon_version(void);
  * demand and are freed by muon_destroy. Returns MUON_ERR_NO_DEVICE when no
  * gfx950 device is current.
  *
- * Tuning (environment; results are the same up to floating-point rounding):
+ * Tuning (environment). The layout and tile edge give bitwise the default's
+ * results; a forced block length changes the rounding only:
  *   MUON_NS_VARIANT=1      read here: Newton-Schulz products on 256x256 tiles
  *                          with 4 waves of 128x128 instead of 8 of 64x128.
  *   MUON_NS_TILE=128|256   read when a plan is built (first call with a new
  *                          set of shapes): force the product tile edge;
  *                          otherwise launches with fewer than 768 256-tiles
  *                          use 128-tiles.
+ *   MUON_NS_BLOCK=1..8     read when a plan is built: Newton-Schulz
+ *                          iterations per block for every rectangular matrix
+ *                          (default 4 where the coefficients allow, below 512
+ *                          on the short side 1).
+ * Tracing: MUON_ROCTX=1, read here, wraps each phase of a call (momentum,
+ * power iteration, each Newton-Schulz pass, the Aurora D update, the tail)
+ * in a ROCTx range for rocprofv3 --marker-trace; the ROCTx library is loaded
+ * at run time and the ranges are skipped when it is absent.
  */
 muon_status muon_create(muon_handle** handle, void* stream);
 

@@ -19,6 +19,7 @@
 //   -> tail reduce -> tail finalise (Contra, Frobenius restore, aspect, floor)
 //   -> tail apply (update_out, W -= lr V).
 #include <hip/hip_runtime.h>
+#include <dlfcn.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -225,6 +226,10 @@ struct muon_handle {
   uint64_t tick = 0;
   void* pinned = nullptr;
   int32_t* bad_host = nullptr;   // pinned, kMaxBatch flags: the input check's per-matrix results
+  // ROCTx ranges per phase (MUON_ROCTX=1 at handle creation): the SDK's
+  // push/pop, looked up with dlopen so the library has no link dependency
+  int (*rx_push)(const char*) = nullptr;
+  int (*rx_pop)() = nullptr;
   size_t pinned_bytes = 0;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -602,6 +607,18 @@ hipEvent_t pool_event(muon_handle* h) {
   return e;
 }
 
+// A named ROCTx range over a phase of a call (annotates rocprofv3 traces run
+// with --marker-trace); nothing when the handle has no ROCTx.
+struct Range {
+  muon_handle* h;
+  explicit Range(muon_handle* hh, const char* name) : h(hh) {
+    if (h->rx_push) h->rx_push(name);
+  }
+  ~Range() {
+    if (h->rx_push) h->rx_pop();
+  }
+};
+
 struct ProfScope {
   muon_handle* h;
   ProfRec r{};
@@ -824,7 +841,10 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   }
 
   // 1. momentum/Nesterov (or input) + norms
+  Range call_range(h, c.kind == KIND_UPDATE ? "libmuon muon_update" : c.kind == KIND_NS ? "libmuon ns_polar"
+                                                                                  : "libmuon aurora_orthogonalize");
   {
+    Range rg(h, "momentum");
     ProfScope ps(h, 1, b_mom);
     CHECK_LAUNCH(h, launch_momentum_stats(D, dev_list(meta, P->stream), P->stream.nblk, upd ? 1 : 0, cfg.mu,
                                           cfg.nesterov, (cfg.flags & MUON_FLAG_SGD_MOMENTUM) ? 1 : 0, st));
@@ -837,6 +857,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   }
   // 2. power iteration (profiled as one span: its launches are back to back)
   if (contra) {
+    Range rg(h, "power iteration");
     ProfScope ps(h, 1, 0);
     ps.r.count = 0;
     for (int r = 0; r <= cfg.power_steps; ++r) {
@@ -870,6 +891,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   // is the block's last, A <- B'_j (B'_j A); then X' = Q X.
   for (int p = 0; p < P->passes; ++p) {
     const int g = p == 0 ? 0 : 1;
+    Range rg(h, p == 0 ? "Newton-Schulz pass 1" : p == 1 ? "Newton-Schulz pass 2" : "Newton-Schulz pass 3+");
     for (int t = 0; t < 2; ++t) {
       const HostList& L = P->prologue[g][t];
       if (L.nblk == 0) continue;
@@ -925,6 +947,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         }
       }
     if (p + 1 < P->passes) {
+      Range rd(h, "Aurora D update");
       for (int t = 0; t < 2; ++t) {
         const HostList& L = P->dupdate[t];
         if (L.nblk == 0) continue;
@@ -936,6 +959,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     }
   }
   // 4. tail
+  Range rt(h, "tail");
   if (upd) {
     {
       ProfScope ps(h, 1, b_tail_r);
@@ -1092,6 +1116,15 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
     h->static_stage = nullptr;
     muon_destroy(h);
     return MUON_ERR_ALLOC;
+  }
+  if (const char* v = getenv("MUON_ROCTX")) {
+    if (atoi(v) != 0) {
+      if (void* lib = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL)) {
+        h->rx_push = (int (*)(const char*))dlsym(lib, "roctxRangePushA");
+        h->rx_pop = (int (*)())dlsym(lib, "roctxRangePop");
+        if (!h->rx_push || !h->rx_pop) h->rx_push = nullptr, h->rx_pop = nullptr;
+      }
+    }
   }
   if (hipHostMalloc((void**)&h->bad_host, kMaxBatch * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
     (void)hipGetLastError();

@@ -544,6 +544,26 @@ def test_profile_counts_and_flops(dev):
     assert p2["stream_bytes"] == pytest.approx(2 * p1["stream_bytes"], rel=1e-12)
 
 
+def test_roctx_ranges_leave_results_unchanged(dev, monkeypatch):
+    """MUON_ROCTX=1 at handle creation wraps each phase of a call in a ROCTx
+    range (rocprofv3 --marker-trace shows them); the results are the bits
+    of a handle without them."""
+    say("ROCTx phase ranges")
+    mats = [gen.custom_matrix(sh, 3400 + i, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16)
+            for i, sh in enumerate([(600, 2048), (256, 256)])]
+    out = {}
+    for on in ("0", "1"):
+        monkeypatch.setenv("MUON_ROCTX", on)
+        h = mu.Handle(dev.index)
+        try:
+            out[on] = run_update(dev, mats, handle=h)[3:]
+        finally:
+            h.close()
+    for a, b in zip(out["0"], out["1"]):
+        for x, y in zip(a, b):
+            assert same_bits(x, y)
+
+
 def same_bits(a, b):
     """Bitwise equality (torch.equal is False wherever a NaN sits)."""
     it = {2: torch.int16, 4: torch.int32}[a.element_size()]
