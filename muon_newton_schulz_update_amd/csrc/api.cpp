@@ -230,6 +230,7 @@ struct muon_handle {
   // push/pop, looked up with dlopen so the library has no link dependency
   int (*rx_push)(const char*) = nullptr;
   int (*rx_pop)() = nullptr;
+  void* rx_lib = nullptr;
   size_t pinned_bytes = 0;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -1120,6 +1121,7 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
   if (const char* v = getenv("MUON_ROCTX")) {
     if (atoi(v) != 0) {
       if (void* lib = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL)) {
+        h->rx_lib = lib;
         h->rx_push = (int (*)(const char*))dlsym(lib, "roctxRangePushA");
         h->rx_pop = (int (*)())dlsym(lib, "roctxRangePop");
         if (!h->rx_push || !h->rx_pop) h->rx_push = nullptr, h->rx_pop = nullptr;
@@ -1147,6 +1149,7 @@ extern "C" muon_status muon_destroy(muon_handle* h) {
   if (h->static_done) (void)hipEventDestroy(h->static_done);
   if (h->static_stage) (void)hipHostFree(h->static_stage);
   if (h->bad_host) (void)hipHostFree(h->bad_host);
+  if (h->rx_lib) dlclose(h->rx_lib);
   for (auto& r : h->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (auto e : h->ev_pool) (void)hipEventDestroy(e);
   delete h;
