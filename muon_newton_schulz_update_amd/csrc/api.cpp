@@ -48,6 +48,7 @@ hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, in
 hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, float pp_eps, float pp_beta,
                                  hipStream_t st);
 hipError_t launch_aurora_scale(DevMat* m, LaunchList L, int nblk, float ns_eps, hipStream_t st);
+hipError_t launch_aurora_dfinish(DevMat* m, LaunchList L, int nblk, float pp_eps, float pp_beta, hipStream_t st);
 hipError_t launch_power_matvec(const DevMat* m, LaunchList L, int nblk, int steps, int final_pass, hipStream_t st);
 hipError_t launch_power_rmatvec(const DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_fused(int ns_t, const DevMat* m, LaunchList L, int nblk, int steps, int max_cols,
@@ -86,6 +87,8 @@ struct MatInfo {
   int block;                 // Newton-Schulz iterations per block (1 for squares)
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv, wband;
+  bool band_d;               // Aurora on the long side with later passes: D from the last product's band sums
+  size_t o_lsq;
   size_t o_xn, o_x[2], o_xt[2], o_x8, o_sq[SQ_COUNT], o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
       o_pwpart, o_tailpart, o_linepart, o_scal, o_ist;
 };
@@ -178,7 +181,8 @@ struct Plan {
   HostList fused[2];                      // power rounds: fused X^T X v pass, one list per NS type
   HostList matvec_w, rmatvec_w;           // X v + X^T u for matrices wider than kFusedCols
   HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
-  HostList dupdate[2];      // [ns_t]
+  HostList dupdate[2];      // [ns_t]: D update reading the pass's result (matrices equilibrated on the short side)
+  HostList dfinish;         // D update from the last product's band sums (the others)
   GemmList gemm[2][2][2][3];   // [pass group][block class][ns_t][list]
   int block = kDefaultBlock;    // iterations per block of a rectangular matrix
   bool fp8 = false;             // MUON_FLAG_FP8_GRAM: the class-1 bf16 matrices' first Gram is fp8
@@ -364,6 +368,10 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
     m.o_tailpart = take(std::max((size_t)m.n_rt * m.n_seg * 4, (size_t)2 * cdiv(m.L, 4)) * 4);
     // per line block: row-sum total, (D rho)^2 total, largest line norm^2
     m.o_linepart = take((size_t)3 * line_blocks(m.rows, m.cols) * 4);
+    // the D update of a long-side Aurora matrix with passes after the first
+    // takes its line sums from the pass's last product (per 64-row band)
+    m.band_d = m.aurora && !m.eq_short && pp > 1;
+    m.o_lsq = m.band_d ? take((size_t)(m.s_pad / 64) * m.L_pad * 4) : 0;
     m.o_scal = take(SC_COUNT * 4);
     m.o_ist = take(IS_COUNT * 4);
     if (m.aurora) P->any_aurora = true;
@@ -446,11 +454,17 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
   for (int t = 0; t < 2; ++t) {
     std::vector<int> ms, bl;
     for (int i = 0; i < nm; ++i)
-      if (P->mats[i].aurora && P->mats[i].ns_t == t) {
+      if (P->mats[i].aurora && !P->mats[i].band_d && P->mats[i].ns_t == t) {
         ms.push_back(i);   // one wave per equilibrated line, 4 per block
         bl.push_back(cdiv(P->mats[i].eq_short ? P->mats[i].s : P->mats[i].L, 4));
       }
     add_list(meta, P->dupdate[t], ms, bl);
+  }
+  {
+    std::vector<int> ms, bl;
+    for (int i = 0; i < nm; ++i)
+      if (P->mats[i].band_d) { ms.push_back(i); bl.push_back(cdiv(P->mats[i].L, 256)); }   // a thread per line
+    add_list(meta, P->dfinish, ms, bl);
   }
   {
     std::vector<int> ms, bl;
@@ -776,6 +790,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     d.pu = (float*)(ws + m.o_pu); d.pv = (float*)(ws + m.o_pv);
     d.pwpart = (float*)(ws + m.o_pwpart); d.tailpart = (float*)(ws + m.o_tailpart);
     d.linepart = (float*)(ws + m.o_linepart);
+    d.lsq = m.band_d ? (float*)(ws + m.o_lsq) : nullptr;
     d.scal = (float*)(ws + m.o_scal); d.ist = (int32_t*)(ws + m.o_ist);
   }
   if (use_static) {
@@ -803,7 +818,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
 
   // algorithmic byte counts for the profile
   double el_ns = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
-  double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_dup[2] = {0, 0};
+  double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_dup[2] = {0, 0}, b_dfin = 0;
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
     const double el = (double)m.rows * m.cols;
@@ -819,7 +834,8 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     b_pro[0][m.ns_t] += pro;
     if (m.aurora) {
       b_pro[1][m.ns_t] += pro;
-      b_dup[m.ns_t] += (double)m.s * m.L * esz(m.ns_t);   // one read of U
+      if (m.band_d) b_dfin += (double)(m.s_pad / 64) * m.L_pad * 4;   // the band sums
+      else b_dup[m.ns_t] += (double)m.s * m.L * esz(m.ns_t);          // one read of U
     }
   }
   (void)el_all;
@@ -955,6 +971,11 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         ProfScope ps(h, 2, b_dup[t]);
         CHECK_LAUNCH(h, launch_aurora_dupdate(t, D, dev_list(meta, L), L.nblk, cfg.pp_eps, cfg.pp_beta, st));
       }
+      if (P->dfinish.nblk) {
+        ProfScope ps(h, 2, b_dfin);
+        CHECK_LAUNCH(h, launch_aurora_dfinish(D, dev_list(meta, P->dfinish), P->dfinish.nblk, cfg.pp_eps,
+                                              cfg.pp_beta, st));
+      }
       ProfScope ps(h, 2, 0);
       CHECK_LAUNCH(h, launch_aurora_scale(D, dev_list(meta, P->ascale), P->ascale.nblk, cfg.ns_eps, st));
     }
@@ -1018,7 +1039,7 @@ std::string check_plan(const Plan& P) {
       {&P.matvec, "matvec"}, {&P.ascale, "ascale"}, {&P.fused[0], "fused"}, {&P.fused[1], "fused"},
       {&P.matvec_w, "matvec_w"}, {&P.rmatvec_w, "rmatvec_w"}, {&P.prologue[0][0], "prologue"},
       {&P.prologue[0][1], "prologue"}, {&P.prologue[1][0], "prologue"}, {&P.prologue[1][1], "prologue"},
-      {&P.dupdate[0], "dupdate"}, {&P.dupdate[1], "dupdate"}};
+      {&P.dupdate[0], "dupdate"}, {&P.dupdate[1], "dupdate"}, {&P.dfinish, "dfinish"}};
   for (const auto& l : lists) {
     std::string e = list_ok(*l.first, l.second);
     if (!e.empty()) return e;

@@ -117,6 +117,9 @@ struct DevMat {
   float* pv;        // cols : v
   float* pwpart;    // n_rmv x cols : partial w per row band
   float* tailpart;  // n_rt * n_seg * 4 : partial tail sums per streaming tile
+  float* lsq;       // (s_pad / 64) x L_pad, or null: the last product of each non-final Aurora pass of a
+                    // matrix equilibrated on its long side writes, per 64-row band and long-side line
+                    // (a column of X'), the sum of squares of the line's stored entries in that band
   float* linepart;  // 3 * (ceil(rows/256) + (rows < cols ? ceil(cols/256) : 0)): per-block norm
                     // partials of the line sums and the largest line norm^2; reused for the blocks
                     // of ||w||^2

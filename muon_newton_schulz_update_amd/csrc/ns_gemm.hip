@@ -509,9 +509,9 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   if constexpr (mode == GM_BX) {
     out = M.x[cur ^ 1]; outT = M.xt[cur ^ 1]; ldo = Lp; ldt = sp;
     // the last product of a pass writes only the orientation read next: the
-    // D update reads the long-side lines (rows of X'^T; rows of X' when the
-    // wide matrix is equilibrated on its rows), the tail reads the storage
-    // orientation (X'^T for a tall matrix, X' otherwise)
+    // D update reads rows of X' when the wide matrix is equilibrated on its
+    // rows (on the long side it takes the band sums below instead), the tail
+    // reads the storage orientation (X'^T for a tall matrix, X' otherwise)
     write_t = true;
     if (last & 1) {
       if ((last & 2) || !M.aurora) { write_t = M.tall != 0; write_o = !write_t; }   // this matrix's last pass
@@ -521,6 +521,12 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     out = M.sq[role_o]; outT = out; ldo = sp; ldt = sp;
     write_t = it.tm != it.tn;
   }
+  // The last product of a non-final Aurora pass of a matrix equilibrated on
+  // its long side feeds only the D update, which needs each long-side line's
+  // (column of X') sum of squares: it writes those, per 64-row band, from the
+  // values it would store, and stores nothing else.
+  const bool band_sums = mode == GM_BX && (last & 1) && !(last & 2) && M.lsq != nullptr;
+  if (band_sums) write_o = write_t = false;
   // A GM_SYM result is symmetric only in exact arithmetic (C[m][n] and C[n][m]
   // come from different products), so its diagonal tiles keep the upper
   // triangle and write the lower one as its mirror: the stored matrix is then
@@ -572,6 +578,26 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
           *(u32x2_t*)(st + sidx(row, col)) = (u32x2_t){lo, hi};
         }
     wave_lds_sync();
+    if (band_sums) {
+#pragma unroll
+      for (int b = 0; b < TR / 64; ++b)
+#pragma unroll
+        for (int cc = 0; cc < TC; cc += 64) {
+          const int c = cc + lane;
+          float sq = 0.f;
+#pragma unroll
+          for (int ch = 0; ch < 8; ++ch) {
+            const u16x8_t v = *(const u16x8_t*)(st + sidx(64 * b + 8 * ch, c));   // rows 64b+8ch .. +7
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = bf2f(v[e]);
+              sq += x * x;
+            }
+          }
+          M.lsq[(size_t)((row0 + 64 * b) >> 6) * Lp + col0 + c] = sq;
+        }
+      return;
+    }
     // row-major: 8 consecutive columns of one row per lane
     if (write_o) {
 #pragma unroll
@@ -622,6 +648,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     // their K loop early wait anyway: 0.3 % on the 3.8B set)
     float* buf = (float*)(smem + wave * kSlabBytes);
     constexpr int SC = NI * 32;                // staged slab: 32 rows x SC columns
+    float bsq[(SC + 63) / 64];                 // band sums of squares per column (band_sums)
     constexpr int KK = SC / 16;                // 8-column chunks per lane per slab
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -642,6 +669,20 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         for (int r = 0; r < 16; ++r)
           buf[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + ni * 32 + (lane & 31)] = agpr_read(acc[mi][ni][r]);
       wave_lds_sync();
+      if (band_sums) {
+        // two 32-row slabs make a 64-row band
+#pragma unroll
+        for (int cc = 0; cc < SC; cc += 64) {
+          const int c = cc + lane;
+          float sq = 0.f;
+#pragma unroll
+          for (int r = 0; r < 32; ++r) sq += buf[r * kPitch + c] * buf[r * kPitch + c];
+          bsq[cc / 64] = (mi & 1) ? bsq[cc / 64] + sq : sq;
+          if (mi & 1) M.lsq[(size_t)((row0 + mi * 32) >> 6) * Lp + col0 + c] = bsq[cc / 64];
+        }
+        wave_lds_sync();
+        continue;
+      }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int q = kk * 64 + lane;

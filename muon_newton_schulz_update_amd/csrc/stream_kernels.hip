@@ -643,6 +643,40 @@ __global__ __launch_bounds__(256) void k_aurora_dupdate(DevMat* __restrict__ mat
   }
 }
 
+// The D update of a matrix equilibrated on its long side, from the band
+// sums of squares the pass's last product wrote (lsq) instead of a read of
+// the pass's result: one thread per line, bands summed in index order; the
+// same damped update as k_aurora_dupdate and the same per-4-line partials of
+// (D_l rho_l)^2 (sums and maxima) for k_aurora_scale.
+__global__ __launch_bounds__(256) void k_aurora_dfinish(DevMat* __restrict__ mats, LaunchList L, float pp_eps,
+                                                        float pp_beta) {
+  int local;
+  DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  const int l = local * 256 + threadIdx.x;
+  const int nl = M.L, nbands = M.s_pad / 64;
+  float contrib = 0.f;
+  if (l < nl) {
+    float s = 0.f;
+    for (int b = 0; b < nbands; ++b) s += gld<float>(M.lsq + (size_t)b * M.L_pad + l);
+    const float target = (float)M.s / (float)M.L;
+    const float rsq = fmaxf(s, pp_eps * pp_eps);
+    const float d = M.dvec[l] * powf(target / rsq, pp_beta);
+    M.dvec[l] = d;
+    const float y = d * M.rho[l];
+    contrib = y * y;
+  }
+  // lines 4g .. 4g+3 are lanes 4g .. 4g+3 of one wave
+  float sum = contrib + __shfl_xor(contrib, 1, 64);
+  sum += __shfl_xor(sum, 2, 64);
+  float mx = fmaxf(contrib, __shfl_xor(contrib, 1, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  const int nb = (nl + 3) / 4, g = l >> 2;
+  if ((threadIdx.x & 3) == 0 && g < nb) {
+    M.tailpart[g] = sum;
+    M.tailpart[nb + g] = mx;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_aurora_scale(DevMat* __restrict__ mats, LaunchList L, float ns_eps) {
   __shared__ float red[8];
   int local;
@@ -1348,6 +1382,10 @@ hipError_t launch_aurora_dupdate(int ns_t, DevMat* m, LaunchList L, int nblk, fl
                                  hipStream_t st) {
   if (ns_t == DT_BF16) LAUNCH(k_aurora_dupdate<__bf16>, nblk, m, L, pp_eps, pp_beta);
   else LAUNCH(k_aurora_dupdate<float>, nblk, m, L, pp_eps, pp_beta);
+  return hipGetLastError();
+}
+hipError_t launch_aurora_dfinish(DevMat* m, LaunchList L, int nblk, float pp_eps, float pp_beta, hipStream_t st) {
+  LAUNCH(k_aurora_dfinish, nblk, m, L, pp_eps, pp_beta);
   return hipGetLastError();
 }
 hipError_t launch_aurora_scale(DevMat* m, LaunchList L, int nblk, float ns_eps, hipStream_t st) {
