@@ -221,8 +221,12 @@ const char* muon_version(void);
  * Create a handle bound to the current HIP device and to `stream`
  * (a hipStream_t; NULL = the default stream). The stream is borrowed, not
  * owned. The handle owns its device workspace and plan cache; both grow on
- * demand and are freed by muon_destroy. Returns MUON_ERR_NO_DEVICE when no
- * gfx950 device is current.
+ * demand and are freed by muon_destroy. It also owns a second stream of
+ * default priority: on sets whose product launches are small, a call runs
+ * the first Newton-Schulz pass of its one-iteration matrices there, beside
+ * the other matrices' pass, and `stream` waits for it before the pass ends,
+ * so every call still completes in order on `stream`. Returns
+ * MUON_ERR_NO_DEVICE when no gfx950 device is current.
  *
  * Tuning (environment). The layout and tile edge give bitwise the default's
  * results; a forced block length changes the rounding only:
@@ -236,6 +240,10 @@ const char* muon_version(void);
  *                          iterations per block for every rectangular matrix
  *                          (default 4 where the coefficients allow, below 512
  *                          on the short side 1).
+ *   MUON_NS_SIDE=0|1       read here: 0 keeps every launch on `stream`, 1
+ *                          uses the second stream whenever a call has both
+ *                          one-iteration and block matrices (bitwise the
+ *                          same results either way).
  * Tracing: MUON_ROCTX=1, read here, wraps each phase of a call (momentum,
  * power iteration, each Newton-Schulz pass, the Aurora D update, the tail)
  * in a ROCTx range for rocprofv3 --marker-trace; the ROCTx library is loaded

@@ -185,6 +185,10 @@ struct Plan {
   HostList dfinish;         // D update from the last product's band sums (the others)
   GemmList gemm[2][2][2][3];   // [pass group][block class][ns_t][list]
   int block = kDefaultBlock;    // iterations per block of a rectangular matrix
+  // The first pass's two block classes are independent chains of launches:
+  // two_chains when both have matrices, side when the second stream pays
+  // (every class-1 product launch under kSmallLaunchTiles 256-tiles)
+  bool two_chains = false, side = false;
   bool fp8 = false;             // MUON_FLAG_FP8_GRAM: the class-1 bf16 matrices' first Gram is fp8
   // device meta: DevMat array followed by the list arrays
   std::vector<uint8_t> meta_host;  // list part (static)
@@ -224,6 +228,12 @@ struct muon_handle {
   int device = 0;
   int ns_variant = 0;        // Newton-Schulz tile layout (MUON_NS_VARIANT; 0 = 8 waves, 1 = 4 waves)
   hipStream_t stream = nullptr;
+  // second stream (default priority, non-blocking) for the first pass's
+  // one-iteration class when the plan runs it beside the other class;
+  // MUON_NS_SIDE (read at creation): 0 never, 1 whenever both classes exist
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  int side_mode = -1;
   void* ws = nullptr;
   size_t ws_bytes = 0;
   std::map<std::string, std::unique_ptr<muon::Plan>> plans;
@@ -532,6 +542,25 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
           }
           add_gemm(meta, G, items);
         }
+  // Small sets: their launches fill a round of the CUs or less, and the
+  // one-iteration class on a second stream fills the other class's partial
+  // rounds and launch gaps (GPT-2-124M set 6.25 -> 5.96 ms, one 3.8B layer
+  // -0.4 %). With launches of many rounds there is nothing to fill and the
+  // two chains' operand panels share the L2s (3.8B set +2.8 %), so those
+  // stay on one stream.
+  bool c0 = false, c1 = false, c1_small = true;
+  for (int t = 0; t < 2; ++t) {
+    c0 = c0 || P->gemm[0][0][t][LIST_GRAM].n > 0;
+    for (int li = 0; li < 3; ++li) {
+      const GemmList& G = P->gemm[0][1][t][li];
+      if (G.n == 0) continue;
+      c1 = true;
+      const double per256 = (double)G.tile * G.tile / ((double)kTile * kTile);
+      c1_small = c1_small && G.n * per256 < kSmallLaunchTiles;
+    }
+  }
+  P->two_chains = c0 && c1;
+  P->side = P->two_chains && c1_small;
   return P;
 }
 
@@ -638,8 +667,9 @@ struct ProfScope {
   muon_handle* h;
   ProfRec r{};
   bool on;
-  ProfScope(muon_handle* hh, int cls, double amount, double amount2 = 0, double amount3 = 0)
-      : h(hh), on(hh->prof && !hh->in_static) {
+  hipStream_t s;   // the stream the bracketed launches go to
+  ProfScope(muon_handle* hh, int cls, double amount, double amount2 = 0, double amount3 = 0, bool on_side = false)
+      : h(hh), on(hh->prof && !hh->in_static), s(on_side ? hh->side : hh->stream) {
     if (!on) return;
     r.cls = cls;
     r.amount = amount;
@@ -649,11 +679,11 @@ struct ProfScope {
     r.a = pool_event(h);
     r.b = pool_event(h);
     if (!r.a || !r.b) { on = false; return; }
-    (void)hipEventRecord(r.a, h->stream);
+    (void)hipEventRecord(r.a, s);
   }
   ~ProfScope() {
     if (!on) return;
-    (void)hipEventRecord(r.b, h->stream);
+    (void)hipEventRecord(r.b, s);
     h->recs.push_back(r);
   }
 };
@@ -906,6 +936,25 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   // iterations run in blocks of r (see ns_gemm.hip): A = X X^T; for each j,
   // B'_j = a I + b A + c A^2 (into Q0 when j = 0), Q <- B'_j Q, and unless j
   // is the block's last, A <- B'_j (B'_j A); then X' = Q X.
+  // When the plan runs the first pass's one-iteration class on the second
+  // stream, that stream waits for everything enqueued so far, and the call's
+  // stream waits for it at the end of the pass (before the D update, which
+  // may read class-0 matrices; on an early error return too).
+  const bool fork = !h->in_static && h->side &&
+                    (h->side_mode == 1 ? P->two_chains : h->side_mode != 0 && P->side);
+  struct SideJoin {
+    muon_handle* h;
+    hipStream_t st;
+    bool pending = false;
+    hipError_t join() {
+      pending = false;
+      hipError_t e = hipEventRecord(h->join_ev, h->side);
+      return e != hipSuccess ? e : hipStreamWaitEvent(st, h->join_ev, 0);
+    }
+    ~SideJoin() {
+      if (pending) (void)join();
+    }
+  } side_join{h, st};
   for (int p = 0; p < P->passes; ++p) {
     const int g = p == 0 ? 0 : 1;
     Range rg(h, p == 0 ? "Newton-Schulz pass 1" : p == 1 ? "Newton-Schulz pass 2" : "Newton-Schulz pass 3+");
@@ -916,10 +965,17 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
       CHECK_LAUNCH(h, launch_prologue(t, D, dev_list(meta, L), L.nblk, upd ? 1 : 0, st));
     }
     const int last_pass = p + 1 == P->passes ? NS_LAST_PASS : 0;
+    if (fork && p == 0) {
+      HIP_TRY(h, hipEventRecord(h->fork_ev, st));
+      HIP_TRY(h, hipStreamWaitEvent(h->side, h->fork_ev, 0));
+      side_join.pending = true;
+    }
     for (int c = 0; c < 2; ++c)
       for (int t = 0; t < 2; ++t) {
         const GemmList* GL = P->gemm[g][c][t];
         if (GL[LIST_GRAM].n == 0) continue;
+        const bool on_side = fork && p == 0 && c == 0;
+        const hipStream_t cs = on_side ? h->side : st;
         const int r = c == 0 ? 1 : P->block;
         // the first Gram of the pass reads the prologue's fp8 copy of X0 when
         // this class's matrices have one (all or none: bf16 with blocks)
@@ -927,7 +983,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         // profiling: one event pair around this class's launches of the pass
         // (they run back to back on the stream), with their flops and count
         // summed; a pair per launch cost about 6 us each on the small sets
-        ProfScope ps(h, 0, 0.0, 0.0, 0.0);
+        ProfScope ps(h, 0, 0.0, 0.0, 0.0, on_side);
         ps.r.count = 0;
         auto gemm = [&](int li, int mode, int cur, int roles, double counted, int et) -> muon_status {
           const GemmList& G = GL[li];
@@ -936,7 +992,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
           ps.r.amount3 += G.algorithmic;
           ps.r.count += 1;
           CHECK_LAUNCH(h, launch_ns_gemm(et, D, (const TileItem*)(meta + G.off), G.n, mode, cur,
-                                         roles, cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, G.tile, st));
+                                         roles, cfg.ns_a, cfg.ns_b, cfg.ns_c, h->ns_variant, G.tile, cs));
           return MUON_OK;
         };
         int cur = 0;
@@ -963,6 +1019,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
           if (e) return e;
         }
       }
+    if (side_join.pending) HIP_TRY(h, side_join.join());
     if (p + 1 < P->passes) {
       Range rd(h, "Aurora D update");
       for (int t = 0; t < 2; ++t) {
@@ -1120,6 +1177,7 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
   h->device = dev;
   h->stream = (hipStream_t)stream;
   if (const char* v = getenv("MUON_NS_VARIANT")) h->ns_variant = atoi(v) == 1 ? 1 : 0;
+  if (const char* v = getenv("MUON_NS_SIDE")) h->side_mode = atoi(v) == 0 ? 0 : 1;
   if (hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming) != hipSuccess) {
     (void)hipGetLastError();
     delete h;
@@ -1155,6 +1213,15 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
     muon_destroy(h);
     return MUON_ERR_ALLOC;
   }
+  // the second stream of small sets (default priority; non-blocking, so it
+  // never waits on the legacy null stream except through the call's events)
+  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    muon_destroy(h);
+    return MUON_ERR_HIP;
+  }
   *out = h;
   return MUON_OK;
 }
@@ -1171,6 +1238,12 @@ extern "C" muon_status muon_destroy(muon_handle* h) {
   if (h->static_stage) (void)hipHostFree(h->static_stage);
   if (h->bad_host) (void)hipHostFree(h->bad_host);
   if (h->rx_lib) dlclose(h->rx_lib);
+  if (h->side) {
+    (void)hipStreamSynchronize(h->side);
+    (void)hipStreamDestroy(h->side);
+  }
+  if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
+  if (h->join_ev) (void)hipEventDestroy(h->join_ev);
   for (auto& r : h->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (auto e : h->ev_pool) (void)hipEventDestroy(e);
   delete h;
