@@ -223,9 +223,10 @@ const char* muon_version(void);
  * owned. The handle owns its device workspace and plan cache; both grow on
  * demand and are freed by muon_destroy. It also owns a second stream of
  * default priority: on sets whose product launches are small, a call runs
- * the first Newton-Schulz pass of its one-iteration matrices there, beside
- * the other matrices' pass, and `stream` waits for it before the pass ends,
- * so every call still completes in order on `stream`. Returns
+ * part of each Newton-Schulz pass there (the one-iteration matrices beside
+ * the blocked ones, or half of a set with only one kind), and `stream`
+ * waits for it before the pass ends, so every call still completes in order
+ * on `stream`. Returns
  * MUON_ERR_NO_DEVICE when no gfx950 device is current.
  *
  * Tuning (environment). The layout and tile edge give bitwise the default's
@@ -241,9 +242,9 @@ const char* muon_version(void);
  *                          (default 4 where the coefficients allow, below 512
  *                          on the short side 1).
  *   MUON_NS_SIDE=0|1       read here: 0 keeps every launch on `stream`, 1
- *                          uses the second stream whenever a call has both
- *                          one-iteration and block matrices (bitwise the
- *                          same results either way).
+ *                          uses the second stream in every pass that has
+ *                          both one-iteration and blocked matrices, however
+ *                          large (bitwise the same results either way).
  * Tracing: MUON_ROCTX=1, read here, wraps each phase of a call (momentum,
  * power iteration, each Newton-Schulz pass, the Aurora D update, the tail)
  * in a ROCTx range for rocprofv3 --marker-trace; the ROCTx library is loaded

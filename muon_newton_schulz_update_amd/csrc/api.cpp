@@ -85,6 +85,7 @@ struct MatInfo {
   bool tall, square, aurora, eq_short;
   bool f8;                   // the first Gram of each pass on fp8 operands (MUON_FLAG_FP8_GRAM)
   int block;                 // Newton-Schulz iterations per block (1 for squares)
+  int chain;                 // launch chain of the Newton-Schulz passes (0 or 1; see build_plan)
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv, wband;
   bool band_d;               // Aurora on the long side with later passes: D from the last product's band sums
@@ -116,10 +117,6 @@ constexpr int kBlockMinShort = 512;
 inline bool fused_power(const MatInfo& m) {
   return m.cols <= kFusedCols && ((size_t)m.cols * (m.ns_t == DT_BF16 ? 2 : 4)) % 16 == 0;
 }
-
-// Matrices of one pass group launch together when they share a block length:
-// class 0 holds the one-iteration blocks, class 1 the longer ones.
-inline int block_class(const MatInfo& m) { return m.block > 1 ? 1 : 0; }
 
 // Block length for the rectangular matrices of a call (see kDefaultBlock);
 // *forced is set when MUON_NS_BLOCK gives it.
@@ -185,9 +182,12 @@ struct Plan {
   HostList dfinish;         // D update from the last product's band sums (the others)
   GemmList gemm[2][2][2][3];   // [pass group][block class][ns_t][list]
   int block = kDefaultBlock;    // iterations per block of a rectangular matrix
-  // The first pass's two block classes are independent chains of launches:
-  // two_chains when both have matrices, side when the second stream pays
-  // (every class-1 product launch under kSmallLaunchTiles 256-tiles)
+  // The Newton-Schulz passes run as two chains of launches, independent of
+  // each other (see build_plan): chain_block[c] iterations per block in
+  // chain c; two_chains when both have matrices in the first pass, side when
+  // the second stream pays (every chain-1 product launch under
+  // kSmallLaunchTiles 256-tiles)
+  int chain_block[2] = {1, kDefaultBlock};
   bool two_chains = false, side = false;
   bool fp8 = false;             // MUON_FLAG_FP8_GRAM: the class-1 bf16 matrices' first Gram is fp8
   // device meta: DevMat array followed by the list arrays
@@ -308,7 +308,7 @@ void add_gemm(std::vector<uint8_t>& meta, GemmList& G, std::vector<TileItem>& it
 // caller pointers, strides, weights and outputs go into the per-call
 // descriptors.
 std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int block, bool forced, int n,
-                                 const muon_matrix* in) {
+                                 const muon_matrix* in, bool may_split) {
   auto P = std::make_unique<Plan>();
   P->kind = kind;
   P->block = block;
@@ -389,6 +389,48 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
   }
   P->ws_bytes = off;
   P->passes = P->any_aurora ? pp : 1;
+
+  // Chains. The one-iteration matrices (chain 0) and those with blocks
+  // (chain 1) never read each other's results inside a pass, so the two
+  // chains' launches may run side by side (on the second stream, when the
+  // launches are small; see two_chains and side below). A call with only
+  // one of the two kinds and small launches is split into two chains of
+  // about equal work (largest first, each to the lighter chain) when the
+  // second stream may be used.
+  P->chain_block[0] = 1;
+  P->chain_block[1] = block;
+  bool has[2] = {false, false};
+  long n256[2] = {0, 0};   // the widest list of each kind, in 256-tiles
+  for (int c = 0; c < 2; ++c) {
+    long lists[2][3] = {};
+    for (auto& m : P->mats) {
+      if ((m.block > 1 ? 1 : 0) != c) continue;
+      has[c] = true;
+      const long ts = m.s_pad / kTile, tl = m.L_pad / kTile;
+      lists[m.ns_t][LIST_GRAM] += ts * (ts + 1) / 2;
+      lists[m.ns_t][LIST_SQ] += ts * (ts + 1) / 2;
+      lists[m.ns_t][LIST_BX] += ts * tl;
+    }
+    for (int t = 0; t < 2; ++t)
+      for (int li = 0; li < 3; ++li) n256[c] = std::max(n256[c], lists[t][li]);
+  }
+  for (auto& m : P->mats) m.chain = m.block > 1 ? 1 : 0;
+  if (may_split && has[0] != has[1] && P->mats.size() >= 2) {
+    const int c = has[1] ? 1 : 0;
+    if (n256[c] < kSmallLaunchTiles) {
+      P->chain_block[0] = P->chain_block[1] = c == 1 ? block : 1;
+      std::vector<int> order(P->mats.size());
+      for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+      auto cost = [&](int i) { return (double)P->mats[i].s_pad * P->mats[i].s_pad * P->mats[i].L_pad; };
+      std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost(a) > cost(b); });
+      double load[2] = {0.0, 0.0};
+      for (int i : order) {
+        const int k = load[0] <= load[1] ? 0 : 1;
+        P->mats[i].chain = k;
+        load[k] += cost(i);
+      }
+    }
+  }
 
   const int nm = (int)P->mats.size();
   std::vector<uint8_t>& meta = P->meta_host;
@@ -496,7 +538,7 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
           std::vector<int> order;
           for (int i = 0; i < nm; ++i) {
             const MatInfo& m = P->mats[i];
-            if (m.ns_t != t || (g == 1 && !m.aurora) || block_class(m) != c) continue;
+            if (m.ns_t != t || (g == 1 && !m.aurora) || m.chain != c) continue;
             order.push_back(i);
           }
           auto kdim = [&](int i) {
@@ -542,12 +584,11 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
           }
           add_gemm(meta, G, items);
         }
-  // Small sets: their launches fill a round of the CUs or less, and the
-  // one-iteration class on a second stream fills the other class's partial
-  // rounds and launch gaps (GPT-2-124M set 6.25 -> 5.96 ms, one 3.8B layer
-  // -0.4 %). With launches of many rounds there is nothing to fill and the
-  // two chains' operand panels share the L2s (3.8B set +2.8 %), so those
-  // stay on one stream.
+  // Small sets: their launches fill a round of the CUs or less, and chain 0
+  // on a second stream fills chain 1's partial rounds and launch gaps
+  // (GPT-2-124M set 6.25 -> 5.96 ms, one 3.8B layer -0.4 %). With launches
+  // of many rounds there is nothing to fill and the two chains' operand
+  // panels share the L2s (3.8B set +2.8 %), so those stay on one stream.
   bool c0 = false, c1 = false, c1_small = true;
   for (int t = 0; t < 2; ++t) {
     c0 = c0 || P->gemm[0][0][t][LIST_GRAM].n > 0;
@@ -756,7 +797,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
       if (victim->second->meta_dev) HIP_TRY(h, hipFree(victim->second->meta_dev));
       h->plans.erase(victim);
     }
-    auto p = build_plan(c.kind, pp, wide_rows, fp8, block, forced, c.n, c.in);
+    auto p = build_plan(c.kind, pp, wide_rows, fp8, block, forced, c.n, c.in, h->side_mode != 0);
     P = p.get();
     h->plans.emplace(key, std::move(p));
   } else {
@@ -936,12 +977,15 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   // iterations run in blocks of r (see ns_gemm.hip): A = X X^T; for each j,
   // B'_j = a I + b A + c A^2 (into Q0 when j = 0), Q <- B'_j Q, and unless j
   // is the block's last, A <- B'_j (B'_j A); then X' = Q X.
-  // When the plan runs the first pass's one-iteration class on the second
-  // stream, that stream waits for everything enqueued so far, and the call's
-  // stream waits for it at the end of the pass (before the D update, which
-  // may read class-0 matrices; on an early error return too).
+  // When the plan runs chain 0 on the second stream (in each pass where both
+  // chains have matrices), that stream waits for everything enqueued so far,
+  // and the call's stream waits for it at the end of the pass (before the D
+  // update, which may read chain-0 matrices; on an early error return too).
   const bool fork = !h->in_static && h->side &&
                     (h->side_mode == 1 ? P->two_chains : h->side_mode != 0 && P->side);
+  auto chain_has = [&](int g, int c) {
+    return P->gemm[g][c][0][LIST_GRAM].n > 0 || P->gemm[g][c][1][LIST_GRAM].n > 0;
+  };
   struct SideJoin {
     muon_handle* h;
     hipStream_t st;
@@ -965,7 +1009,8 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
       CHECK_LAUNCH(h, launch_prologue(t, D, dev_list(meta, L), L.nblk, upd ? 1 : 0, st));
     }
     const int last_pass = p + 1 == P->passes ? NS_LAST_PASS : 0;
-    if (fork && p == 0) {
+    const bool fork_p = fork && chain_has(g, 0) && chain_has(g, 1);
+    if (fork_p) {
       HIP_TRY(h, hipEventRecord(h->fork_ev, st));
       HIP_TRY(h, hipStreamWaitEvent(h->side, h->fork_ev, 0));
       side_join.pending = true;
@@ -974,12 +1019,12 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
       for (int t = 0; t < 2; ++t) {
         const GemmList* GL = P->gemm[g][c][t];
         if (GL[LIST_GRAM].n == 0) continue;
-        const bool on_side = fork && p == 0 && c == 0;
+        const bool on_side = fork_p && c == 0;
         const hipStream_t cs = on_side ? h->side : st;
-        const int r = c == 0 ? 1 : P->block;
+        const int r = P->chain_block[c];
         // the first Gram of the pass reads the prologue's fp8 copy of X0 when
-        // this class's matrices have one (all or none: bf16 with blocks)
-        const bool f8 = c == 1 && t == DT_BF16 && P->fp8;
+        // this chain's matrices have one (all or none: bf16 with blocks)
+        const bool f8 = r > 1 && t == DT_BF16 && P->fp8;
         // profiling: one event pair around this class's launches of the pass
         // (they run back to back on the stream), with their flops and count
         // summed; a pair per launch cost about 6 us each on the small sets
@@ -1110,6 +1155,11 @@ std::string check_plan(const Plan& P) {
       if (off[i + 1] - off[i] != m.n_rt * m.n_seg) return "stream: block count differs from the tile grid";
     }
   }
+  // chains: every matrix in one, with that chain's block length (its launches
+  // run that many iterations per block for all their matrices)
+  for (const MatInfo& m : P.mats)
+    if ((m.chain != 0 && m.chain != 1) || m.block != P.chain_block[m.chain])
+      return "matrix in a chain of another block length";
   // product tile lists
   for (int g = 0; g < 2; ++g)
     for (int c = 0; c < 2; ++c)
@@ -1124,8 +1174,8 @@ std::string check_plan(const Plan& P) {
             const TileItem& x = it[k];
             if (x.mat >= nm) return "product tile of an unknown matrix";
             const MatInfo& m = P.mats[x.mat];
-            if (m.ns_t != t || (m.block > 1) != (c == 1) || (g == 1 && !m.aurora))
-              return "product tile in another class's list";
+            if (m.ns_t != t || m.chain != c || (g == 1 && !m.aurora))
+              return "product tile in another chain's list";
             if (m.s_pad % 256 || m.L_pad % 256) return "padded extents not a multiple of 256";
             const int ts = m.s_pad / tile, tcols = li == LIST_BX ? m.L_pad / tile : ts;
             if (x.tm >= ts || x.tn >= tcols || (li != LIST_BX && x.tm > x.tn)) {
@@ -1138,7 +1188,7 @@ std::string check_plan(const Plan& P) {
           }
           for (int i = 0; i < nm; ++i) {
             const MatInfo& m = P.mats[i];
-            const bool member = m.ns_t == t && (m.block > 1) == (c == 1) && (g == 0 || m.aurora);
+            const bool member = m.ns_t == t && m.chain == c && (g == 0 || m.aurora);
             const int ts = m.s_pad / tile, tcols = li == LIST_BX ? m.L_pad / tile : ts;
             const size_t need = li == LIST_BX ? (size_t)ts * tcols : (size_t)ts * (ts + 1) / 2;
             size_t have = 0;
@@ -1276,7 +1326,7 @@ extern "C" muon_status muon_debug_check_plan(int kind, int n, const muon_matrix*
   bool forced = false;
   const int block = rect_block(c, &forced);
   std::unique_ptr<Plan> P = build_plan(k, pp, (c.flags & MUON_FLAG_WIDE_ROWS) != 0,
-                                       (c.flags & MUON_FLAG_FP8_GRAM) != 0, block, forced, n, shapes);
+                                       (c.flags & MUON_FLAG_FP8_GRAM) != 0, block, forced, n, shapes, true);
   const std::string e = check_plan(*P);
   if (e.empty()) return MUON_OK;
   if (msg && len > 0) snprintf(msg, (size_t)len, "%s", e.c_str());
@@ -1298,7 +1348,7 @@ extern "C" muon_status muon_reserve(muon_handle* h, int n, const muon_matrix* sh
     muon_config dflt;
     muon_config_default(&dflt);
     const int block = rect_block(dflt, &forced);
-    auto P = build_plan(kind, 2, false, false, block, forced, n, shapes);
+    auto P = build_plan(kind, 2, false, false, block, forced, n, shapes, true);
     need = std::max(need, P->ws_bytes);
   }
   return ensure_workspace(h, need);

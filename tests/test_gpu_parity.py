@@ -373,49 +373,57 @@ def test_engine_layouts_and_tiles_agree_bitwise(dev, monkeypatch):
 
 
 def test_side_stream_matches_one_stream(dev, monkeypatch):
-    """On small sets the first pass's one-iteration class (squares, and
-    rectangular matrices whose short side is under 512, which carry Aurora
-    and so feed the D update after the pass) runs on the handle's second
-    stream beside the block class, and the call's stream waits for it at
-    the end of the pass. Two calls in a row (the fork and join events are
-    reused, the second call reads the first one's momenta and weights) give
-    the one-stream bits (MUON_NS_SIDE=0) exactly, by default and with the
-    second stream forced on; the default's second step is checked against
-    the oracle too."""
+    """On small sets the Newton-Schulz passes run as two chains of launches
+    on two streams: the one-iteration matrices (squares, and rectangular
+    matrices whose short side is under 512, which carry Aurora and so feed
+    the D update after the pass) beside those with blocks, or, in a call
+    with only one of the two kinds, two halves of it (here: squares only,
+    and blocked rectangles only, whose second Aurora pass forks too). The
+    call's stream waits for the second one at the end of each pass. Two
+    calls in a row (the fork and join events are reused, the second call
+    reads the first one's momenta and weights) give the one-stream bits
+    (MUON_NS_SIDE=0, no split) exactly, by default and with the second
+    stream forced on; the default's second step is checked against the
+    oracle too."""
     say("second stream of small sets against one stream")
-    mats = [gen.custom_matrix(sh, 1380 + i, dev, grad_dtype=dt, weight_dtype=dt)
-            for i, (sh, dt) in enumerate([((600, 1300), torch.bfloat16), ((768, 768), torch.bfloat16),
-                                          ((300, 700), torch.bfloat16), ((700, 300), torch.float32),
-                                          ((520, 1030), torch.float32), ((256, 256), torch.float32)])]
-    results = {}
-    for name, env in (("one stream", "0"), ("default", None), ("forced", "1")):
-        monkeypatch.delenv("MUON_NS_SIDE", raising=False)
-        if env is not None:
-            monkeypatch.setenv("MUON_NS_SIDE", env)
-        h = mu.Handle(dev.index)
-        try:
-            G = [g for g, _, _ in mats]
-            M = [m.clone() for _, m, _ in mats]
-            W = [w.clone() for _, _, w in mats]
-            V = [torch.empty(g.shape, device=dev) for g in G]
-            mu.muon_update(G, M, W, mu.default_config(), update_out=V, handle=h)
-            M1 = [m.clone() for m in M]
-            W1 = [w.clone() for w in W]
-            mu.muon_update(G, M, W, mu.default_config(), update_out=V, handle=h)
-            torch.cuda.synchronize()
-            results[name] = (M1, W1, M, W, V)
-        finally:
-            h.close()
-    base = results["one stream"]
-    for name, res in results.items():
-        for a, b in zip(res, base):
-            for i in range(len(mats)):
-                assert same_bits(a[i], b[i]), (name, i)
-        say(f"  {name}: bitwise equal to one stream over two calls")
-    M1, W1, M, W, V = results["default"]
-    for i, (g, _, _) in enumerate(mats):
-        tol = BF16_TOL if g.dtype == torch.bfloat16 else FP32_TOL
-        check_update(f"side[{i}]", g, M1[i], W1[i], M[i], V[i], W[i], mu.default_config(), tol)
+    batches = {
+        "mixed": [((600, 1300), torch.bfloat16), ((768, 768), torch.bfloat16), ((300, 700), torch.bfloat16),
+                  ((700, 300), torch.float32), ((520, 1030), torch.float32), ((256, 256), torch.float32)],
+        "squares": [((768, 768), torch.bfloat16)] * 5 + [((512, 512), torch.float32)] * 2,
+        "blocked": [((600, 1300), torch.bfloat16), ((1300, 600), torch.bfloat16), ((768, 2304), torch.bfloat16)],
+    }
+    for bname, spec in batches.items():
+        mats = [gen.custom_matrix(sh, 1380 + 10 * len(bname) + i, dev, grad_dtype=dt, weight_dtype=dt)
+                for i, (sh, dt) in enumerate(spec)]
+        results = {}
+        for name, env in (("one stream", "0"), ("default", None), ("forced", "1")):
+            monkeypatch.delenv("MUON_NS_SIDE", raising=False)
+            if env is not None:
+                monkeypatch.setenv("MUON_NS_SIDE", env)
+            h = mu.Handle(dev.index)
+            try:
+                G = [g for g, _, _ in mats]
+                M = [m.clone() for _, m, _ in mats]
+                W = [w.clone() for _, _, w in mats]
+                V = [torch.empty(g.shape, device=dev) for g in G]
+                mu.muon_update(G, M, W, mu.default_config(), update_out=V, handle=h)
+                M1 = [m.clone() for m in M]
+                W1 = [w.clone() for w in W]
+                mu.muon_update(G, M, W, mu.default_config(), update_out=V, handle=h)
+                torch.cuda.synchronize()
+                results[name] = (M1, W1, M, W, V)
+            finally:
+                h.close()
+        base = results["one stream"]
+        for name, res in results.items():
+            for a, b in zip(res, base):
+                for i in range(len(mats)):
+                    assert same_bits(a[i], b[i]), (bname, name, i)
+            say(f"  {bname}, {name}: bitwise equal to one stream over two calls")
+        M1, W1, M, W, V = results["default"]
+        for i, (g, _, _) in enumerate(mats):
+            tol = BF16_TOL if g.dtype == torch.bfloat16 else FP32_TOL
+            check_update(f"{bname}[{i}]", g, M1[i], W1[i], M[i], V[i], W[i], mu.default_config(), tol)
 
 
 @pytest.mark.parametrize("block", [1, 2, 3, 8])
