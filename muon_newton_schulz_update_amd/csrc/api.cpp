@@ -180,7 +180,7 @@ struct Plan {
   HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
   HostList dupdate[2];      // [ns_t]: D update reading the pass's result (matrices equilibrated on the short side)
   HostList dfinish;         // D update from the last product's band sums (the others)
-  GemmList gemm[2][2][2][3];   // [pass group][block class][ns_t][list]
+  GemmList gemm[2][2][2][3];   // [pass group][chain][ns_t][list]
   int block = kDefaultBlock;    // iterations per block of a rectangular matrix
   // The Newton-Schulz passes run as two chains of launches, independent of
   // each other (see build_plan): chain_block[c] iterations per block in
@@ -230,7 +230,7 @@ struct muon_handle {
   hipStream_t stream = nullptr;
   // second stream (default priority, non-blocking) for the first pass's
   // one-iteration class when the plan runs it beside the other class;
-  // MUON_NS_SIDE (read at creation): 0 never, 1 whenever both classes exist
+  // MUON_NS_SIDE (read at creation): 0 never, 1 in every pass with both chains
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   int side_mode = -1;
@@ -524,7 +524,7 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
       if (P->mats[i].aurora) { ms.push_back(i); bl.push_back(1); }
     add_list(meta, P->ascale, ms, bl);
   }
-  // Newton-Schulz tile lists, one set per (pass group, block class, NS type):
+  // Newton-Schulz tile lists, one set per (pass group, chain, NS type):
   // the Gram (s x s upper tiles, K = L), the short-side products (s x s upper
   // tiles, K = s; shared by GM_SQ and GM_SYM) and X' = Q X (s x L, K = s).
   // Longest reduction first (LPT); within a matrix, tiles sharing a tile row
@@ -973,7 +973,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec), P->matvec.nblk, cfg.power_steps, 1, st));
     CHECK_LAUNCH(h, launch_power_sigma(D, dev_list(meta, P->permat), P->permat.nblk, cfg.contra, st));
   }
-  // 3. Newton-Schulz passes. Per pass group, block class and type, the
+  // 3. Newton-Schulz passes. Per pass group, chain and type, the
   // iterations run in blocks of r (see ns_gemm.hip): A = X X^T; for each j,
   // B'_j = a I + b A + c A^2 (into Q0 when j = 0), Q <- B'_j Q, and unless j
   // is the block's last, A <- B'_j (B'_j A); then X' = Q X.
@@ -1025,7 +1025,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         // the first Gram of the pass reads the prologue's fp8 copy of X0 when
         // this chain's matrices have one (all or none: bf16 with blocks)
         const bool f8 = r > 1 && t == DT_BF16 && P->fp8;
-        // profiling: one event pair around this class's launches of the pass
+        // profiling: one event pair around this chain's launches of the pass
         // (they run back to back on the stream), with their flops and count
         // summed; a pair per launch cost about 6 us each on the small sets
         ProfScope ps(h, 0, 0.0, 0.0, 0.0, on_side);
@@ -1105,7 +1105,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
 
 // Host-only consistency check of a plan (muon_debug_check_plan): every
 // workspace region inside the workspace and disjoint from the others; every
-// product tile in bounds, in the list of its matrix's pass group, block class
+// product tile in bounds, in the list of its matrix's pass group, chain
 // and type, and every tile a product needs present exactly once; streaming
 // lists with consistent block offsets. Returns an empty string when the plan
 // passes, else the first violation.
