@@ -189,7 +189,7 @@ struct Plan {
   // kSmallLaunchTiles 256-tiles)
   int chain_block[2] = {1, kDefaultBlock};
   bool two_chains = false, side = false;
-  bool fp8 = false;             // MUON_FLAG_FP8_GRAM: the class-1 bf16 matrices' first Gram is fp8
+  bool fp8 = false;             // MUON_FLAG_FP8_GRAM: the blocked bf16 matrices' first Gram is fp8
   // device meta: DevMat array followed by the list arrays
   std::vector<uint8_t> meta_host;  // list part (static)
   size_t meta_devmat_bytes = 0;
@@ -228,8 +228,8 @@ struct muon_handle {
   int device = 0;
   int ns_variant = 0;        // Newton-Schulz tile layout (MUON_NS_VARIANT; 0 = 8 waves, 1 = 4 waves)
   hipStream_t stream = nullptr;
-  // second stream (default priority, non-blocking) for the first pass's
-  // one-iteration class when the plan runs it beside the other class;
+  // second stream (default priority, non-blocking) for chain 0 of the
+  // Newton-Schulz passes when the plan runs it beside chain 1;
   // MUON_NS_SIDE (read at creation): 0 never, 1 in every pass with both chains
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
