@@ -222,11 +222,11 @@ const char* muon_version(void);
  * (a hipStream_t; NULL = the default stream). The stream is borrowed, not
  * owned. The handle owns its device workspace and plan cache; both grow on
  * demand and are freed by muon_destroy. It also owns a second stream of
- * default priority: on sets whose product launches are small, a call runs
- * part of each Newton-Schulz pass there (the one-iteration matrices beside
- * the blocked ones, or half of a set with only one kind), and `stream`
- * waits for it before the pass ends, so every call still completes in order
- * on `stream`. Returns
+ * default priority, made by the first call that uses it: on sets whose
+ * product launches are small, a call runs part of each Newton-Schulz pass
+ * there (the one-iteration matrices beside the blocked ones, or half of a
+ * set with only one kind), and `stream` waits for it before the pass ends,
+ * so every call still completes in order on `stream`. Returns
  * MUON_ERR_NO_DEVICE when no gfx950 device is current.
  *
  * Tuning (environment). The layout and tile edge give bitwise the default's

@@ -85,7 +85,7 @@ struct MatInfo {
   bool tall, square, aurora, eq_short;
   bool f8;                   // the first Gram of each pass on fp8 operands (MUON_FLAG_FP8_GRAM)
   int block;                 // Newton-Schulz iterations per block (1 for squares)
-  int chain;                 // launch chain of the Newton-Schulz passes (0 or 1; see build_plan)
+  int chain[2];              // launch chain (0 or 1) in each pass group (see build_plan)
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv, wband;
   bool band_d;               // Aurora on the long side with later passes: D from the last product's band sums
@@ -182,13 +182,13 @@ struct Plan {
   HostList dfinish;         // D update from the last product's band sums (the others)
   GemmList gemm[2][2][2][3];   // [pass group][chain][ns_t][list]
   int block = kDefaultBlock;    // iterations per block of a rectangular matrix
-  // The Newton-Schulz passes run as two chains of launches, independent of
-  // each other (see build_plan): chain_block[c] iterations per block in
-  // chain c; two_chains when both have matrices in the first pass, side when
-  // the second stream pays (every chain-1 product launch under
+  // Each Newton-Schulz pass runs as two chains of launches, independent of
+  // each other (see build_plan): chain_block[g][c] iterations per block in
+  // chain c of pass group g; two_chains[g] when both have matrices, side[g]
+  // when the second stream pays (every product launch of the group under
   // kSmallLaunchTiles 256-tiles)
-  int chain_block[2] = {1, kDefaultBlock};
-  bool two_chains = false, side = false;
+  int chain_block[2][2] = {{1, kDefaultBlock}, {1, kDefaultBlock}};
+  bool two_chains[2] = {false, false}, side[2] = {false, false};
   bool fp8 = false;             // MUON_FLAG_FP8_GRAM: the blocked bf16 matrices' first Gram is fp8
   // device meta: DevMat array followed by the list arrays
   std::vector<uint8_t> meta_host;  // list part (static)
@@ -229,8 +229,9 @@ struct muon_handle {
   int ns_variant = 0;        // Newton-Schulz tile layout (MUON_NS_VARIANT; 0 = 8 waves, 1 = 4 waves)
   hipStream_t stream = nullptr;
   // second stream (default priority, non-blocking) for chain 0 of the
-  // Newton-Schulz passes when the plan runs it beside chain 1;
-  // MUON_NS_SIDE (read at creation): 0 never, 1 in every pass with both chains
+  // Newton-Schulz passes when the plan runs it beside chain 1, made by the
+  // first call that needs it; MUON_NS_SIDE (read at creation): 0 never, 1 in
+  // every pass with both chains
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   int side_mode = -1;
@@ -390,45 +391,46 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
   P->ws_bytes = off;
   P->passes = P->any_aurora ? pp : 1;
 
-  // Chains. The one-iteration matrices (chain 0) and those with blocks
-  // (chain 1) never read each other's results inside a pass, so the two
-  // chains' launches may run side by side (on the second stream, when the
-  // launches are small; see two_chains and side below). A call with only
-  // one of the two kinds and small launches is split into two chains of
-  // about equal work (largest first, each to the lighter chain) when the
-  // second stream may be used.
-  P->chain_block[0] = 1;
-  P->chain_block[1] = block;
-  bool has[2] = {false, false};
-  long n256[2] = {0, 0};   // the widest list of each kind, in 256-tiles
-  for (int c = 0; c < 2; ++c) {
-    long lists[2][3] = {};
-    for (auto& m : P->mats) {
-      if ((m.block > 1 ? 1 : 0) != c) continue;
-      has[c] = true;
+  // Chains, per pass group (0: every matrix, 1: the Aurora matrices in the
+  // passes after the first). The one-iteration matrices (chain 0) and those
+  // with blocks (chain 1) never read each other's results inside a pass, so
+  // the two chains' launches may run side by side (on the second stream,
+  // when the launches are small; see two_chains and side below). A group
+  // with only one of the two kinds and small launches is split into two
+  // chains of about equal work (largest first, each to the lighter chain)
+  // when the second stream may be used.
+  for (int g = 0; g < 2; ++g) {
+    P->chain_block[g][0] = 1;
+    P->chain_block[g][1] = block;
+    std::vector<int> members;
+    bool has[2] = {false, false};
+    long lists[2][2][3] = {};   // [kind][ns_t][list], in 256-tiles
+    for (int i = 0; i < (int)P->mats.size(); ++i) {
+      MatInfo& m = P->mats[i];
+      const int kind = m.block > 1 ? 1 : 0;
+      m.chain[g] = kind;
+      if (g == 1 && !m.aurora) continue;
+      members.push_back(i);
+      has[kind] = true;
       const long ts = m.s_pad / kTile, tl = m.L_pad / kTile;
-      lists[m.ns_t][LIST_GRAM] += ts * (ts + 1) / 2;
-      lists[m.ns_t][LIST_SQ] += ts * (ts + 1) / 2;
-      lists[m.ns_t][LIST_BX] += ts * tl;
+      lists[kind][m.ns_t][LIST_GRAM] += ts * (ts + 1) / 2;
+      lists[kind][m.ns_t][LIST_SQ] += ts * (ts + 1) / 2;
+      lists[kind][m.ns_t][LIST_BX] += ts * tl;
     }
+    if (!may_split || has[0] == has[1] || members.size() < 2) continue;
+    const int kind = has[1] ? 1 : 0;
+    long n256 = 0;
     for (int t = 0; t < 2; ++t)
-      for (int li = 0; li < 3; ++li) n256[c] = std::max(n256[c], lists[t][li]);
-  }
-  for (auto& m : P->mats) m.chain = m.block > 1 ? 1 : 0;
-  if (may_split && has[0] != has[1] && P->mats.size() >= 2) {
-    const int c = has[1] ? 1 : 0;
-    if (n256[c] < kSmallLaunchTiles) {
-      P->chain_block[0] = P->chain_block[1] = c == 1 ? block : 1;
-      std::vector<int> order(P->mats.size());
-      for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
-      auto cost = [&](int i) { return (double)P->mats[i].s_pad * P->mats[i].s_pad * P->mats[i].L_pad; };
-      std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost(a) > cost(b); });
-      double load[2] = {0.0, 0.0};
-      for (int i : order) {
-        const int k = load[0] <= load[1] ? 0 : 1;
-        P->mats[i].chain = k;
-        load[k] += cost(i);
-      }
+      for (int li = 0; li < 3; ++li) n256 = std::max(n256, lists[kind][t][li]);
+    if (n256 >= kSmallLaunchTiles) continue;
+    P->chain_block[g][0] = P->chain_block[g][1] = kind == 1 ? block : 1;
+    auto cost = [&](int i) { return (double)P->mats[i].s_pad * P->mats[i].s_pad * P->mats[i].L_pad; };
+    std::stable_sort(members.begin(), members.end(), [&](int a, int b) { return cost(a) > cost(b); });
+    double load[2] = {0.0, 0.0};
+    for (int i : members) {
+      const int k = load[0] <= load[1] ? 0 : 1;
+      P->mats[i].chain[g] = k;
+      load[k] += cost(i);
     }
   }
 
@@ -538,7 +540,7 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
           std::vector<int> order;
           for (int i = 0; i < nm; ++i) {
             const MatInfo& m = P->mats[i];
-            if (m.ns_t != t || (g == 1 && !m.aurora) || m.chain != c) continue;
+            if (m.ns_t != t || (g == 1 && !m.aurora) || m.chain[g] != c) continue;
             order.push_back(i);
           }
           auto kdim = [&](int i) {
@@ -589,19 +591,20 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
   // (GPT-2-124M set 6.25 -> 5.96 ms, one 3.8B layer -0.4 %). With launches
   // of many rounds there is nothing to fill and the two chains' operand
   // panels share the L2s (3.8B set +2.8 %), so those stay on one stream.
-  bool c0 = false, c1 = false, c1_small = true;
-  for (int t = 0; t < 2; ++t) {
-    c0 = c0 || P->gemm[0][0][t][LIST_GRAM].n > 0;
-    for (int li = 0; li < 3; ++li) {
-      const GemmList& G = P->gemm[0][1][t][li];
-      if (G.n == 0) continue;
-      c1 = true;
-      const double per256 = (double)G.tile * G.tile / ((double)kTile * kTile);
-      c1_small = c1_small && G.n * per256 < kSmallLaunchTiles;
-    }
+  for (int g = 0; g < 2; ++g) {
+    bool has[2] = {false, false}, small = true;
+    for (int c = 0; c < 2; ++c)
+      for (int t = 0; t < 2; ++t)
+        for (int li = 0; li < 3; ++li) {
+          const GemmList& G = P->gemm[g][c][t][li];
+          if (G.n == 0) continue;
+          has[c] = true;
+          const double per256 = (double)G.tile * G.tile / ((double)kTile * kTile);
+          small = small && G.n * per256 < kSmallLaunchTiles;
+        }
+    P->two_chains[g] = has[0] && has[1];
+    P->side[g] = P->two_chains[g] && small;
   }
-  P->two_chains = c0 && c1;
-  P->side = P->two_chains && c1_small;
   return P;
 }
 
@@ -805,6 +808,16 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   }
   P->last_use = ++h->tick;
   if (P->mats.empty()) return MUON_OK;
+  // the second stream and its events, made by the first call whose plan
+  // forks, before anything of the call is enqueued (default priority;
+  // non-blocking, so it waits on the legacy null stream only through the
+  // call's events)
+  if (!use_static && !h->side && h->side_mode != 0 &&
+      (h->side_mode == 1 ? P->two_chains[0] || P->two_chains[1] : P->side[0] || P->side[1])) {
+    HIP_TRY(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
+    HIP_TRY(h, hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming));
+    HIP_TRY(h, hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming));
+  }
   muon_status rc = MUON_OK;
   uint8_t* ws;
   uint8_t* meta;
@@ -981,11 +994,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   // chains have matrices), that stream waits for everything enqueued so far,
   // and the call's stream waits for it at the end of the pass (before the D
   // update, which may read chain-0 matrices; on an early error return too).
-  const bool fork = !h->in_static && h->side &&
-                    (h->side_mode == 1 ? P->two_chains : h->side_mode != 0 && P->side);
-  auto chain_has = [&](int g, int c) {
-    return P->gemm[g][c][0][LIST_GRAM].n > 0 || P->gemm[g][c][1][LIST_GRAM].n > 0;
-  };
+  const bool may_fork = !h->in_static && h->side && h->side_mode != 0;
   struct SideJoin {
     muon_handle* h;
     hipStream_t st;
@@ -1009,7 +1018,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
       CHECK_LAUNCH(h, launch_prologue(t, D, dev_list(meta, L), L.nblk, upd ? 1 : 0, st));
     }
     const int last_pass = p + 1 == P->passes ? NS_LAST_PASS : 0;
-    const bool fork_p = fork && chain_has(g, 0) && chain_has(g, 1);
+    const bool fork_p = may_fork && (h->side_mode == 1 ? P->two_chains[g] : P->side[g]);
     if (fork_p) {
       HIP_TRY(h, hipEventRecord(h->fork_ev, st));
       HIP_TRY(h, hipStreamWaitEvent(h->side, h->fork_ev, 0));
@@ -1021,7 +1030,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         if (GL[LIST_GRAM].n == 0) continue;
         const bool on_side = fork_p && c == 0;
         const hipStream_t cs = on_side ? h->side : st;
-        const int r = P->chain_block[c];
+        const int r = P->chain_block[g][c];
         // the first Gram of the pass reads the prologue's fp8 copy of X0 when
         // this chain's matrices have one (all or none: bf16 with blocks)
         const bool f8 = r > 1 && t == DT_BF16 && P->fp8;
@@ -1155,11 +1164,14 @@ std::string check_plan(const Plan& P) {
       if (off[i + 1] - off[i] != m.n_rt * m.n_seg) return "stream: block count differs from the tile grid";
     }
   }
-  // chains: every matrix in one, with that chain's block length (its launches
-  // run that many iterations per block for all their matrices)
+  // chains: every matrix of a pass group in one of the group's chains, with
+  // that chain's block length (its launches run that many iterations per
+  // block for all their matrices)
   for (const MatInfo& m : P.mats)
-    if ((m.chain != 0 && m.chain != 1) || m.block != P.chain_block[m.chain])
-      return "matrix in a chain of another block length";
+    for (int g = 0; g < 2; ++g)
+      if ((g == 0 || m.aurora) &&
+          ((m.chain[g] != 0 && m.chain[g] != 1) || m.block != P.chain_block[g][m.chain[g]]))
+        return "matrix in a chain of another block length";
   // product tile lists
   for (int g = 0; g < 2; ++g)
     for (int c = 0; c < 2; ++c)
@@ -1174,7 +1186,7 @@ std::string check_plan(const Plan& P) {
             const TileItem& x = it[k];
             if (x.mat >= nm) return "product tile of an unknown matrix";
             const MatInfo& m = P.mats[x.mat];
-            if (m.ns_t != t || m.chain != c || (g == 1 && !m.aurora))
+            if (m.ns_t != t || m.chain[g] != c || (g == 1 && !m.aurora))
               return "product tile in another chain's list";
             if (m.s_pad % 256 || m.L_pad % 256) return "padded extents not a multiple of 256";
             const int ts = m.s_pad / tile, tcols = li == LIST_BX ? m.L_pad / tile : ts;
@@ -1188,7 +1200,7 @@ std::string check_plan(const Plan& P) {
           }
           for (int i = 0; i < nm; ++i) {
             const MatInfo& m = P.mats[i];
-            const bool member = m.ns_t == t && m.chain == c && (g == 0 || m.aurora);
+            const bool member = m.ns_t == t && m.chain[g] == c && (g == 0 || m.aurora);
             const int ts = m.s_pad / tile, tcols = li == LIST_BX ? m.L_pad / tile : ts;
             const size_t need = li == LIST_BX ? (size_t)ts * tcols : (size_t)ts * (ts + 1) / 2;
             size_t have = 0;
@@ -1262,15 +1274,6 @@ extern "C" muon_status muon_create(muon_handle** out, void* stream) {
     h->bad_host = nullptr;
     muon_destroy(h);
     return MUON_ERR_ALLOC;
-  }
-  // the second stream of small sets (default priority; non-blocking, so it
-  // never waits on the legacy null stream except through the call's events)
-  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming) != hipSuccess) {
-    (void)hipGetLastError();
-    muon_destroy(h);
-    return MUON_ERR_HIP;
   }
   *out = h;
   return MUON_OK;

@@ -376,10 +376,12 @@ def test_side_stream_matches_one_stream(dev, monkeypatch):
     """On small sets the Newton-Schulz passes run as two chains of launches
     on two streams: the one-iteration matrices (squares, and rectangular
     matrices whose short side is under 512, which carry Aurora and so feed
-    the D update after the pass) beside those with blocks, or, in a call
-    with only one of the two kinds, two halves of it (here: squares only,
-    and blocked rectangles only, whose second Aurora pass forks too). The
-    call's stream waits for the second one at the end of each pass. Two
+    the D update after the pass) beside those with blocks, or, in a pass
+    with only one of the two kinds, two halves of it (here: squares only;
+    blocked rectangles only, split in both Aurora passes; squares beside
+    blocked rectangles in the first pass, the rectangles split in the
+    second). The call's stream waits for the second one at the end of each
+    pass. Two
     calls in a row (the fork and join events are reused, the second call
     reads the first one's momenta and weights) give the one-stream bits
     (MUON_NS_SIDE=0, no split) exactly, by default and with the second
@@ -391,6 +393,8 @@ def test_side_stream_matches_one_stream(dev, monkeypatch):
                   ((700, 300), torch.float32), ((520, 1030), torch.float32), ((256, 256), torch.float32)],
         "squares": [((768, 768), torch.bfloat16)] * 5 + [((512, 512), torch.float32)] * 2,
         "blocked": [((600, 1300), torch.bfloat16), ((1300, 600), torch.bfloat16), ((768, 2304), torch.bfloat16)],
+        "squares and blocked": [((768, 768), torch.bfloat16)] * 3 + [((768, 3072), torch.bfloat16),
+                                                                      ((3072, 768), torch.bfloat16)],
     }
     for bname, spec in batches.items():
         mats = [gen.custom_matrix(sh, 1380 + 10 * len(bname) + i, dev, grad_dtype=dt, weight_dtype=dt)
