@@ -165,10 +165,13 @@ typedef struct {
 #define MUON_FLAG_CHECK_FINITE 0x8u
 #define MUON_FLAG_ALL          0xFu
 
-/* Per-kernel-class timing gathered when profiling is on (see muon_profile_*). */
+/* Per-kernel-class timing gathered when profiling is on (see muon_profile_*).
+   Each *_ms is the wall time the class's event pairs cover: their summed
+   durations less the time they overlap (launches on the handle's second
+   stream run beside those on the call's stream). */
 typedef struct {
   int64_t gemm_launches;      /* Newton-Schulz matrix-core launches */
-  double  gemm_ms;            /* summed event time of those launches */
+  double  gemm_ms;            /* event time of those launches */
   double  gemm_counted_flop;  /* 4 s^2 L + 2 s^3 per iteration per matrix (s <= L) */
   double  gemm_executed_flop; /* flops the tiles actually issue (symmetric tiles skipped) */
   double  gemm_algorithmic_flop; /* flops the products need: the upper half of each symmetric

@@ -732,9 +732,32 @@ struct ProfScope {
   }
 };
 
+// Each class's time is the wall time its records cover: the sum of their
+// durations less the time they overlap (records on the second stream run
+// beside those on the call's stream; on one stream nothing overlaps).
 muon_status drain_profile(muon_handle* h) {
+  if (h->recs.empty()) return MUON_OK;
+  std::vector<std::pair<float, float>> span[3];   // per class: [start, end] from the first record's start
   for (auto& r : h->recs) {
     HIP_TRY(h, hipEventSynchronize(r.b));
+    float t0 = 0.f, t1 = 0.f;
+    HIP_TRY(h, hipEventElapsedTime(&t0, h->recs[0].a, r.a));
+    HIP_TRY(h, hipEventElapsedTime(&t1, h->recs[0].a, r.b));
+    span[std::min(std::max(r.cls, 0), 2)].emplace_back(t0, t1);
+  }
+  double overlap[3] = {0.0, 0.0, 0.0};
+  for (int k = 0; k < 3; ++k) {
+    std::sort(span[k].begin(), span[k].end());
+    float reach = -1e30f;
+    for (auto& iv : span[k]) {
+      if (iv.first < reach) overlap[k] += std::min(reach, iv.second) - iv.first;
+      reach = std::max(reach, iv.second);
+    }
+  }
+  h->acc.gemm_ms -= overlap[0];
+  h->acc.stream_ms -= overlap[1];
+  h->acc.aux_ms -= overlap[2];
+  for (auto& r : h->recs) {
     float ms = 0.f;
     HIP_TRY(h, hipEventElapsedTime(&ms, r.a, r.b));
     if (r.cls == 0) {

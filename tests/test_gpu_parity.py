@@ -573,7 +573,10 @@ def test_profile_counts_and_flops(dev):
     blocks: GRAM, 4 SQ, 9 SYM, BX), 36 + 90 engine launches, the algorithmic
     flops 12 * 4 s^3 and 2 * 3 * (3 s^2 L + 13 s^3), the counted flops
     (4 s^2 L + 2 s^3 per iteration and pass), positive times, and the
-    streaming bytes of the momentum pass; twice that after a second step."""
+    streaming bytes of the momentum pass; twice that after a second step.
+    The first pass runs the two matrices' chains on two streams; the
+    classes' times are wall time covered (overlap counted once), so
+    together they fit inside the call's own time."""
     say("profile counts and flops")
     mats = [gen.custom_matrix((256, 256), 3300, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16),
             gen.custom_matrix((600, 2048), 3301, dev, grad_dtype=torch.bfloat16, weight_dtype=torch.bfloat16)]
@@ -581,7 +584,12 @@ def test_profile_counts_and_flops(dev):
     try:
         h.profile_reset()
         h.profile_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         run_update(dev, mats, handle=h)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = e0.elapsed_time(e1)
         p1 = h.profile_read()
         run_update(dev, mats, handle=h)
         p2 = h.profile_read()
@@ -596,6 +604,8 @@ def test_profile_counts_and_flops(dev):
     assert p1["gemm_algorithmic_flop"] == pytest.approx(algo, rel=1e-12)
     assert p1["gemm_counted_flop"] == pytest.approx(counted, rel=1e-12)
     assert p1["gemm_ms"] > 0 and p1["stream_ms"] > 0 and p1["aux_ms"] > 0
+    say(f"  classes {p1['gemm_ms'] + p1['stream_ms'] + p1['aux_ms']:.3f} ms of the call's {wall:.3f} ms")
+    assert p1["gemm_ms"] + p1["stream_ms"] + p1["aux_ms"] <= wall * 1.001 + 0.01
     assert p1["stream_bytes"] >= (256 * 256 + 600 * 2048) * (2 + 8 + 2)   # at least the momentum pass
     assert p2["gemm_launches"] == 2 * p1["gemm_launches"]
     assert p2["gemm_algorithmic_flop"] == pytest.approx(2 * algo, rel=1e-12)
