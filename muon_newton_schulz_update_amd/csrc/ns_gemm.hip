@@ -71,8 +71,19 @@ struct F8 {
 namespace {
 
 constexpr int kRowBytes = 128;                 // K bytes per tile row per stage
-constexpr int kPitch = 132;                    // floats per staged epilogue row (widest slab 128, + 4 spreads banks)
+constexpr int kPitch = 128;                    // floats per staged epilogue row (the widest slab)
 constexpr int kSlabBytes = 32 * kPitch * 4;    // one wave's 32 x 128 staging slab
+// Column swizzle of the fp32 staging slab: row r keeps its columns in 8-float
+// chunks XOR-ed with g(r) = f((r / 8) % 4), f = 0, 16, 40, 56. The
+// transposed read takes 8 rows of one column per lane, four lanes per column
+// at rows 8 apart: the XOR sends those four to different banks (32 or 64 of
+// them, per half-wave or per wave), and chunks stay whole for the row reads
+// (with a padded pitch instead they shared a bank: the swizzle is -0.3 % on
+// the 3.8B set, whose second products stage fp32 slabs).
+__device__ __forceinline__ int slab_col(int r, int c) {
+  const int g = (r >> 3) & 3;
+  return c ^ (((g & 1) << 4) | ((g >> 1) * 40));
+}
 
 // Read one accumulator through an explicit AGPR->VGPR move. The "a"
 // constraint keeps the accumulators allocated in AGPRs for their whole live
@@ -672,8 +683,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          buf[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + ni * 32 + (lane & 31)] = agpr_read(acc[mi][ni][r]);
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          buf[row * kPitch + slab_col(row, ni * 32 + (lane & 31))] = agpr_read(acc[mi][ni][r]);
+        }
       wave_lds_sync();
       if (band_sums) {
         // two 32-row slabs make a 64-row band
@@ -682,7 +695,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
           const int c = cc + lane;
           float sq = 0.f;
 #pragma unroll
-          for (int r = 0; r < 32; ++r) sq += buf[r * kPitch + c] * buf[r * kPitch + c];
+          for (int r = 0; r < 32; ++r) {
+            const float x = buf[r * kPitch + slab_col(r, c)];
+            sq += x * x;
+          }
           bsq[cc / 64] = (mi & 1) ? bsq[cc / 64] + sq : sq;
           if (mi & 1) M.lsq[(size_t)((row0 + mi * 32) >> 6) * Lp + col0 + c] = bsq[cc / 64];
         }
@@ -701,10 +717,11 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
           Elem<T>::cvt(araw[kk], av);
           const int dg = (row0 + mi * 32 + rr) - (col0 + c8);   // the diagonal is at e = dg
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = cc * buf[rr * kPitch + c8 + e] + cb * av[e] + (e == dg ? ca : 0.f);
+          for (int e = 0; e < 8; ++e)
+            v[e] = cc * buf[rr * kPitch + slab_col(rr, c8) + e] + cb * av[e] + (e == dg ? ca : 0.f);
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = buf[rr * kPitch + c8 + e];
+          for (int e = 0; e < 8; ++e) v[e] = buf[rr * kPitch + slab_col(rr, c8) + e];
         }
         if (write_o) {
           const int d = (col0 + c8) - (row0 + mi * 32 + rr);   // upper when d + e >= 0
@@ -713,7 +730,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         }
         if (mode == GM_SQ && write_t) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) buf[rr * kPitch + c8 + e] = v[e];
+          for (int e = 0; e < 8; ++e) buf[rr * kPitch + slab_col(rr, c8) + e] = v[e];
         }
       }
       if (write_t) {
@@ -724,7 +741,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
           const int c1 = q >> 2, rc = (q & 3) * 8;
           float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = buf[(rc + e) * kPitch + c1];
+          for (int e = 0; e < 8; ++e) v[e] = buf[(rc + e) * kPitch + slab_col(rc + e, c1)];
           const size_t tidx = (size_t)(col0 + c1) * ldt + row0 + mi * 32 + rc;
           const int d = (col0 + c1) - (row0 + mi * 32 + rc);   // mirror of a strict-upper source when e < d
           if (!diag_sym || d >= 8) Elem<T>::st8(outT, tidx, v);
