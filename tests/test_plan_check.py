@@ -2,11 +2,12 @@
 `muon_debug_check_plan`, no device needed): every workspace region inside
 the workspace and disjoint from the others, every Newton-Schulz product tile
 inside its matrix's padded tile grid and in the list of that matrix's pass,
-block class and element type, every tile a product needs listed exactly
-once, and consistent streaming lists. Edge shapes and seeded random batches
-over the shape space the library accepts, every call kind, and the options
-that change plans: Aurora pass count, wide rows, the fp8 first Gram, and a
-forced block length or tile edge."""
+chain and element type, every tile a product needs listed exactly once,
+each chain's matrices of one block length, and consistent streaming lists.
+Edge shapes, the named workloads, and seeded random batches over the shape
+space the library accepts, every call kind, and the options that change
+plans: Aurora pass count, wide rows, the fp8 first Gram, and a forced block
+length or tile edge."""
 import os
 import random
 
@@ -41,6 +42,17 @@ def test_edge_shapes_alone_and_together(lib):
             check(kind, [(r, c, dt) for r, c in EDGE])
         check(kind, [(r, c, dt) for r, c in EDGE for dt in (torch.float32, torch.bfloat16)])
         check(kind, [])
+
+
+def test_named_workloads(lib):
+    """The benchmark's shape sets, and sets of 3072 x 3072 squares alone and
+    beside a few blocked rectangles (lists of thousands of 256-tiles)."""
+    from muon_newton_schulz_update_amd import inputs as gen
+    for name, w in gen.WORKLOADS.items():
+        dt = w.grad_dtype
+        check("update", [(r, c, dt) for r, c in w.shapes])
+    check("polar", [(3072, 3072, torch.bfloat16)] * 56)
+    check("update", [(3072, 3072, torch.bfloat16)] * 56 + [(3072, 12288, torch.bfloat16)] * 3)
 
 
 def rand_shape(rng):
