@@ -155,7 +155,10 @@ struct GemmList {
   double executed = 0;              // flops the tiles of one launch issue (padding, whole diagonal tiles)
   double algorithmic = 0;           // flops one launch needs (upper half of a symmetric result)
 };
-enum { LIST_GRAM = 0, LIST_SQ = 1, LIST_BX = 2 };   // tile lists: Gram, short-side products, X' = Q X
+// tile lists: Gram, short-side products, X' = Q X, and the short-side list
+// twice (items of the second copy marked), for a launch of two independent
+// short-side products
+enum { LIST_GRAM = 0, LIST_SQ = 1, LIST_BX = 2, LIST_SQ2 = 3 };
 
 // A product launch with fewer 256-tiles than this uses 128-tiles: with one
 // 256-tile workgroup per CU such a launch is a few rounds of workgroups and
@@ -180,7 +183,7 @@ struct Plan {
   HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
   HostList dupdate[2];      // [ns_t]: D update reading the pass's result (matrices equilibrated on the short side)
   HostList dfinish;         // D update from the last product's band sums (the others)
-  GemmList gemm[2][2][2][3];   // [pass group][chain][ns_t][list]
+  GemmList gemm[2][2][2][4];   // [pass group][chain][ns_t][list]
   int block = kDefaultBlock;    // iterations per block of a rectangular matrix
   // Each Newton-Schulz pass runs as two chains of launches, independent of
   // each other (see build_plan): chain_block[g][c] iterations per block in
@@ -585,6 +588,20 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
             }
           }
           add_gemm(meta, G, items);
+          if (li == LIST_SQ) {
+            GemmList& G2 = P->gemm[g][c][t][LIST_SQ2];
+            G2 = G;
+            G2.executed = 2 * G.executed;
+            G2.algorithmic = 2 * G.algorithmic;
+            G2.counted_iter = 0;
+            const size_t n1 = items.size();
+            for (size_t k = 0; k < n1; ++k) {
+              TileItem x = items[k];
+              x.pad = 1;
+              items.push_back(x);
+            }
+            add_gemm(meta, G2, items);
+          }
         }
   // Small sets: their launches fill a round of the CUs or less, and chain 0
   // on a second stream fills chain 1's partial rounds and launch gaps
@@ -1080,13 +1097,14 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
           for (int j = 0; !e && j < rr; ++j) {
             const int bj = j == 0 ? SQ_Q0 : SQ_B;   // B'_0 is Q_1 itself
             e = gemm(LIST_SQ, GM_SQ, cur, ns_roles(SQ_A, SQ_A, bj), 0.0, t);
-            if (!e && j >= 1)
-              e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(SQ_B, (j - 1) & 1 ? SQ_Q1 : SQ_Q0, j & 1 ? SQ_Q1 : SQ_Q0),
-                       0.0, t);
-            if (!e && j + 1 < rr) {
-              e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_A, SQ_T), 0.0, t);
-              if (!e) e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_T, SQ_A), 0.0, t);
-            }
+            // Q <- B'_j Q and T = B'_j A need only B'_j: one launch of both
+            // (the list twice; marked tiles take the second roles)
+            const int q_roles = ns_roles(SQ_B, (j - 1) & 1 ? SQ_Q1 : SQ_Q0, j & 1 ? SQ_Q1 : SQ_Q0);
+            const int t_roles = ns_roles(bj, SQ_A, SQ_T);
+            if (!e && j >= 1 && j + 1 < rr) e = gemm(LIST_SQ2, GM_SYM, cur, q_roles | (t_roles << 16), 0.0, t);
+            else if (!e && j >= 1) e = gemm(LIST_SQ, GM_SYM, cur, q_roles, 0.0, t);
+            else if (!e && j + 1 < rr) e = gemm(LIST_SQ, GM_SYM, cur, t_roles, 0.0, t);
+            if (!e && j + 1 < rr) e = gemm(LIST_SQ, GM_SYM, cur, ns_roles(bj, SQ_T, SQ_A), 0.0, t);
           }
           if (!e) {
             const int roles = ns_roles((rr - 1) & 1 ? SQ_Q1 : SQ_Q0, 0, 0) |
@@ -1233,6 +1251,20 @@ std::string check_plan(const Plan& P) {
               return buf;
             }
             if (!member && have) return "tiles of a matrix that does not take part";
+          }
+          const TileItem* its = (const TileItem*)(P.meta_host.data() + G.off);
+          for (int k = 0; k < G.n; ++k)
+            if (its[k].pad) return "a marked tile outside the paired list";
+          // the paired list: the short-side list, then the same tiles marked
+          if (li == LIST_SQ) {
+            const GemmList& G2 = P.gemm[g][c][t][LIST_SQ2];
+            const TileItem* it2 = (const TileItem*)(P.meta_host.data() + G2.off);
+            if (G2.n != 2 * G.n || G2.tile != G.tile) return "paired list not twice the short-side list";
+            for (int k = 0; k < 2 * G.n; ++k) {
+              const TileItem& x = its[k % G.n];
+              if (it2[k].mat != x.mat || it2[k].tm != x.tm || it2[k].tn != x.tn || it2[k].pad != (k >= G.n ? 1 : 0))
+                return "paired list differs from the short-side list";
+            }
           }
         }
   return "";

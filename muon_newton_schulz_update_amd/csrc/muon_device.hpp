@@ -78,6 +78,9 @@ enum SqRole : int {
 // only pass of a matrix without the preconditioner).
 constexpr int NS_LAST_BX = 1 << 12;
 constexpr int NS_LAST_PASS = 1 << 13;
+// A launch of two independent short-side products carries the second
+// product's roles in bits 16-27; its tiles are the ones whose TileItem::pad
+// is 1.
 inline constexpr int ns_roles(int rp, int rq, int rd) { return rp | (rq << 4) | (rd << 8); }
 
 struct DevMat {
@@ -132,7 +135,7 @@ struct TileItem {
   uint16_t mat;   // index into the launch's DevMat array
   uint16_t tm;    // tile row
   uint16_t tn;    // tile column
-  uint16_t pad;
+  uint16_t pad;   // 1: a tile of the launch's second product (roles bits 16-27)
 };
 
 // Matrices taking part in one streaming launch: blocks [off[i], off[i+1])

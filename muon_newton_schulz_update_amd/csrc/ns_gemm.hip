@@ -193,7 +193,9 @@ template <> struct Elem<float> {
 // run executes together on one XCD and reuses its L2.
 // roles: the roles in DevMat::sq of operand P (bits 0-3), operand Q (bits
 // 4-7) and the output (bits 8-11); GM_BX only: bit 12 = the last product of a pass,
-// bit 13 = that pass is the last Aurora pass (NS_LAST_BX, NS_LAST_PASS).
+// bit 13 = that pass is the last Aurora pass (NS_LAST_BX, NS_LAST_PASS). A
+// GM_SYM launch may hold two independent products: tiles whose item has
+// pad = 1 take roles bits 16-27 instead.
 template <typename T, int mode, int S, int WM, int WN, int TILE>
 __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(const DevMat* __restrict__ mats,
                                                              const TileItem* __restrict__ items, int n_items,
@@ -227,7 +229,8 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   const int wm = wave / WN, wn = wave % WN;
   const int sp = M.s_pad, Lp = M.L_pad;
 
-  const int role_p = roles & 15, role_q = (roles >> 4) & 15, role_o = (roles >> 8) & 15, last = (roles >> 12) & 3;
+  const int ro = it.pad ? roles >> 16 : roles;   // the tile's product (two in one GM_SYM launch)
+  const int role_p = ro & 15, role_q = (ro >> 4) & 15, role_o = (ro >> 8) & 15, last = (roles >> 12) & 3;
   const T *P, *Q;
   int ld, K;
   if constexpr (mode == GM_GRAM) {
