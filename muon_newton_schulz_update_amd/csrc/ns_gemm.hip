@@ -14,7 +14,8 @@
 // and B'_j is a polynomial in A_0, so they commute, A_{j+1} = B'_j A_j B'_j
 // (two GM_SYM products) and X_{j+r} = Q X_j with Q = B'_{r-1} ... B'_0 (GM_SYM
 // products, then one GM_BX), which needs 3 s^2 L + (4 r - 3) s^3 flops
-// instead of r (3 s^2 L + s^3). X^T is kept beside X, written by the BX
+// instead of r (3 s^2 L + s^3); the Q update and B'_j A_j, which need only
+// B'_j, share one launch. X^T is kept beside X, written by the BX
 // epilogue, so every product reads both operands with the reduction index
 // contiguous: C[m][n] = sum_k P[m][k] Q[n][k].
 //
