@@ -432,15 +432,30 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
     // one 3.8B layer's (1248, its X' = Q X on 256-tiles with K = 3072)
     // 15.15 -> 16.03, so larger lists stay whole.
     if (n256 >= kSplitTiles) continue;
-    P->chain_block[g][0] = P->chain_block[g][1] = kind == 1 ? block : 1;
     auto cost = [&](int i) { return (double)P->mats[i].s_pad * P->mats[i].s_pad * P->mats[i].L_pad; };
     std::stable_sort(members.begin(), members.end(), [&](int a, int b) { return cost(a) > cost(b); });
     double load[2] = {0.0, 0.0};
-    for (int i : members) {
-      const int k = load[0] <= load[1] ? 0 : 1;
-      P->mats[i].chain[g] = k;
-      load[k] += cost(i);
+    long half[2][2][3] = {};   // [chain][ns_t][list], in 256-tiles
+    std::vector<int> to(members.size());
+    for (size_t k = 0; k < members.size(); ++k) {
+      const MatInfo& m = P->mats[members[k]];
+      const int c = load[0] <= load[1] ? 0 : 1;
+      to[k] = c;
+      load[c] += cost(members[k]);
+      const long ts = m.s_pad / kTile, tl = m.L_pad / kTile;
+      half[c][m.ns_t][LIST_GRAM] += ts * (ts + 1) / 2;
+      half[c][m.ns_t][LIST_SQ] += ts * (ts + 1) / 2;
+      half[c][m.ns_t][LIST_BX] += ts * tl;
     }
+    // only if both halves' launches are small enough to run side by side
+    // (one dominant matrix would leave its chain as large as the whole)
+    long hmax = 0;
+    for (int c = 0; c < 2; ++c)
+      for (int t = 0; t < 2; ++t)
+        for (int li = 0; li < 3; ++li) hmax = std::max(hmax, half[c][t][li]);
+    if (hmax >= kSmallLaunchTiles) continue;
+    P->chain_block[g][0] = P->chain_block[g][1] = kind == 1 ? block : 1;
+    for (size_t k = 0; k < members.size(); ++k) P->mats[members[k]].chain[g] = to[k];
   }
 
   const int nm = (int)P->mats.size();
