@@ -57,7 +57,8 @@ hipError_t launch_power_wsum(DevMat* m, LaunchList L, int nblk, int steps, hipSt
 hipError_t launch_power_normalize(DevMat* m, LaunchList L, int nblk, int steps, hipStream_t st);
 hipError_t launch_power_sigma(DevMat* m, LaunchList L, int nblk, float contra, hipStream_t st);
 hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, hipStream_t st);
-hipError_t launch_tail_finalize(DevMat* m, LaunchList L, int nblk, float target_uw, hipStream_t st);
+hipError_t launch_tail_rows(const DevMat* m, LaunchList L, int nblk, hipStream_t st);
+hipError_t launch_tail_finalize(DevMat* m, LaunchList L, int nblk, float target_uw, float contra, hipStream_t st);
 hipError_t launch_tail_apply(const DevMat* m, LaunchList L, int nblk, float lr, int copy_only, hipStream_t st);
 size_t static_scratch_bytes();
 hipError_t static_scratch_address(int dev, void** out);
@@ -89,7 +90,8 @@ struct MatInfo {
   int ns_t;
   int n_rt, n_ct, n_seg, n_rmv, wband;
   bool band_d;               // Aurora on the long side with later passes: D from the last product's band sums
-  size_t o_lsq;
+  bool ft;                   // fused tail (see fused_tail)
+  size_t o_lsq, o_ftail, o_frow, o_fwp;
   size_t o_xn, o_x[2], o_xt[2], o_x8, o_sq[SQ_COUNT], o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
       o_pwpart, o_tailpart, o_linepart, o_scal, o_ist;
 };
@@ -138,6 +140,19 @@ int rect_block(const muon_config& cfg, bool* forced) {
   return std::min(kDefaultBlock, std::max(1, r));
 }
 
+// Fused tail: the matrices of a muon_update call with the bf16 NS type take
+// the tail's sums in the epilogue of their final X' = Q X (||U||^2, <U, X>
+// and the parts of sigma = ||X v||) and in the momentum pass (||W||^2), so
+// the tail reads U, X and W once, in its single pass, and the power
+// iteration ends without its last X v. fp32 matrices keep the tail's
+// reduction pass and the last X v (the fp32 engine's epilogue stages fp32
+// slabs). MUON_FUSED_TAIL=0 (read when a plan is built) turns it off.
+inline bool fused_tail(int kind, int ns_t) {
+  if (kind != KIND_UPDATE || ns_t != DT_BF16) return false;
+  const char* v = getenv("MUON_FUSED_TAIL");
+  return !(v && atoi(v) == 0);
+}
+
 // Host copy of one LaunchList: offset of its int arrays in the meta buffer.
 struct HostList {
   int n = 0;
@@ -179,6 +194,8 @@ struct Plan {
   bool any_aurora = false;
   // lists
   HostList stream, permat, lines, colblk, matvec, ascale;
+  HostList stream_r;                      // the tail's reduction pass: streaming tiles of the matrices without the fused tail
+  HostList frows;                         // fused tail: sigma's row sums, one block per 256 rows
   HostList fused[2];                      // power rounds: fused X^T X v pass, one list per NS type
   HostList matvec_w, rmatvec_w;           // X v + X^T u for matrices wider than kFusedCols
   HostList prologue[2][2];  // [group: 0 all, 1 aurora][ns_t]
@@ -387,6 +404,10 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
     // takes its line sums from the pass's last product (per 64-row band)
     m.band_d = m.aurora && !m.eq_short && pp > 1;
     m.o_lsq = m.band_d ? take((size_t)(m.s_pad / 64) * m.L_pad * 4) : 0;
+    m.ft = fused_tail(kind, m.ns_t);
+    m.o_ftail = m.ft ? take((size_t)cdiv(m.rows, 64) * cdiv(m.cols, 64) * 2 * 4) : 0;
+    m.o_frow = m.ft ? take((size_t)cdiv(m.cols, 64) * m.rows * 4) : 0;
+    m.o_fwp = m.ft ? take((size_t)m.n_rt * m.n_seg * 4) : 0;
     m.o_scal = take(SC_COUNT * 4);
     m.o_ist = take(IS_COUNT * 4);
     if (m.aurora) P->any_aurora = true;
@@ -472,14 +493,29 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
     blocks[i] = m.n_rt * m.n_seg;   // kStreamRows x kSegCols tiles
   }
   add_list(meta, P->stream, all, blocks);
+  {
+    std::vector<int> ms, bl, fm, fb;
+    for (int i = 0; i < nm; ++i) {
+      const MatInfo& m = P->mats[i];
+      if (!m.ft) { ms.push_back(i); bl.push_back(m.n_rt * m.n_seg); }
+      else { fm.push_back(i); fb.push_back(cdiv(m.rows, 256)); }
+    }
+    add_list(meta, P->stream_r, ms, bl);
+    add_list(meta, P->frows, fm, fb);
+  }
   for (int i = 0; i < nm; ++i) blocks[i] = 1;
   add_list(meta, P->permat, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = line_blocks(P->mats[i].rows, P->mats[i].cols);
   add_list(meta, P->lines, all, blocks);
   for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].cols, 256);
   add_list(meta, P->colblk, all, blocks);
-  for (int i = 0; i < nm; ++i) blocks[i] = cdiv(P->mats[i].rows, 16);   // 4 waves x 4 rows
-  add_list(meta, P->matvec, all, blocks);   // the final X v of every matrix
+  {
+    // the final X v of every matrix without the fused tail
+    std::vector<int> ms, bl;
+    for (int i = 0; i < nm; ++i)
+      if (!P->mats[i].ft) { ms.push_back(i); bl.push_back(cdiv(P->mats[i].rows, 16)); }   // 4 waves x 4 rows
+    add_list(meta, P->matvec, ms, bl);
+  }
   {
     // Power rounds: the matrices fused_power() takes run the fused X^T X v
     // pass, one launch per NS type, widest first; the others take X v then
@@ -936,6 +972,13 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     d.pwpart = (float*)(ws + m.o_pwpart); d.tailpart = (float*)(ws + m.o_tailpart);
     d.linepart = (float*)(ws + m.o_linepart);
     d.lsq = m.band_d ? (float*)(ws + m.o_lsq) : nullptr;
+    if (m.ft) {
+      d.ftail = (float*)(ws + m.o_ftail);
+      d.frow = (float*)(ws + m.o_frow);
+      d.fwp = (float*)(ws + m.o_fwp);
+      d.ftx = cfg.contra != 0.f;
+      d.ftw = d.w != nullptr;
+    }
     d.scal = (float*)(ws + m.o_scal); d.ist = (int32_t*)(ws + m.o_ist);
   }
   if (use_static) {
@@ -962,7 +1005,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   const bool contra = upd && cfg.contra != 0.f;
 
   // algorithmic byte counts for the profile
-  double el_ns = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
+  double el_ns = 0, el_mv = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
   double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_dup[2] = {0, 0}, b_dfin = 0;
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
@@ -970,9 +1013,11 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     const DevMat& d = dm[i];
     el_all += el;
     el_ns += el * esz(m.ns_t);
+    if (!m.ft) el_mv += el * esz(m.ns_t);
     (fused_power(m) ? el_fused[m.ns_t] : el_wide) += el * esz(m.ns_t);
-    b_mom += upd ? el * (esz(d.dt_g) + 8 + esz(m.ns_t)) : el * esz(d.dt_g);
-    b_tail_r += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? esz(d.dt_w) : 0));
+    b_mom += upd ? el * (esz(d.dt_g) + 8 + esz(m.ns_t) + (d.ftw ? esz(d.dt_w) : 0)) : el * esz(d.dt_g);
+    if (!m.ft) b_tail_r += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? esz(d.dt_w) : 0));
+    else if (contra) b_tail_r += el * 4.0 / 64;   // sigma's row parts
     b_tail_a += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? 2 * esz(d.dt_w) : 0) + (d.uo ? esz(d.dt_uo) : 0));
     // prologue bytes: read the source, write the iterate and its transpose
     const double pro = el * esz(m.ns_t) + 2.0 * m.s_pad * (double)m.L_pad * esz(m.ns_t);
@@ -984,6 +1029,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     }
   }
   (void)el_all;
+  (void)el_ns;
 
   // 0. optional input check: read-only, before anything is written; the
   // flags come back into pinned host memory and the call waits for them
@@ -1042,10 +1088,13 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
       CHECK_LAUNCH(h, launch_power_wsum(D, dev_list(meta, P->colblk), P->colblk.nblk, cfg.power_steps, st));
       CHECK_LAUNCH(h, launch_power_normalize(D, dev_list(meta, P->permat), P->permat.nblk, cfg.power_steps, st));
     }
-    ps.r.amount += el_ns;
-    ps.r.count += 2;
-    CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec), P->matvec.nblk, cfg.power_steps, 1, st));
-    CHECK_LAUNCH(h, launch_power_sigma(D, dev_list(meta, P->permat), P->permat.nblk, cfg.contra, st));
+    // the final X v and sigma (fused-tail matrices take both in the tail)
+    if (P->matvec.nblk) {
+      ps.r.amount += el_mv;
+      ps.r.count += 2;
+      CHECK_LAUNCH(h, launch_power_matvec(D, dev_list(meta, P->matvec), P->matvec.nblk, cfg.power_steps, 1, st));
+      CHECK_LAUNCH(h, launch_power_sigma(D, dev_list(meta, P->permat), P->permat.nblk, cfg.contra, st));
+    }
   }
   // 3. Newton-Schulz passes. Per pass group, chain and type, the
   // iterations run in blocks of r (see ns_gemm.hip): A = X X^T; for each j,
@@ -1156,13 +1205,15 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   // 4. tail
   Range rt(h, "tail");
   if (upd) {
-    {
+    if (P->stream_r.nblk || (contra && P->frows.nblk)) {
       ProfScope ps(h, 1, b_tail_r);
-      CHECK_LAUNCH(h, launch_tail_reduce(D, dev_list(meta, P->stream), P->stream.nblk, st));
+      CHECK_LAUNCH(h, launch_tail_reduce(D, dev_list(meta, P->stream_r), P->stream_r.nblk, st));
+      if (contra) CHECK_LAUNCH(h, launch_tail_rows(D, dev_list(meta, P->frows), P->frows.nblk, st));
     }
     {
       ProfScope ps(h, 1, 0);
-      CHECK_LAUNCH(h, launch_tail_finalize(D, dev_list(meta, P->permat), P->permat.nblk, cfg.target_uw, st));
+      CHECK_LAUNCH(h, launch_tail_finalize(D, dev_list(meta, P->permat), P->permat.nblk, cfg.target_uw, cfg.contra,
+                                           st));
     }
     ProfScope ps(h, 1, b_tail_a);
     CHECK_LAUNCH(h, launch_tail_apply(D, dev_list(meta, P->stream), P->stream.nblk, cfg.lr, 0, st));
@@ -1212,7 +1263,8 @@ std::string check_plan(const Plan& P) {
       {&P.matvec, "matvec"}, {&P.ascale, "ascale"}, {&P.fused[0], "fused"}, {&P.fused[1], "fused"},
       {&P.matvec_w, "matvec_w"}, {&P.rmatvec_w, "rmatvec_w"}, {&P.prologue[0][0], "prologue"},
       {&P.prologue[0][1], "prologue"}, {&P.prologue[1][0], "prologue"}, {&P.prologue[1][1], "prologue"},
-      {&P.dupdate[0], "dupdate"}, {&P.dupdate[1], "dupdate"}, {&P.dfinish, "dfinish"}};
+      {&P.dupdate[0], "dupdate"}, {&P.dupdate[1], "dupdate"}, {&P.dfinish, "dfinish"},
+      {&P.stream_r, "stream_r"}, {&P.frows, "frows"}};
   for (const auto& l : lists) {
     std::string e = list_ok(*l.first, l.second);
     if (!e.empty()) return e;

@@ -128,6 +128,18 @@ struct DevMat {
                     // of ||w||^2
   float* scal;      // SC_COUNT
   int32_t* ist;     // IS_COUNT
+  // Fused tail (muon_update, bf16 NS type; null otherwise): the epilogue of
+  // the matrix's final X' = Q X takes the tail's sums from the values it
+  // stores, and the momentum pass takes ||W||^2, so no kernel reads U, X
+  // and W before the tail's single pass.
+  float* ftail;     // cdiv(rows,64) x cdiv(cols,64) x 2: per 64 x 64 block of the storage frame, ||U||^2 and
+                    // <U, X> (X the stored blended update)
+  float* frow;      // cdiv(cols,64) x rows: per storage row and 64-column block, the block's part of
+                    // (X / ||X||_F) v, v the last power-iteration vector (sigma = ||X v||)
+  float* fwp;       // n_rt x n_seg: ||W||^2 per streaming tile, from the momentum pass (tailpart is
+                    // taken by the D update in between)
+  int32_t ftx;      // per call: the epilogue also takes <U, X> and the sigma parts (contra != 0)
+  int32_t ftw;      // per call: the momentum pass takes ||W||^2 (a weight is given)
 };
 
 // One output tile of a Newton-Schulz product.

@@ -68,6 +68,7 @@ struct F8 {
 };
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+#define GAS __attribute__((address_space(1)))
 
 namespace {
 
@@ -548,6 +549,49 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // values it would store, and stores nothing else.
   const bool band_sums = mode == GM_BX && (last & 1) && !(last & 2) && M.lsq != nullptr;
   if (band_sums) write_o = write_t = false;
+  // Fused tail: the final product of a bf16 muon_update matrix stores U as
+  // usual and also takes, per 64 x 64 block of the storage frame, ||U||^2 and
+  // <U, X> of the stored values (ftail) and, per storage row, the block's part
+  // of (X / ||X||_F) v (frow), X the blended update, v the power iteration's
+  // last vector. A block's lanes take 8 storage rows per step, 8 lanes of 8
+  // columns per row, and sum in one fixed order, the same for every tile size
+  // and layout, so the sums do not depend on how the product was tiled. The X
+  // chunks of the wave's first blocks are requested before the staging.
+  constexpr int FTC = NI * 32 / 64;                  // 64-wide blocks across the wave's tile
+  constexpr int FTB = (MI * 32 / 64) * FTC;          // 64 x 64 blocks per wave
+  constexpr int FTP = FTB <= 2 ? FTB : 0;            // blocks whose X is requested early
+  bool ft = false;
+  if constexpr (mode == GM_BX && sizeof(T) == 2) ft = (last & 1) && ((last & 2) || !M.aurora) && M.ftail != nullptr;
+  const bool ftx = ft && M.ftx != 0;
+  const int fa0 = lane >> 3, fch = lane & 7;
+  auto ft_origin = [&](int b, int& srow0, int& scol0) {
+    const int bi = b / FTC, bj = b % FTC;
+    if (M.tall) { srow0 = col0 + 64 * bj; scol0 = row0 + 64 * bi; }
+    else { srow0 = row0 + 64 * bi; scol0 = col0 + 64 * bj; }
+  };
+  // 8 elements of X at storage (i, j..j+7), zero outside the matrix
+  auto ft_ldx = [&](int i, int j) -> u16x8_t {
+    u16x8_t q = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (!ftx || i >= M.rows || j >= M.cols) return q;
+    const GAS unsigned short* xp = (const GAS unsigned short*)M.xn + (size_t)i * M.cols + j;
+    if ((M.cols & 7) == 0) return *(const GAS u16x8_t*)xp;   // j % 8 == 0, so j + 8 <= cols
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j + e < M.cols) q[e] = xp[e];
+    return q;
+  };
+  u16x8_t fxq[FTP > 0 ? FTP : 1][8];
+  if constexpr (FTP > 0) {
+    if (ftx) {
+#pragma unroll
+      for (int b = 0; b < FTP; ++b) {
+        int srow0, scol0;
+        ft_origin(b, srow0, scol0);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) fxq[b][kk] = ft_ldx(srow0 + 8 * kk + fa0, scol0 + 8 * fch);
+      }
+    }
+  }
   // A GM_SYM result is symmetric only in exact arithmetic (C[m][n] and C[n][m]
   // come from different products), so its diagonal tiles keep the upper
   // triangle and write the lower one as its mirror: the stored matrix is then
@@ -618,6 +662,80 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
           M.lsq[(size_t)((row0 + 64 * b) >> 6) * Lp + col0 + c] = sq;
         }
       return;
+    }
+    if constexpr (mode == GM_BX && sizeof(T) == 2) {
+      if (ft) {
+        const float n2 = M.scal[SC_XNORM2];
+        const float xin = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+        const int nbc = (M.cols + 63) >> 6;
+#pragma unroll
+        for (int b = 0; b < FTB; ++b) {
+          const int bi = b / FTC, bj = b % FTC;
+          int srow0, scol0;
+          ft_origin(b, srow0, scol0);
+          u16x8_t xq[8];
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            if constexpr (FTP > 0) xq[kk] = fxq[b < FTP ? b : 0][kk];
+            else xq[kk] = ft_ldx(srow0 + 8 * kk + fa0, scol0 + 8 * fch);
+          }
+          // v over this lane's 8 storage columns
+          float vv[8];
+          const int j = scol0 + 8 * fch;
+          if (ftx && j + 8 <= M.cols) {
+            const f32x4_t v0 = *(const GAS f32x4_t*)(M.pv + j), v1 = *(const GAS f32x4_t*)(M.pv + j + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { vv[e] = v0[e]; vv[e + 4] = v1[e]; }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[e] = (ftx && j + e < M.cols) ? ((const GAS float*)M.pv)[j + e] : 0.f;
+          }
+          float uu = 0.f, ux = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            u16x8_t u;
+            if (M.tall) {
+              // storage row col0 + c, its columns row0 + r8 .. + 7 (8 rows of the staged column)
+              const int r8 = 64 * bi + 8 * fch, c = 64 * bj + 8 * kk + fa0;
+              u = *(const u16x8_t*)(st + sidx(r8, c));
+              *(u16x8_t*)((unsigned short*)outT + (size_t)(col0 + c) * ldt + row0 + r8) = u;
+            } else {
+              const int r = 64 * bi + 8 * kk + fa0, c8 = 64 * bj + 8 * fch;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) u[e] = st[sidx(r, c8 + e)];
+              *(u16x8_t*)((unsigned short*)out + (size_t)(row0 + r) * ldo + col0 + c8) = u;
+            }
+            float pr = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float uf = bf2f(u[e]), xf = bf2f(xq[kk][e]);
+              uu += uf * uf;
+              ux += uf * xf;
+              pr += xf * vv[e];
+            }
+            if (ftx) {
+              // the row's 64 columns: its 8 lanes (lane >> 3 equal), in one order
+              pr += __shfl_xor(pr, 1, 64);
+              pr += __shfl_xor(pr, 2, 64);
+              pr += __shfl_xor(pr, 4, 64);
+              const int i = srow0 + 8 * kk + fa0;
+              if (fch == 0 && i < M.rows && scol0 < M.cols)
+                *(GAS float*)(M.frow + (size_t)(scol0 >> 6) * M.rows + i) = pr * xin;
+            }
+          }
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) {
+            uu += __shfl_xor(uu, o, 64);
+            ux += __shfl_xor(ux, o, 64);
+          }
+          if (lane == 0 && srow0 < M.rows && scol0 < M.cols) {
+            GAS float* dst = (GAS float*)(M.ftail + ((size_t)(srow0 >> 6) * nbc + (scol0 >> 6)) * 2);
+            dst[0] = uu;
+            dst[1] = ux;
+          }
+        }
+        return;
+      }
     }
     // row-major: 8 consecutive columns of one row per lane
     if (write_o) {

@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "muon_device.hpp"
 
@@ -223,11 +224,16 @@ __device__ __forceinline__ float strided_sum(const float* p, size_t stride, int 
 // tile's columns) and, for wide matrices, colpart[tile_row][c] (column sums
 // over the tile's rows, the four waves combined in LDS).
 // ---------------------------------------------------------------------------
-template <typename TG, typename TX, bool NP>
+// TW (not void): a fused-tail matrix with a weight; the pass also reads W and
+// writes the tile's ||W||^2 to fwp[local] (the tail then reads U, X and W
+// only once, in its single pass).
+template <typename TG, typename TX, bool NP, typename TW = void>
 __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float mu, int nesterov, int sgd,
-                                              float* cp) {
+                                              float* cp, float* wred) {
   typedef Ty<TG> G;
   typedef Ty<float> F;
+  constexpr bool kW = !std::is_void<TW>::value;
+  typedef std::conditional_t<kW, TW, float> TWx;
   constexpr int R = kWaveRows;
   const int tr = local / M.n_seg, sg = local % M.n_seg;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -237,8 +243,10 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
   const int dg = sizeof(TG) == 2 ? DT_BF16 : DT_F32, dx = sizeof(TX) == 2 ? DT_BF16 : DT_F32;
   const int nv = max(0, min(8, M.cols - c));
   const bool fast = nr == R && nv == 8 && aligned16(M.g, M.ld_g, dg) &&
-                    (!NP || (aligned16(M.m, M.ld_m, DT_F32) && aligned16(M.xn, M.cols, dx)));
+                    (!NP || (aligned16(M.m, M.ld_m, DT_F32) && aligned16(M.xn, M.cols, dx))) &&
+                    (!kW || aligned16(M.w, M.ld_w, sizeof(TWx) == 2 ? DT_BF16 : DT_F32));
   float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float sw = 0.f;   // this lane's part of the tile's ||W||^2 (kW)
   float rsl[R];   // this lane's part of each row's sum of squares
   // one row: the update (stored through vector or element-wise stores), then
   // this lane's sums of squares; a row's floats die before the next row is
@@ -268,18 +276,24 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
     rsl[k] = rs;
   };
   if (fast) {
-    // fp32 grads load in two batches of R/2 rows: the kernel's register
-    // budget is set by its largest body
-    constexpr int RB = sizeof(TG) == 2 ? R : R / 2;
+    // fp32 grads load in two batches of R/2 rows, and so do bf16 ones with
+    // a weight (fp32 weights in four of R/4): the kernel's register budget
+    // is set by its largest body
+    constexpr int RB = !kW ? (sizeof(TG) == 2 ? R : R / 2) : (sizeof(TWx) == 2 ? R / 2 : R / 4);
 #pragma unroll
     for (int k0 = 0; k0 < R; k0 += RB) {
       typename G::Raw qg[RB];
       typename F::Raw qm[RB];
+      typename Ty<TWx>::Raw qw[kW ? RB : 1];
 #pragma unroll
       for (int k = 0; k < RB; ++k) qg[k] = G::ld(M.g, (size_t)(r + k0 + k) * M.ld_g + c);
       if (NP) {
 #pragma unroll
         for (int k = 0; k < RB; ++k) qm[k] = F::ld(M.m, (size_t)(r + k0 + k) * M.ld_m + c);
+      }
+      if constexpr (kW) {
+#pragma unroll
+        for (int k = 0; k < RB; ++k) qw[k] = Ty<TW>::ld(M.w, (size_t)(r + k0 + k) * M.ld_w + c);
       }
 #pragma unroll
       for (int k = 0; k < RB; ++k) {
@@ -287,6 +301,12 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
         G::cvt(qg[k], x);
         if (NP) F::cvt(qm[k], m);
         row(k0 + k, x, m, true);
+        if constexpr (kW) {
+          float wv[8];
+          Ty<TW>::cvt(qw[k], wv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sw += wv[e] * wv[e];
+        }
       }
     }
   } else {
@@ -297,7 +317,20 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
       ld_part<TG>(M.g, (size_t)(r + k) * M.ld_g + c, n, x);
       if (NP) ld_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m);
       row(k, x, m, false);
+      if constexpr (kW) {
+        float wv[8];
+        ld_part<TW>(M.w, (size_t)(r + k) * M.ld_w + c, n, wv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sw += wv[e] * wv[e];
+      }
     }
+  }
+  if constexpr (kW) {
+    // the four waves' sums in order (block-uniform: every wave gets here)
+    sw = wave_sum(sw);
+    if (lane == 0) wred[w] = sw;
+    __syncthreads();
+    if (threadIdx.x == 0) gst<float>(M.fwp + local, wred[0] + wred[1] + wred[2] + wred[3]);
   }
 #pragma unroll
   for (int k = 0; k < R; ++k) {
@@ -321,15 +354,23 @@ __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict
                                                         int nesterov_pass, float mu, int nesterov, int sgd) {
   static_assert(kStreamRows == 4 * kWaveRows, "four waves per streaming tile");
   __shared__ float cp[4 * kSegCols];
+  __shared__ float wred[4];
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  // the grad's type is the NS type (plans are keyed by it)
+  // the grad's type is the NS type (plans are keyed by it); fused-tail
+  // matrices are bf16
   if (M.dt_g == DT_BF16) {
-    if (nesterov_pass) momentum_body<__bf16, __bf16, true>(M, local, mu, nesterov, sgd, cp);
-    else momentum_body<__bf16, __bf16, false>(M, local, mu, nesterov, sgd, cp);
+    if (nesterov_pass && M.ftw) {
+      if (M.dt_w == DT_BF16) momentum_body<__bf16, __bf16, true, __bf16>(M, local, mu, nesterov, sgd, cp, wred);
+      else momentum_body<__bf16, __bf16, true, float>(M, local, mu, nesterov, sgd, cp, wred);
+    } else if (nesterov_pass) {
+      momentum_body<__bf16, __bf16, true>(M, local, mu, nesterov, sgd, cp, wred);
+    } else {
+      momentum_body<__bf16, __bf16, false>(M, local, mu, nesterov, sgd, cp, wred);
+    }
   } else {
-    if (nesterov_pass) momentum_body<float, float, true>(M, local, mu, nesterov, sgd, cp);
-    else momentum_body<float, float, false>(M, local, mu, nesterov, sgd, cp);
+    if (nesterov_pass) momentum_body<float, float, true>(M, local, mu, nesterov, sgd, cp, wred);
+    else momentum_body<float, float, false>(M, local, mu, nesterov, sgd, cp, wred);
   }
 }
 
@@ -1099,10 +1140,12 @@ __global__ __launch_bounds__(256) void k_power_normalize(DevMat* __restrict__ ma
 }
 
 // sigma = ||X v|| (from u = (X/||X||) v), kappa = (contra/2) / max(sigma, 1e-7).
+// A fused-tail matrix takes sigma in the tail instead (k_tail_finalize).
 __global__ __launch_bounds__(256) void k_power_sigma(DevMat* __restrict__ mats, LaunchList L, float contra) {
   __shared__ float red[8];
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  if (M.ftail) return;
   float s = 0.f;
   for (int r = threadIdx.x; r < M.rows; r += 256) {
     const float u = gld<float>(M.pu + r);
@@ -1251,22 +1294,69 @@ __global__ __launch_bounds__(256) void k_tail_reduce(const DevMat* __restrict__ 
   TAIL_DISPATCH(tail_reduce_body, M, local, red);
 }
 
+// Fused tail, sigma = ||X v||: u_i = the sum of storage row i's parts over
+// its 64-column blocks (frow, from the final product's epilogue, in block
+// order), then per block of 256 rows the sum of u_i^2 into linepart[local]
+// (free by the tail: the norms and the power iteration are done with it).
+__global__ __launch_bounds__(256) void k_tail_rows(const DevMat* __restrict__ mats, LaunchList L) {
+  __shared__ float red[8];
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  const int i = local * 256 + threadIdx.x;
+  const int nbc = (M.cols + 63) / 64;
+  const float u = i < M.rows ? strided_sum(M.frow + i, (size_t)M.rows, nbc) : 0.f;
+  const float s = block_sum(u * u, red);
+  if (threadIdx.x == 0) gst<float>(M.linepart + local, s);
+}
+
 // alpha = ||U|| / max(||U - kappa X||, 1e-10) * sqrt(max(1, rows/cols)),
 // then the u/w-floor: if max(||V||,1e-8) / max(||W||,1e-8) < target, scale up.
-__global__ __launch_bounds__(256) void k_tail_finalize(DevMat* __restrict__ mats, LaunchList L, float target_uw) {
+// A fused-tail matrix has ||U||^2 and <U, X> per 64 x 64 block (ftail),
+// ||W||^2 per streaming tile (fwp) and, with the Contra term, sigma's row
+// blocks (linepart, k_tail_rows): sigma and kappa are set here, and
+// ||U - kappa X||^2 = ||U||^2 - 2 kappa <U, X> + kappa^2 ||X||^2 (no
+// cancellation to fear: kappa X has operator norm contra / 2 < 1 = that of U).
+__global__ __launch_bounds__(256) void k_tail_finalize(DevMat* __restrict__ mats, LaunchList L, float target_uw,
+                                                       float contra) {
   __shared__ float red[8];
   int local;
   DevMat& M = mats[find_job(L, blockIdx.x, &local)];
   const int nb = M.n_rt * M.n_seg;
-  float su = 0.f, sv = 0.f, sw = 0.f;
-  for (int i = threadIdx.x; i < nb; i += 256) {
-    su += gld<float>(M.tailpart + (size_t)i * 4 + 0);
-    sv += gld<float>(M.tailpart + (size_t)i * 4 + 1);
-    sw += gld<float>(M.tailpart + (size_t)i * 4 + 2);
+  float su = 0.f, sv = 0.f, sw = 0.f, sx = 0.f;
+  if (M.ftail) {
+    const int nft = ((M.rows + 63) / 64) * ((M.cols + 63) / 64);
+    const int nrb = (M.rows + 255) / 256;
+    for (int i = threadIdx.x; i < nft; i += 256) {
+      su += gld<float>(M.ftail + (size_t)i * 2 + 0);
+      sx += gld<float>(M.ftail + (size_t)i * 2 + 1);
+    }
+    if (M.ftw)
+      for (int i = threadIdx.x; i < nb; i += 256) sw += gld<float>(M.fwp + i);
+    if (M.ftx)
+      for (int i = threadIdx.x; i < nrb; i += 256) sv += gld<float>(M.linepart + i);
+  } else {
+    for (int i = threadIdx.x; i < nb; i += 256) {
+      su += gld<float>(M.tailpart + (size_t)i * 4 + 0);
+      sv += gld<float>(M.tailpart + (size_t)i * 4 + 1);
+      sw += gld<float>(M.tailpart + (size_t)i * 4 + 2);
+    }
   }
   su = block_sum(su, red);
   sv = block_sum(sv, red);
   sw = block_sum(sw, red);
+  sx = block_sum(sx, red);
+  if (threadIdx.x == 0 && M.ftail) {
+    // sv holds sum u_i^2 with u = (X / ||X||) v here
+    float kappa = 0.f;
+    const float n2 = M.scal[SC_XNORM2];
+    if (M.ftx) {
+      const float sigma = (n2 > 0.f && M.ist[IS_PSTEPS] > 0) ? sqrtf(sv) * sqrtf(n2) : 0.f;
+      kappa = 0.5f * contra / fmaxf(sigma, 1e-7f);
+      M.scal[SC_SIGMA] = sigma;
+      M.scal[SC_KAPPA] = kappa;
+    }
+    sv = fmaxf(su - 2.f * kappa * sx + kappa * kappa * n2, 0.f);
+  }
   if (threadIdx.x == 0) {
     const float f = sqrtf(su), nv = sqrtf(sv);
     float alpha = f / fmaxf(nv, 1e-10f);
@@ -1425,8 +1515,12 @@ hipError_t launch_tail_reduce(const DevMat* m, LaunchList L, int nblk, hipStream
   LAUNCH(k_tail_reduce, nblk, m, L);
   return hipGetLastError();
 }
-hipError_t launch_tail_finalize(DevMat* m, LaunchList L, int nblk, float target_uw, hipStream_t st) {
-  LAUNCH(k_tail_finalize, nblk, m, L, target_uw);
+hipError_t launch_tail_rows(const DevMat* m, LaunchList L, int nblk, hipStream_t st) {
+  LAUNCH(k_tail_rows, nblk, m, L);
+  return hipGetLastError();
+}
+hipError_t launch_tail_finalize(DevMat* m, LaunchList L, int nblk, float target_uw, float contra, hipStream_t st) {
+  LAUNCH(k_tail_finalize, nblk, m, L, target_uw, contra);
   return hipGetLastError();
 }
 hipError_t launch_tail_apply(const DevMat* m, LaunchList L, int nblk, float lr, int copy_only, hipStream_t st) {

@@ -767,6 +767,56 @@ def test_update_floor_forced(dev):
     assert float(ratio) == pytest.approx(0.35, rel=1e-4)
 
 
+FUSED_TAIL_CASES = {
+    "default": dict(), "contra0": dict(contra=0.0), "contra1": dict(contra=1.0), "pp0": dict(pp_iterations=0),
+    "ns_steps1": dict(ns_steps=1), "no_weight_floor": dict(target_uw=0.0),
+}
+
+
+@pytest.mark.parametrize("case", list(FUSED_TAIL_CASES))
+def test_fused_tail_matches_reduction_pass(dev, monkeypatch, case):
+    """bf16 muon_update with the fused tail (||U||^2, <U, X> and the parts of
+    sigma = ||X v|| taken in the final product's epilogue, ||W||^2 in the
+    momentum pass) against the tail's own reduction pass and last X v
+    (MUON_FUSED_TAIL=0, a new handle): the same update up to the float32
+    order of those sums, both within the bf16 tolerance of the oracle. Tall,
+    wide, square and ragged matrices, one without a weight, one whose floor
+    fires (W ~ N(0,1)), and an fp32 matrix (never fused) in the same call."""
+    say(f"fused tail against the reduction pass: {case}")
+    cfg = mu.default_config()
+    for k, v in FUSED_TAIL_CASES[case].items():
+        setattr(cfg, k, v)
+    shapes = [(384, 200), (200, 520), (256, 256), (130, 61), (61, 130), (96, 300)]
+    mats = [gen.custom_matrix(sh, 4400 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3, mom_sd=1e-3,
+                              weight_dtype=torch.bfloat16, weight_sd=1.0 if i == 5 else 0.02)
+            for i, sh in enumerate(shapes)]
+    mats[1] = (mats[1][0], mats[1][1], None)
+    mats.append(gen.custom_matrix((90, 200), 4410, dev))
+    runs = []
+    for fused in ("1", "0"):
+        monkeypatch.setenv("MUON_FUSED_TAIL", fused)
+        h = mu.Handle(dev.index)
+        try:
+            runs.append(run_update(dev, mats, cfg=cfg, handle=h))
+        finally:
+            h.close()
+    monkeypatch.delenv("MUON_FUSED_TAIL")
+    (G, M0, W0, M, V, W), (_, _, _, Mr, Vr, Wr) = runs
+    for i in range(len(mats)):
+        d = rel(f64(V[i]), f64(Vr[i]))
+        say(f"  [{i}] {tuple(G[i].shape)} {G[i].dtype}: fused vs reduction pass rel(V)={d:.2e}")
+        if G[i].dtype == torch.float32:
+            assert torch.equal(V[i], Vr[i]) and torch.equal(W[i], Wr[i]), i   # same path either way
+        else:
+            assert d <= 2e-5, (i, d)
+        assert torch.equal(M[i], Mr[i]), i
+        tol = FP32_TOL if G[i].dtype == torch.float32 else BF16_TOL
+        check_update(f"fused[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], cfg, tol)
+    if cfg.target_uw > 0:
+        ratio = torch.linalg.norm(V[5].double()) / torch.linalg.norm(W0[5].double())
+        assert float(ratio) == pytest.approx(float(np.float32(cfg.target_uw)), rel=1e-4)
+
+
 OPTIONS = {
     "contra0": dict(contra=0.0), "contra1": dict(contra=1.0), "nesterov0": dict(nesterov=0),
     "pp0": dict(pp_iterations=0), "pp1": dict(pp_iterations=1), "pp3": dict(pp_iterations=3),
