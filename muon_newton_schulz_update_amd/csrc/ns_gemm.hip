@@ -57,6 +57,8 @@ namespace muon {
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -121,6 +123,38 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Sums over lanes in one fixed order with DPP moves (rows of 16 lanes), the
+// row totals read from lanes 0, 16, 32 and 48: valid in every lane.
+template <int ctrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);   // row_half_mirror
+  v += dpp_move<0x140>(v);   // row_mirror
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a + b) + (c + d);
+}
+// Each lane of a group of 8 (a half row, g = lane % 8) holds p[0..7]; returns
+// in lane g the sum of p[g] over the group's 8 lanes. Three halving steps:
+// partners across the half-row mirror (g, 7 - g), then g ^ 2, then g ^ 1;
+// at each a lane keeps the half of its values whose index bit matches its
+// own and adds the partner's copy of them.
+__device__ __forceinline__ float group8_transpose_sum(const float (&p)[8], int g) {
+  const bool h = (g >> 2) & 1, c = (g >> 1) & 1, d = g & 1;
+  float q[4], r[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) q[k] = (h ? p[4 + k] : p[k]) + dpp_move<0x141>(h ? p[k] : p[4 + k]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) r[k] = (c ? q[2 + k] : q[k]) + dpp_move<0x4E>(c ? q[k] : q[2 + k]);
+  return (d ? r[1] : r[0]) + dpp_move<0xB1>(d ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ unsigned short f2bf(float f) {
   // round to nearest even (inputs here are finite)
   unsigned int u = __float_as_uint(f);
@@ -129,6 +163,11 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
 }
 __device__ __forceinline__ float bf2f(unsigned short h) {
   return __uint_as_float(((unsigned int)h) << 16);
+}
+// c + a.lo b.lo + a.hi b.hi on two packed bf16 pairs (v_dot2c_f32_bf16; the
+// bf16 products are exact in fp32)
+__device__ __forceinline__ float dot2(unsigned int a, unsigned int b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 template <typename T> struct Elem;
@@ -553,13 +592,14 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // usual and also takes, per 64 x 64 block of the storage frame, ||U||^2 and
   // <U, X> of the stored values (ftail) and, per storage row, the block's part
   // of (X / ||X||_F) v (frow), X the blended update, v the power iteration's
-  // last vector. A block's lanes take 8 storage rows per step, 8 lanes of 8
-  // columns per row, and sum in one fixed order, the same for every tile size
-  // and layout, so the sums do not depend on how the product was tiled. The X
-  // chunks of the wave's first blocks are requested before the staging.
+  // last vector. In a block, lane l takes storage rows 8 k + l / 8 (k = 0..7)
+  // at columns 8 (l % 8) .. + 7; the sums run in one fixed order, the same for
+  // every tile size and layout, so they do not depend on how the product was
+  // tiled. The X chunks are requested once the tile is staged, and arrive
+  // while the wave stores U.
   constexpr int FTC = NI * 32 / 64;                  // 64-wide blocks across the wave's tile
   constexpr int FTB = (MI * 32 / 64) * FTC;          // 64 x 64 blocks per wave
-  constexpr int FTP = FTB <= 2 ? FTB : 0;            // blocks whose X is requested early
+  constexpr int FTP = FTB <= 2 ? FTB : 0;            // blocks whose X is requested before U is stored
   bool ft = false;
   if constexpr (mode == GM_BX && sizeof(T) == 2) ft = (last & 1) && ((last & 2) || !M.aurora) && M.ftail != nullptr;
   const bool ftx = ft && M.ftx != 0;
@@ -569,29 +609,32 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     if (M.tall) { srow0 = col0 + 64 * bj; scol0 = row0 + 64 * bi; }
     else { srow0 = row0 + 64 * bi; scol0 = col0 + 64 * bj; }
   };
-  // 8 elements of X at storage (i, j..j+7), zero outside the matrix
-  auto ft_ldx = [&](int i, int j) -> u16x8_t {
-    u16x8_t q = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (!ftx || i >= M.rows || j >= M.cols) return q;
-    const GAS unsigned short* xp = (const GAS unsigned short*)M.xn + (size_t)i * M.cols + j;
-    if ((M.cols & 7) == 0) return *(const GAS u16x8_t*)xp;   // j % 8 == 0, so j + 8 <= cols
+  // a block's X chunks (rows srow0 + 8 k + l / 8, columns scol0 + 8 (l % 8)) and
+  // v entries: plain vector loads for a block inside a matrix of whole
+  // 16-byte rows (the branch is uniform over the wave), element-wise ones
+  // with zeros outside the matrix otherwise
+  auto ft_load = [&](int srow0, int scol0, u16x8_t (&q)[8], float (&vv)[8]) {
+    const int j = scol0 + 8 * fch;
+    if (srow0 + 64 <= M.rows && scol0 + 64 <= M.cols && (M.cols & 7) == 0) {
+      const GAS unsigned short* xp = (const GAS unsigned short*)M.xn + (size_t)(srow0 + fa0) * M.cols + j;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (j + e < M.cols) q[e] = xp[e];
-    return q;
-  };
-  u16x8_t fxq[FTP > 0 ? FTP : 1][8];
-  if constexpr (FTP > 0) {
-    if (ftx) {
+      for (int kk = 0; kk < 8; ++kk) q[kk] = *(const GAS u16x8_t*)(xp + (size_t)8 * kk * M.cols);
+      const f32x4_t v0 = *(const GAS f32x4_t*)(M.pv + j), v1 = *(const GAS f32x4_t*)(M.pv + j + 4);
 #pragma unroll
-      for (int b = 0; b < FTP; ++b) {
-        int srow0, scol0;
-        ft_origin(b, srow0, scol0);
+      for (int e = 0; e < 4; ++e) { vv[e] = v0[e]; vv[e + 4] = v1[e]; }
+    } else {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) fxq[b][kk] = ft_ldx(srow0 + 8 * kk + fa0, scol0 + 8 * fch);
+      for (int kk = 0; kk < 8; ++kk) {
+        const int i = srow0 + 8 * kk + fa0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          q[kk][e] = (i < M.rows && j + e < M.cols) ? ((const GAS unsigned short*)M.xn)[(size_t)i * M.cols + j + e]
+                                                    : (unsigned short)0;
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vv[e] = j + e < M.cols ? ((const GAS float*)M.pv)[j + e] : 0.f;
     }
-  }
+  };
   // A GM_SYM result is symmetric only in exact arithmetic (C[m][n] and C[n][m]
   // come from different products), so its diagonal tiles keep the upper
   // triangle and write the lower one as its mirror: the stored matrix is then
@@ -668,71 +711,104 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         const float n2 = M.scal[SC_XNORM2];
         const float xin = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
         const int nbc = (M.cols + 63) >> 6;
+        u16x8_t fxq[FTP > 0 ? FTP : 1][8];
+        float fvv[FTP > 0 ? FTP : 1][8];
+        if constexpr (FTP > 0) {
+          if (ftx) {
+#pragma unroll
+            for (int b = 0; b < FTP; ++b) {
+              int srow0, scol0;
+              ft_origin(b, srow0, scol0);
+              ft_load(srow0, scol0, fxq[b], fvv[b]);
+            }
+          }
+        }
+        float uus[FTB], uxs[FTB];
+        // the stored chunk k of block (bi, bj) of this lane, read from the
+        // staged tile; store != 0 also writes it to U
+        auto chunk = [&](auto tall_c, int bi, int bj, int kk, bool store) -> u16x8_t {
+          u16x8_t u;
+          if constexpr (decltype(tall_c)::value) {
+            // storage row col0 + c: 8 staged rows of column c
+            const int r8 = 64 * bi + 8 * fch, c = 64 * bj + 8 * kk + fa0;
+            u = *(const u16x8_t*)(st + sidx(r8, c));
+            if (store) *(u16x8_t*)((unsigned short*)outT + (size_t)(col0 + c) * ldt + row0 + r8) = u;
+          } else {
+            const int r = 64 * bi + 8 * kk + fa0, c8 = 64 * bj + 8 * fch;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = st[sidx(r, c8 + e)];
+            if (store) *(u16x8_t*)((unsigned short*)out + (size_t)(row0 + r) * ldo + col0 + c8) = u;
+          }
+          return u;
+        };
+        auto blocks = [&](auto tall_c) {
+          // U stored and ||U||^2 taken while the X chunks are on their way
+#pragma unroll
+          for (int b = 0; b < FTB; ++b) {
+            float uu = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const u32x4_t uw = __builtin_bit_cast(u32x4_t, chunk(tall_c, b / FTC, b % FTC, kk, true));
+#pragma unroll
+              for (int p = 0; p < 4; ++p) uu = dot2(uw[p], uw[p], uu);
+            }
+            uus[b] = uu;
+            uxs[b] = 0.f;
+          }
+          if (!ftx) return;
+#pragma unroll
+          for (int b = 0; b < FTB; ++b) {
+            int srow0, scol0;
+            ft_origin(b, srow0, scol0);
+            u16x8_t xq[8];
+            float vv[8];
+            if constexpr (FTP > 0) {
+#pragma unroll
+              for (int kk = 0; kk < 8; ++kk) xq[kk] = fxq[b < FTP ? b : 0][kk];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) vv[e] = fvv[b < FTP ? b : 0][e];
+            } else {
+              ft_load(srow0, scol0, xq, vv);
+            }
+            // v as a sum of two bf16 parts, vh + vl (v to about 16 bits), so
+            // that X v takes packed bf16 products too
+            unsigned int vh[4], vl[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const unsigned short h0 = f2bf(vv[2 * p]), h1 = f2bf(vv[2 * p + 1]);
+              vh[p] = (unsigned int)h0 | ((unsigned int)h1 << 16);
+              vl[p] = (unsigned int)f2bf(vv[2 * p] - bf2f(h0)) | ((unsigned int)f2bf(vv[2 * p + 1] - bf2f(h1)) << 16);
+            }
+            float ux = 0.f, pr[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const u32x4_t uw = __builtin_bit_cast(u32x4_t, chunk(tall_c, b / FTC, b % FTC, kk, false));
+              const u32x4_t xw = __builtin_bit_cast(u32x4_t, xq[kk]);
+              pr[kk] = 0.f;
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                ux = dot2(uw[p], xw[p], ux);
+                pr[kk] = dot2(xw[p], vh[p], pr[kk]);
+                pr[kk] = dot2(xw[p], vl[p], pr[kk]);
+              }
+            }
+            uxs[b] = ux;
+            // each row's 8 parts (one per lane of an 8-lane group) to one
+            // lane: lane g of the group ends with row 8 g + l / 8
+            const float t = group8_transpose_sum(pr, fch);
+            const int i = srow0 + 8 * fch + fa0;
+            if (i < M.rows && scol0 < M.cols) *(GAS float*)(M.frow + (size_t)(scol0 >> 6) * M.rows + i) = t * xin;
+          }
+        };
+        if (M.tall) blocks(std::true_type{});
+        else blocks(std::false_type{});
 #pragma unroll
         for (int b = 0; b < FTB; ++b) {
-          const int bi = b / FTC, bj = b % FTC;
           int srow0, scol0;
           ft_origin(b, srow0, scol0);
-          u16x8_t xq[8];
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            if constexpr (FTP > 0) xq[kk] = fxq[b < FTP ? b : 0][kk];
-            else xq[kk] = ft_ldx(srow0 + 8 * kk + fa0, scol0 + 8 * fch);
-          }
-          // v over this lane's 8 storage columns
-          float vv[8];
-          const int j = scol0 + 8 * fch;
-          if (ftx && j + 8 <= M.cols) {
-            const f32x4_t v0 = *(const GAS f32x4_t*)(M.pv + j), v1 = *(const GAS f32x4_t*)(M.pv + j + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { vv[e] = v0[e]; vv[e + 4] = v1[e]; }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vv[e] = (ftx && j + e < M.cols) ? ((const GAS float*)M.pv)[j + e] : 0.f;
-          }
-          float uu = 0.f, ux = 0.f;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            u16x8_t u;
-            if (M.tall) {
-              // storage row col0 + c, its columns row0 + r8 .. + 7 (8 rows of the staged column)
-              const int r8 = 64 * bi + 8 * fch, c = 64 * bj + 8 * kk + fa0;
-              u = *(const u16x8_t*)(st + sidx(r8, c));
-              *(u16x8_t*)((unsigned short*)outT + (size_t)(col0 + c) * ldt + row0 + r8) = u;
-            } else {
-              const int r = 64 * bi + 8 * kk + fa0, c8 = 64 * bj + 8 * fch;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) u[e] = st[sidx(r, c8 + e)];
-              *(u16x8_t*)((unsigned short*)out + (size_t)(row0 + r) * ldo + col0 + c8) = u;
-            }
-            float pr = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float uf = bf2f(u[e]), xf = bf2f(xq[kk][e]);
-              uu += uf * uf;
-              ux += uf * xf;
-              pr += xf * vv[e];
-            }
-            if (ftx) {
-              // the row's 64 columns: its 8 lanes (lane >> 3 equal), in one order
-              pr += __shfl_xor(pr, 1, 64);
-              pr += __shfl_xor(pr, 2, 64);
-              pr += __shfl_xor(pr, 4, 64);
-              const int i = srow0 + 8 * kk + fa0;
-              if (fch == 0 && i < M.rows && scol0 < M.cols)
-                *(GAS float*)(M.frow + (size_t)(scol0 >> 6) * M.rows + i) = pr * xin;
-            }
-          }
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) {
-            uu += __shfl_xor(uu, o, 64);
-            ux += __shfl_xor(ux, o, 64);
-          }
-          if (lane == 0 && srow0 < M.rows && scol0 < M.cols) {
-            GAS float* dst = (GAS float*)(M.ftail + ((size_t)(srow0 >> 6) * nbc + (scol0 >> 6)) * 2);
-            dst[0] = uu;
-            dst[1] = ux;
-          }
+          const float su = wave_sum_dpp(uus[b]), sx = wave_sum_dpp(uxs[b]);
+          if (lane == 0 && srow0 < M.rows && scol0 < M.cols)
+            *(GAS f32x2_t*)(M.ftail + ((size_t)(srow0 >> 6) * nbc + (scol0 >> 6)) * 2) = (f32x2_t){su, sx};
         }
         return;
       }
