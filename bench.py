@@ -244,8 +244,8 @@ def main() -> int:
                     help="research option, not the headline: the first Gram of each pass on fp8 operands "
                          "(MUON_FLAG_FP8_GRAM); the line's dtype says so")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="before the steps, run one plain device copy of this many MiB (a known-size "
-                         "reference for hardware byte counters)")
+                    help="before the steps, run one plain device copy, one read-only sum and one fill "
+                         "of this many MiB (known-size references for hardware byte counters)")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -282,7 +282,12 @@ def main() -> int:
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"[bench] copy calibration: {a.copy_calibration_mib} MiB read + {a.copy_calibration_mib} MiB written")
+        tot = src.sum()              # reads the buffer once (a few bytes of partial sums written)
+        torch.cuda.synchronize()
+        dst.fill_(2.0)               # writes it once
+        torch.cuda.synchronize()
+        log(f"[bench] calibration: copy of {a.copy_calibration_mib} MiB, then a sum reading it "
+            f"({float(tot):.0f}) and a fill writing it")
         del src, dst
 
     def step():
