@@ -248,6 +248,12 @@ const char* muon_version(void);
  *                          uses the second stream in every pass that has
  *                          both one-iteration and blocked matrices, however
  *                          large (bitwise the same results either way).
+ *   MUON_FUSED_TAIL=0      read when a plan is built: bf16 matrices of
+ *                          muon_update take the tail's norms in a reduction
+ *                          pass over U, X and W (and the operator-norm
+ *                          estimate in its own X v launch) instead of in the
+ *                          final Newton-Schulz product's epilogue and the
+ *                          momentum pass (the same sums in another order).
  * Tracing: MUON_ROCTX=1, read here, wraps each phase of a call (momentum,
  * power iteration, each Newton-Schulz pass, the Aurora D update, the tail)
  * in a ROCTx range for rocprofv3 --marker-trace; the ROCTx library is loaded

@@ -1005,14 +1005,13 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
   const bool contra = upd && cfg.contra != 0.f;
 
   // algorithmic byte counts for the profile
-  double el_ns = 0, el_mv = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
+  double el_mv = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
   double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_dup[2] = {0, 0}, b_dfin = 0;
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
     const double el = (double)m.rows * m.cols;
     const DevMat& d = dm[i];
     el_all += el;
-    el_ns += el * esz(m.ns_t);
     if (!m.ft) el_mv += el * esz(m.ns_t);
     (fused_power(m) ? el_fused[m.ns_t] : el_wide) += el * esz(m.ns_t);
     b_mom += upd ? el * (esz(d.dt_g) + 8 + esz(m.ns_t) + (d.ftw ? esz(d.dt_w) : 0)) : el * esz(d.dt_g);
@@ -1029,7 +1028,6 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     }
   }
   (void)el_all;
-  (void)el_ns;
 
   // 0. optional input check: read-only, before anything is written; the
   // flags come back into pinned host memory and the call waits for them
