@@ -91,6 +91,8 @@ struct MatInfo {
   int n_rt, n_ct, n_seg, n_rmv, wband;
   bool band_d;               // Aurora on the long side with later passes: D from the last product's band sums
   bool ft;                   // fused tail (see fused_tail)
+  bool x0n;                  // X0^T read from xn by each pass's first X' = Q X (see tall_x0_direct)
+  bool x0g;                  // X0 read from xn by the pass's first Gram (see tall_x0_direct)
   size_t o_lsq, o_ftail, o_frow, o_fwp;
   size_t o_xn, o_x[2], o_xt[2], o_x8, o_sq[SQ_COUNT], o_rowpart, o_colpart, o_rowsq, o_colsq, o_rho, o_dvec, o_pu, o_pv,
       o_pwpart, o_tailpart, o_linepart, o_scal, o_ist;
@@ -150,6 +152,21 @@ int rect_block(const muon_config& cfg, bool* forced) {
 inline bool fused_tail(int kind, int ns_t) {
   if (kind != KIND_UPDATE || ns_t != DT_BF16) return false;
   const char* v = getenv("MUON_FUSED_TAIL");
+  return !(v && atoi(v) == 0);
+}
+
+// A tall matrix's X0^T = scale D o T has the storage orientation of T, the
+// blended update xn, row by row: when its rows and columns are multiples of
+// the tile (no padding, so xn is laid out as xt[0] would be), the pass
+// prologue writes only X0 and the pass's first X' = Q X reads xn, applying
+// scale D_l to its output column l in the epilogue (bf16 NS type, muon_update
+// calls, whose prologue reads xn). MUON_TALL_X0=0 (read when a plan is built)
+// turns it off. Likewise a wide or square matrix without the preconditioner
+// has X0 = scale X in the storage orientation: its prologue writes only X0^T
+// and its pass's first Gram reads xn and scales A by scale^2.
+inline bool tall_x0_direct(int kind, int ns_t, int rows, int cols) {
+  if (kind != KIND_UPDATE || ns_t != DT_BF16 || rows % kTile || cols % kTile) return false;
+  const char* v = getenv("MUON_TALL_X0");
   return !(v && atoi(v) == 0);
 }
 
@@ -405,11 +422,13 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
     m.band_d = m.aurora && !m.eq_short && pp > 1;
     m.o_lsq = m.band_d ? take((size_t)(m.s_pad / 64) * m.L_pad * 4) : 0;
     m.ft = fused_tail(kind, m.ns_t);
+    m.x0n = m.tall && tall_x0_direct(kind, m.ns_t, m.rows, m.cols);
     m.o_ftail = m.ft ? take((size_t)cdiv(m.rows, 64) * cdiv(m.cols, 64) * 2 * 4) : 0;
     m.o_frow = m.ft ? take((size_t)cdiv(m.cols, 64) * m.rows * 4) : 0;
     m.o_fwp = m.ft ? take((size_t)m.n_rt * m.n_seg * 4) : 0;
     m.o_scal = take(SC_COUNT * 4);
     m.o_ist = take(IS_COUNT * 4);
+    m.x0g = !m.tall && !m.aurora && tall_x0_direct(kind, m.ns_t, m.rows, m.cols);
     if (m.aurora) P->any_aurora = true;
     P->mats.push_back(m);
   }
@@ -972,6 +991,8 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     d.pwpart = (float*)(ws + m.o_pwpart); d.tailpart = (float*)(ws + m.o_tailpart);
     d.linepart = (float*)(ws + m.o_linepart);
     d.lsq = m.band_d ? (float*)(ws + m.o_lsq) : nullptr;
+    d.x0n = m.x0n;
+    d.x0g = m.x0g;
     if (m.ft) {
       d.ftail = (float*)(ws + m.o_ftail);
       d.frow = (float*)(ws + m.o_frow);
@@ -1019,7 +1040,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     else if (contra) b_tail_r += el * 4.0 / 64;   // sigma's row parts
     b_tail_a += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? 2 * esz(d.dt_w) : 0) + (d.uo ? esz(d.dt_uo) : 0));
     // prologue bytes: read the source, write the iterate and its transpose
-    const double pro = el * esz(m.ns_t) + 2.0 * m.s_pad * (double)m.L_pad * esz(m.ns_t);
+    const double pro = el * esz(m.ns_t) + (m.x0n || m.x0g ? 1.0 : 2.0) * m.s_pad * (double)m.L_pad * esz(m.ns_t);
     b_pro[0][m.ns_t] += pro;
     if (m.aurora) {
       b_pro[1][m.ns_t] += pro;
@@ -1161,7 +1182,8 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
         for (int k = 0; k < cfg.ns_steps; cur ^= 1) {
           const int rr = std::min(r, cfg.ns_steps - k);
           k += rr;
-          muon_status e = gemm(LIST_GRAM, GM_GRAM, cur, ns_roles(0, 0, SQ_A), 0.0, f8 && k == rr ? DT_F8 : t);
+          muon_status e = gemm(LIST_GRAM, GM_GRAM, cur, ns_roles(0, 0, SQ_A) | (k == rr ? NS_FIRST : 0), 0.0,
+                               f8 && k == rr ? DT_F8 : t);
           for (int j = 0; !e && j < rr; ++j) {
             const int bj = j == 0 ? SQ_Q0 : SQ_B;   // B'_0 is Q_1 itself
             e = gemm(LIST_SQ, GM_SQ, cur, ns_roles(SQ_A, SQ_A, bj), 0.0, t);
@@ -1176,7 +1198,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
           }
           if (!e) {
             const int roles = ns_roles((rr - 1) & 1 ? SQ_Q1 : SQ_Q0, 0, 0) |
-                              (k == cfg.ns_steps ? NS_LAST_BX | last_pass : 0);
+                              (k == cfg.ns_steps ? NS_LAST_BX | last_pass : 0) | (k == rr ? NS_FIRST : 0);
             e = gemm(LIST_BX, GM_BX, cur, roles, rr * GL[LIST_BX].counted_iter, t);
           }
           if (e) return e;

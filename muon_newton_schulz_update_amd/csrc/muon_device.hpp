@@ -78,6 +78,12 @@ enum SqRole : int {
 // only pass of a matrix without the preconditioner).
 constexpr int NS_LAST_BX = 1 << 12;
 constexpr int NS_LAST_PASS = 1 << 13;
+// Bit 14 of a GM_GRAM or GM_BX launch: the pass's first Gram or first
+// X' = Q X. For a matrix with DevMat::x0n that X' = Q X reads the stored
+// blended update instead of X0^T and scales its output columns by the
+// prologue's factor (scale D_l); for one with DevMat::x0g that Gram reads it
+// instead of X0 and scales its output by scale^2.
+constexpr int NS_FIRST = 1 << 14;
 // A launch of two independent short-side products carries the second
 // product's roles in bits 16-27; its tiles are the ones whose TileItem::pad
 // is 1.
@@ -138,6 +144,12 @@ struct DevMat {
                     // (X / ||X||_F) v, v the last power-iteration vector (sigma = ||X v||)
   float* fwp;       // n_rt x n_seg: ||W||^2 per streaming tile, from the momentum pass (tailpart is
                     // taken by the D update in between)
+  int32_t x0n;      // a tall bf16 matrix of muon_update with rows and cols multiples of kTile: X0^T is
+                    // scale D o X row by row, so the pass prologue writes only X0 and each pass's first
+                    // X' = Q X reads xn (ld = cols = s_pad) and applies scale D_l to output column l
+  int32_t x0g;      // a wide or square bf16 matrix of muon_update without the preconditioner, rows and
+                    // cols multiples of kTile: X0 = scale X, so the pass prologue writes only X0^T and the
+                    // pass's first Gram reads xn (ld = cols = L_pad) and scales A by scale^2
   int32_t ftx;      // per call: the epilogue also takes <U, X> and the sigma parts (contra != 0)
   int32_t ftw;      // per call: the momentum pass takes ||W||^2 (a weight is given)
 };

@@ -272,6 +272,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
 
   const int ro = it.pad ? roles >> 16 : roles;   // the tile's product (two in one GM_SYM launch)
   const int role_p = ro & 15, role_q = (ro >> 4) & 15, role_o = (ro >> 8) & 15, last = (roles >> 12) & 3;
+  // a pass's first X' = Q X of a matrix whose X0^T is its blended update scaled row by row
+  const bool x0n = mode == GM_BX && sizeof(T) == 2 && (roles & NS_FIRST) && M.x0n;
+  // a pass's first Gram of a matrix whose X0 is its blended update times scale
+  const bool x0g = mode == GM_GRAM && sizeof(T) == 2 && (roles & NS_FIRST) && M.x0g;
   const T *P, *Q;
   int ld, K;
   if constexpr (mode == GM_GRAM) {
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
       Q = x + (size_t)it.tn * TILE * 64;
       ld = 64; K = Lp;
     } else {
-      const T* x = (const T*)M.x[cur];
+      const T* x = (const T*)(x0g ? M.xn : M.x[cur]);   // xn: ld = cols = L_pad
       P = x + (size_t)it.tm * TILE * Lp;
       Q = x + (size_t)it.tn * TILE * Lp;
       ld = Lp; K = Lp;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     ld = sp; K = sp;
   } else {
     P = (const T*)M.sq[role_p] + (size_t)it.tm * TILE * sp;
-    Q = (const T*)M.xt[cur] + (size_t)it.tn * TILE * sp;
+    Q = (const T*)(x0n ? M.xn : M.xt[cur]) + (size_t)it.tn * TILE * sp;   // xn: ld = cols = s_pad
     ld = sp; K = sp;
   }
 
@@ -655,8 +659,16 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     }
   }
   __syncthreads();   // every wave is done with the slots
-  // the fp8 Gram's products carry the square of the operand scale q
-  const float oscale = kF8 ? M.scal[SC_F8INV2] : 1.f;
+  // the fp8 Gram's products carry the square of the operand scale q; a
+  // pass's first X' = Q X read from xn takes the prologue's scale D_l per
+  // output column l, and a first Gram read from xn the square of its scale
+  const float oscale = kF8 ? M.scal[SC_F8INV2] : x0g ? M.scal[SC_SCALE] * M.scal[SC_SCALE] : 1.f;
+  float cscale[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    cscale[ni] = oscale;
+    if (x0n) cscale[ni] = M.scal[SC_SCALE] * (M.aurora ? M.dvec[col0 + ni * 32 + (lane & 31)] : 1.f);
+  }
   if constexpr ((sizeof(T) == 2 || kF8) && mode != GM_SQ) {
     // bf16 outputs that are the accumulators rounded: each wave stages its
     // whole (MI*32) x (NI*32) tile at once, rounded, column-major (a column's
@@ -679,10 +691,10 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         for (int g = 0; g < 4; ++g) {
           const int col = ni * 32 + (lane & 31);
           const int row = mi * 32 + 8 * g + 4 * (lane >> 5);   // rows row..row+3: registers 4g..4g+3
-          const unsigned int lo = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g]) * oscale) |
-                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 1]) * oscale) << 16);
-          const unsigned int hi = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 2]) * oscale) |
-                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 3]) * oscale) << 16);
+          const unsigned int lo = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g]) * cscale[ni]) |
+                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 1]) * cscale[ni]) << 16);
+          const unsigned int hi = (unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 2]) * cscale[ni]) |
+                                  ((unsigned int)f2bf(agpr_read(acc[mi][ni][4 * g + 3]) * cscale[ni]) << 16);
           *(u32x2_t*)(st + sidx(row, col)) = (u32x2_t){lo, hi};
         }
     wave_lds_sync();

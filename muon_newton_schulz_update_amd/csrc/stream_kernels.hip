@@ -516,7 +516,10 @@ __global__ __launch_bounds__(256) void k_norms_scalars(DevMat* __restrict__ mats
 // ---------------------------------------------------------------------------
 // NS prologue through an LDS transpose: X0 = scale * D o T in the wide
 // orientation, written to x[0] (s_pad x L_pad) and its transpose to xt[0]
-// (L_pad x s_pad), zero padded (the first iteration's products read both).
+// (L_pad x s_pad), zero padded (the first iteration's products read both;
+// for a DevMat::x0n matrix xt[0] is not written: its first X' = Q X reads
+// xn and applies scale D itself; for an x0g matrix x[0] is not written: its
+// first Gram reads xn and applies scale^2).
 // T is the source in storage orientation (rows x cols); for a tall source the
 // wide iterate is its transpose. 64 x 64 tiles over the padded storage frame;
 // a thread loads its two 8-column chunks (and their D entries) before using
@@ -596,7 +599,8 @@ __device__ __forceinline__ void prologue_body(const DevMat& M, int local, const 
       v[e] *= scale * dv[h][e];
       tile[i][j + e] = v[e];
     }
-    Ty<T>::st(dir, (size_t)rr[h] * ld_dir + cc[h], v);
+    // x0n, x0g: the pass's first X' = Q X or first Gram reads xn instead
+    if (!M.x0n && !M.x0g) Ty<T>::st(dir, (size_t)rr[h] * ld_dir + cc[h], v);
     if (x8 && !M.tall) put8(rr[h], cc[h], v);
   }
   __syncthreads();

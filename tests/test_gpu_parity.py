@@ -817,6 +817,48 @@ def test_fused_tail_matches_reduction_pass(dev, monkeypatch, case):
         assert float(ratio) == pytest.approx(float(np.float32(cfg.target_uw)), rel=1e-4)
 
 
+@pytest.mark.parametrize("case", ["default", "pp0", "classic"])
+def test_x0_direct_matches_prologue_copy(dev, monkeypatch, case):
+    """bf16 matrices whose sides are multiples of 256 read the stored blended
+    update in place of a prologue copy (the default): a tall one's first
+    X' = Q X of each pass reads it as X0^T and applies the prologue's scale D
+    to its output columns (the prologue writes only X0); a square or wide one
+    without the preconditioner reads it as X0 in its pass's first Gram,
+    scaled by scale^2 (the prologue writes only X0^T). Against both copies
+    written by the prologue (MUON_TALL_X0=0, a new handle) they differ only
+    by the copy's bf16 rounding (relative 1e-2 allowed); both are within the
+    bf16 tolerance of the oracle. Blocks of four iterations (short side 512
+    and 768) and single ones (256), Aurora, plain NS (pp 0) and the classic
+    recipe; a wide Aurora matrix is never affected and must agree bit for
+    bit."""
+    say(f"X0 or X0^T read from the blended update: {case}")
+    cfg = mu.make_config("classic") if case == "classic" else mu.default_config()
+    if case == "pp0":
+        cfg.pp_iterations = 0
+    shapes = [(1024, 256), (768, 512), (2048, 768), (512, 1024), (512, 512)]
+    mats = [gen.custom_matrix(sh, 4600 + i, dev, grad_dtype=torch.bfloat16, grad_sd=1e-3, mom_sd=1e-3,
+                              weight_dtype=torch.bfloat16) for i, sh in enumerate(shapes)]
+    runs = []
+    for direct in ("1", "0"):
+        monkeypatch.setenv("MUON_TALL_X0", direct)
+        h = mu.Handle(dev.index)
+        try:
+            runs.append(run_update(dev, mats, cfg=cfg, handle=h))
+        finally:
+            h.close()
+    monkeypatch.delenv("MUON_TALL_X0")
+    (G, M0, W0, M, V, W), (_, _, _, Mr, Vr, Wr) = runs
+    for i, sh in enumerate(shapes):
+        d = rel(f64(V[i]), f64(Vr[i]))
+        say(f"  [{i}] {sh}: direct vs prologue copy rel(V)={d:.2e}")
+        if sh[0] >= sh[1] or cfg.pp_iterations == 0:
+            assert d <= 1e-2, (i, d)
+        else:
+            assert torch.equal(V[i], Vr[i]) and torch.equal(W[i], Wr[i]), i
+        assert torch.equal(M[i], Mr[i]), i
+        check_update(f"x0n[{i}]", G[i], M0[i], W0[i], M[i], V[i], W[i], cfg, BF16_TOL)
+
+
 OPTIONS = {
     "contra0": dict(contra=0.0), "contra1": dict(contra=1.0), "nesterov0": dict(nesterov=0),
     "pp0": dict(pp_iterations=0), "pp1": dict(pp_iterations=1), "pp3": dict(pp_iterations=3),
