@@ -254,6 +254,14 @@ const char* muon_version(void);
  *                          estimate in its own X v launch) instead of in the
  *                          final Newton-Schulz product's epilogue and the
  *                          momentum pass (the same sums in another order).
+ *   MUON_TALL_X0=0         read when a plan is built: bf16 matrices of
+ *                          muon_update with both sides multiples of 256 get
+ *                          both orientations of the pass's first iterate
+ *                          from the prologue, instead of the first X' = Q X
+ *                          (tall matrices) or the first Gram (wide or square
+ *                          ones without the preconditioner) reading the
+ *                          blended update and scaling its output (the
+ *                          same products, rounded once less).
  * Tracing: MUON_ROCTX=1, read here, wraps each phase of a call (momentum,
  * power iteration, each Newton-Schulz pass, the Aurora D update, the tail)
  * in a ROCTx range for rocprofv3 --marker-trace; the ROCTx library is loaded
