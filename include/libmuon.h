@@ -173,7 +173,7 @@ typedef struct {
   int64_t gemm_launches;      /* Newton-Schulz matrix-core launches */
   double  gemm_ms;            /* event time of those launches */
   double  gemm_counted_flop;  /* 4 s^2 L + 2 s^3 per iteration per matrix (s <= L) */
-  double  gemm_executed_flop; /* flops the tiles actually issue (symmetric tiles skipped) */
+  double  gemm_executed_flop; /* flops the tiles actually issue (symmetric tiles skipped; on diagonal tiles the waves wholly below the diagonal issue none) */
   double  gemm_algorithmic_flop; /* flops the products need: the upper half of each symmetric
                                     result, no padding (3 s^2 L + (4 r - 3) s^3 per block of r
                                     iterations) */

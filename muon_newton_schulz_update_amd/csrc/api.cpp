@@ -660,7 +660,9 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
             } else {
               const double K = li == LIST_GRAM ? m.L_pad : m.s_pad;
               G.algorithmic += li == LIST_GRAM ? s * s * L : s * s * s;   // the upper half of a symmetric result
-              G.executed += 2.0 * (ts * (ts + 1) / 2) * tile * (double)tile * K;
+              // upper tiles, less the quarter of each diagonal tile whose
+              // waves lie wholly below the diagonal and skip their work
+              G.executed += 2.0 * (ts * (ts + 1) / 2.0 - ts / 4.0) * tile * (double)tile * K;
             }
           }
           add_gemm(meta, G, items);

@@ -470,87 +470,114 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     wait_vm<(S - 3) * LPO>();
   }
   ring_barrier();
-  read_frags(0, 1, 0, 0);
-  // slots of stage k (ps, qs) and of stage k+1 (pn, qn)
-  int ps = 0, qs = 1, pn = 2 % S, qn = 3 % S;
-  constexpr int NDS = KS - 1 < 2 ? KS - 1 : 2;   // k-steps that carry the deferred refill
-  for (int k = 0; k < nk - 1; ++k) {
-    // all k-steps but the last, each with the next k-step's fragments read
-    // between its MFMAs; the first NDS also issue part of operand stage
-    // 2k + S - 1 into the slot freed at the previous barrier (the slot after
-    // stage k + 1's two)
-    const int dslot = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
-#pragma unroll
-    for (int s = 0; s < KS - 1; ++s) {
+  // On a diagonal tile of the symmetric products a wave whose whole part of
+  // the tile lies below the diagonal has nothing to compute: the stored
+  // result is the upper triangle and its mirror. It still issues its share
+  // of every stage's loads and meets every barrier (the same code with the
+  // fragment reads and matrix-core work left out), so the workgroup runs the
+  // same sequence of loads, waits and barriers; the matrix cores do 2 of 8
+  // waves' work less on those tiles (1 of 4 with 128-tiles), which the
+  // power-limited clock gets back.
+  auto kloop = [&](auto idle_c) {
+    constexpr bool IDLE = decltype(idle_c)::value;
+    auto rf = [&](int pslot, int qslot, int st, int buf) {
+      if constexpr (!IDLE) read_frags(pslot, qslot, st, buf);
+    };
+    auto mf = [&](int buf) {
+      if constexpr (!IDLE) mfmas(buf);
+    };
+    auto sp = [&](int nmem, int nloads) {
+      if constexpr (!IDLE) spread(nmem, nloads);
+    };
+    rf(0, 1, 0, 0);
+    // slots of stage k (ps, qs) and of stage k+1 (pn, qn)
+    int ps = 0, qs = 1, pn = 2 % S, qn = 3 % S;
+    constexpr int NDS = KS - 1 < 2 ? KS - 1 : 2;   // k-steps that carry the deferred refill
+    for (int k = 0; k < nk - 1; ++k) {
+      // all k-steps but the last, each with the next k-step's fragments read
+      // between its MFMAs; the first NDS also issue part of operand stage
+      // 2k + S - 1 into the slot freed at the previous barrier (the slot after
+      // stage k + 1's two)
+      const int dslot = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
+  #pragma unroll
+      for (int s = 0; s < KS - 1; ++s) {
+        if constexpr (kEven) {
+          // k-step 0: second half of operand stage 2k + S - 2 (slot qn), at
+          // wave priority 1 (like the raise over the last k-step: a wave
+          // still issuing this stage's loads outranks its SIMD partner; 1.8 %
+          // on the 3.8B set, priority 2 here 0.7 %); k-steps 1, 2: operand
+          // stage 2k + S - 1 in halves (slot dslot)
+          if (s == 0) {
+            __builtin_amdgcn_s_setprio(1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (s == 0) issue(qn, 2 * k + S - 2, LPO / 2, LPO);
+          else issue(dslot, 2 * k + S - 1, (s - 1) * LPO / 2, s * LPO / 2);
+          rf(ps, qs, s + 1, (s + 1) & 1);
+          mf(s & 1);
+          sp(kReadStep + LPO / 2, LPO / 2);
+          if (s == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+          }
+        } else if (s < NDS) {
+          issue(dslot, 2 * k + S - 1, s * LPO / NDS, (s + 1) * LPO / NDS);
+          rf(ps, qs, s + 1, (s + 1) & 1);
+          mf(s & 1);
+          sp(kReadStep + LPO / NDS, LPO / NDS);
+        } else {
+          rf(ps, qs, s + 1, (s + 1) & 1);
+          mf(s & 1);
+          sp(kReadStep, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // stage k+1 has landed for every wave (only the deferred operand stage,
+      // the S - 4 most recent, may be in flight); stage k's slots are free
+      wait_lgkm0();
+      wait_vm<(S - 4) * LPO>();
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // the last k-step: the refill of one freed slot with operand stage 2k+S,
+      // then the next stage's first fragments.
+      // With 256-tiles it runs at raised wave priority: a wave still in it
+      // outranks the waves of its SIMD that have moved on to the next stage, so
+      // the waves reach the next barrier closer together (1-1.2 % faster on the
+      // 3072-row products). 128-tiles, two workgroups per CU, keep the default.
+      if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(2);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (kEven) {
-        // k-step 0: second half of operand stage 2k + S - 2 (slot qn), at
-        // wave priority 1 (like the raise over the last k-step: a wave
-        // still issuing this stage's loads outranks its SIMD partner; 1.8 %
-        // on the 3.8B set, priority 2 here 0.7 %); k-steps 1, 2: operand
-        // stage 2k + S - 1 in halves (slot dslot)
-        if (s == 0) {
-          __builtin_amdgcn_s_setprio(1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (s == 0) issue(qn, 2 * k + S - 2, LPO / 2, LPO);
-        else issue(dslot, 2 * k + S - 1, (s - 1) * LPO / 2, s * LPO / 2);
-        read_frags(ps, qs, s + 1, (s + 1) & 1);
-        mfmas(s & 1);
-        spread(kReadStep + LPO / 2, LPO / 2);
-        if (s == 0) {
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_setprio(0);
-        }
-      } else if (s < NDS) {
-        issue(dslot, 2 * k + S - 1, s * LPO / NDS, (s + 1) * LPO / NDS);
-        read_frags(ps, qs, s + 1, (s + 1) & 1);
-        mfmas(s & 1);
-        spread(kReadStep + LPO / NDS, LPO / NDS);
+        issue(ps, 2 * k + S, 0, LPO / 2);
+        rf(pn, qn, 0, 0);
+        mf(1);
+        sp(LPO / 2 + kReadStep, LPO / 2);
       } else {
-        read_frags(ps, qs, s + 1, (s + 1) & 1);
-        mfmas(s & 1);
-        spread(kReadStep, 0);
+        issue(ps, 2 * k + S, 0, LPO);
+        rf(pn, qn, 0, 0);
+        mf(1);
+        sp(LPO + kReadStep, LPO);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      ps = pn; qs = qn;
+      pn = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
+      qn = (qn + 2 >= S) ? qn + 2 - S : qn + 2;
     }
-    // stage k+1 has landed for every wave (only the deferred operand stage,
-    // the S - 4 most recent, may be in flight); stage k's slots are free
-    wait_lgkm0();
-    wait_vm<(S - 4) * LPO>();
-    ring_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // the last k-step: the refill of one freed slot with operand stage 2k+S,
-    // then the next stage's first fragments.
-    // With 256-tiles it runs at raised wave priority: a wave still in it
-    // outranks the waves of its SIMD that have moved on to the next stage, so
-    // the waves reach the next barrier closer together (1-1.2 % faster on the
-    // 3072-row products). 128-tiles, two workgroups per CU, keep the default.
-    if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(2);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kEven) {
-      issue(ps, 2 * k + S, 0, LPO / 2);
-      read_frags(pn, qn, 0, 0);
-      mfmas(1);
-      spread(LPO / 2 + kReadStep, LPO / 2);
-    } else {
-      issue(ps, 2 * k + S, 0, LPO);
-      read_frags(pn, qn, 0, 0);
-      mfmas(1);
-      spread(LPO + kReadStep, LPO);
+  #pragma unroll
+    for (int s = 0; s < KS - 1; ++s) {
+      rf(ps, qs, s + 1, (s + 1) & 1);
+      mf(s & 1);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (TILE == 256) __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-    ps = pn; qs = qn;
-    pn = (pn + 2 >= S) ? pn + 2 - S : pn + 2;
-    qn = (qn + 2 >= S) ? qn + 2 - S : qn + 2;
+    mf(1);   // KS is even: the last k-step's fragments are in buffer 1
+  };
+  if constexpr (mode == GM_BX) {
+    kloop(std::false_type{});
+  } else {
+    const bool idle = it.tm == it.tn && wm * MI * 32 >= (wn + 1) * NI * 32;
+    if (idle) kloop(std::true_type{});
+    else kloop(std::false_type{});
   }
-#pragma unroll
-  for (int s = 0; s < KS - 1; ++s) {
-    read_frags(ps, qs, s + 1, (s + 1) & 1);
-    mfmas(s & 1);
-  }
-  mfmas(1);   // KS is even: the last k-step's fragments are in buffer 1
   wait_vm<0>();
   // Keep every MFMA above this point and give the last ones time to write
   // their accumulators before the epilogue reads them through inline asm
@@ -639,12 +666,13 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
       for (int e = 0; e < 8; ++e) vv[e] = j + e < M.cols ? ((const GAS float*)M.pv)[j + e] : 0.f;
     }
   };
-  // A GM_SYM result is symmetric only in exact arithmetic (C[m][n] and C[n][m]
-  // come from different products), so its diagonal tiles keep the upper
-  // triangle and write the lower one as its mirror: the stored matrix is then
-  // the mirrored upper triangle whatever the tile size, as for off-diagonal
-  // tiles.
-  const bool diag_sym = mode == GM_SYM && it.tm == it.tn;
+  // A symmetric product's result (Gram, B', or a GM_SYM product, which is
+  // symmetric only in exact arithmetic: C[m][n] and C[n][m] come from
+  // different products) keeps the upper triangle of its diagonal tiles and
+  // writes the lower one as its mirror: the stored matrix is the mirrored
+  // upper triangle whatever the tile size, as for off-diagonal tiles, and the
+  // waves wholly below the diagonal (idle above) store nothing.
+  const bool diag_sym = mode != GM_BX && it.tm == it.tn;
   if (diag_sym) write_t = true;
   // the second product's first slab of A values, requested before the
   // barrier (the waves that finish their K loop first wait there)
