@@ -660,9 +660,11 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
             } else {
               const double K = li == LIST_GRAM ? m.L_pad : m.s_pad;
               G.algorithmic += li == LIST_GRAM ? s * s * L : s * s * s;   // the upper half of a symmetric result
-              // upper tiles, less the quarter of each diagonal tile whose
-              // waves lie wholly below the diagonal and skip their work
-              G.executed += 2.0 * (ts * (ts + 1) / 2.0 - ts / 4.0) * tile * (double)tile * K;
+              // upper tiles; on the diagonal ones bf16 and fp8 operands
+              // leave out the 32 x 32 blocks wholly below the diagonal (28 of
+              // 64 on a 256-tile, 6 of 16 on a 128-tile, in every layout)
+              const double diag_skip = t == DT_F32 ? 0.0 : (tile == 256 ? 28.0 / 64 : 6.0 / 16);
+              G.executed += 2.0 * (ts * (ts + 1) / 2.0 - ts * diag_skip) * tile * (double)tile * K;
             }
           }
           add_gemm(meta, G, items);

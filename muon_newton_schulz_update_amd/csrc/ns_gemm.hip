@@ -225,6 +225,30 @@ template <> struct Elem<float> {
 };
 
 
+// The 32x32 blocks of a wave's part of a tile that the wave computes. OFF
+// is, on a diagonal tile of a symmetric product, the wave's row origin less
+// its column origin in 32-row blocks (-1 elsewhere): block (mi, ni) lies
+// wholly below the diagonal, and is left out, when ni < mi + OFF. Rows and
+// columns with no block left need no fragments.
+template <int OFF, int MI, int NI>
+struct Keep {
+  static constexpr bool blk(int mi, int ni) { return !(OFF >= 0 && ni < mi + OFF); }
+  static constexpr bool row(int mi) { return !(OFF >= 0 && mi + OFF >= NI); }
+  static constexpr bool col(int ni) { return !(OFF >= 0 && ni < OFF); }
+  static constexpr int blocks() {
+    int n = 0;
+    for (int mi = 0; mi < MI; ++mi)
+      for (int ni = 0; ni < NI; ++ni) n += blk(mi, ni) ? 1 : 0;
+    return n;
+  }
+  static constexpr int frags() {
+    int n = 0;
+    for (int mi = 0; mi < MI; ++mi) n += row(mi) ? 1 : 0;
+    for (int ni = 0; ni < NI; ++ni) n += col(ni) ? 1 : 0;
+    return n;
+  }
+};
+
 }  // namespace
 
 // Launch geometry: grid.x = 8 * per_xcd blocks; the hardware deals
@@ -251,7 +275,6 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   // k-steps per stage: 16 bf16, 4 fp32 (four 32x32x2 MFMAs) or 64 fp8 of K per
   // lane pair, so a 128-byte stage row is 4, 4 or 2 k-steps
   constexpr int KS = kF8 ? 2 : 4;
-  constexpr int kMfmaStep = MI * NI * (sizeof(T) == 4 ? 4 : 1);   // MFMAs per k-step
   constexpr int kReadStep = (MI + NI) * (kF8 ? 2 : 1);            // LDS reads per k-step
   static_assert(!kF8 || mode == GM_GRAM, "fp8 operands are for the Gram");
   // S operand slots; after the K loop the same memory stages the epilogue
@@ -367,7 +390,8 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
   typedef typename Elem<T>::Frag Frag;
   Frag fa[2][MI], fb[2][NI];
   const int lr = lane & 31;
-  auto read_frags = [&](int pslot, int qslot, int s, int buf) {
+  auto read_frags = [&](int pslot, int qslot, int s, int buf, auto off_c) {
+    using K = Keep<decltype(off_c)::value, MI, NI>;
     const uint8_t* sa = smem + pslot * kOpBytes;
     const uint8_t* sb = same ? sa : smem + qslot * kOpBytes;
     if constexpr (kF8) {
@@ -379,34 +403,39 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
                          (int)hi[3]};
       };
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) fa[buf][mi] = frag(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes);
+      for (int mi = 0; mi < MI; ++mi)
+        if (K::row(mi)) fa[buf][mi] = frag(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) fb[buf][ni] = frag(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes);
+      for (int ni = 0; ni < NI; ++ni)
+        if (K::col(ni)) fb[buf][ni] = frag(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes);
     } else {
       const int ph = ((2 * s + (lane >> 5)) ^ ((lr >> 1) & 7)) * 16;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        fa[buf][mi] = *(const Frag*)(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes + ph);
+        if (K::row(mi)) fa[buf][mi] = *(const Frag*)(sa + (wm * MI * 32 + mi * 32 + lr) * kRowBytes + ph);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        fb[buf][ni] = *(const Frag*)(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
+        if (K::col(ni)) fb[buf][ni] = *(const Frag*)(sb + (wn * NI * 32 + ni * 32 + lr) * kRowBytes + ph);
     }
   };
-  auto mfmas = [&](int buf) {
+  auto mfmas = [&](int buf, auto off_c) {
+    using K = Keep<decltype(off_c)::value, MI, NI>;
     if constexpr (kF8) {
       // e4m3 operands (format 0), unit block scales (E8M0 127 = 1.0)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[buf][mi], fb[buf][ni], acc[mi][ni], 0, 0,
-                                                                        0, 127, 0, 127);
+          if (K::blk(mi, ni))
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[buf][mi], fb[buf][ni], acc[mi][ni], 0,
+                                                                          0, 0, 127, 0, 127);
     } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][mi], fb[buf][ni], acc[mi][ni], 0, 0, 0);
+          if (K::blk(mi, ni))
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][mi], fb[buf][ni], acc[mi][ni], 0, 0, 0);
     } else {
       // the 4 floats of a chunk are 4 consecutive k; lanes 0-31 and 32-63
       // supply the two k slots of each 32x32x2 step
@@ -416,19 +445,26 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][mi][e], fb[buf][ni][e], acc[mi][ni], 0, 0, 0);
+            if (K::blk(mi, ni))
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][mi][e], fb[buf][ni][e], acc[mi][ni], 0, 0,
+                                                                 0);
     }
   };
   // Spread nmem memory instructions evenly between one k-step's MFMAs, the
   // first nloads of them direct loads, the rest LDS reads. The compiler
   // cannot tell the refill and the reads apart, so the pattern keeps their
   // program order.
-  auto spread = [&](int nmem, int nloads) {
+  // nmem counts a whole wave part's kReadStep LDS reads; a wave leaving
+  // blocks out (Keep) has fewer MFMAs and reads.
+  auto spread = [&](int nmem, int nloads, auto off_c) {
+    using K = Keep<decltype(off_c)::value, MI, NI>;
+    constexpr int nmf = K::blocks() * (sizeof(T) == 4 ? 4 : 1);
+    nmem += K::frags() * (kF8 ? 2 : 1) - kReadStep;
 #pragma unroll
-    for (int q = 0; q < kMfmaStep; ++q) {
+    for (int q = 0; q < nmf; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
 #pragma unroll
-      for (int t = q * nmem / kMfmaStep; t < (q + 1) * nmem / kMfmaStep; ++t) {
+      for (int t = q * nmem / nmf; t < (q + 1) * nmem / nmf; ++t) {
         if (t < nloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct load
         else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // one LDS read
       }
@@ -470,24 +506,26 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     wait_vm<(S - 3) * LPO>();
   }
   ring_barrier();
-  // On a diagonal tile of the symmetric products a wave whose whole part of
-  // the tile lies below the diagonal has nothing to compute: the stored
-  // result is the upper triangle and its mirror. It still issues its share
-  // of every stage's loads and meets every barrier (the same code with the
-  // fragment reads and matrix-core work left out), so the workgroup runs the
-  // same sequence of loads, waits and barriers; the matrix cores do 2 of 8
-  // waves' work less on those tiles (1 of 4 with 128-tiles), which the
-  // power-limited clock gets back.
-  auto kloop = [&](auto idle_c) {
-    constexpr bool IDLE = decltype(idle_c)::value;
+  // On a diagonal tile of the symmetric products the 32x32 blocks wholly
+  // below the diagonal need no work: the stored result is the upper triangle
+  // and its mirror. Each wave runs the K loop compiled for its offset from
+  // the diagonal (Keep), without those blocks' matrix-core work and without
+  // the fragments no kept block reads (a wave wholly below the diagonal does
+  // none); every wave still issues its share of every stage's loads and
+  // meets every barrier, so the workgroup runs the same sequence of loads,
+  // waits and barriers. The matrix cores do 28 of 64 blocks' work less on
+  // those tiles (8 waves of 64 x 128), which the power-limited clock gets
+  // back.
+  auto kloop = [&](auto off_c) {
+    constexpr bool kAny = Keep<decltype(off_c)::value, MI, NI>::blocks() > 0;
     auto rf = [&](int pslot, int qslot, int st, int buf) {
-      if constexpr (!IDLE) read_frags(pslot, qslot, st, buf);
+      if constexpr (kAny) read_frags(pslot, qslot, st, buf, off_c);
     };
     auto mf = [&](int buf) {
-      if constexpr (!IDLE) mfmas(buf);
+      if constexpr (kAny) mfmas(buf, off_c);
     };
     auto sp = [&](int nmem, int nloads) {
-      if constexpr (!IDLE) spread(nmem, nloads);
+      if constexpr (kAny) spread(nmem, nloads, off_c);
     };
     rf(0, 1, 0, 0);
     // slots of stage k (ps, qs) and of stage k+1 (pn, qn)
@@ -571,12 +609,20 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     }
     mf(1);   // KS is even: the last k-step's fragments are in buffer 1
   };
-  if constexpr (mode == GM_BX) {
-    kloop(std::false_type{});
+  using Off = std::integral_constant<int, -1>;
+  if constexpr (mode == GM_BX || sizeof(T) == 4) {
+    // (fp32 operands compute whole tiles: the reduced forms spill registers
+    // in their second product)
+    kloop(Off{});
   } else {
-    const bool idle = it.tm == it.tn && wm * MI * 32 >= (wn + 1) * NI * 32;
-    if (idle) kloop(std::true_type{});
-    else kloop(std::false_type{});
+    // the wave's offset from the diagonal in 32-row blocks; the layouts here
+    // give -NI.., 0, 2 (8 waves of 64 x 128) and NI or more (wholly below)
+    const int off = it.tm == it.tn ? wm * MI - wn * NI : -1;
+    if (off < 0) kloop(Off{});
+    else if (off >= NI) kloop(std::integral_constant<int, NI>{});
+    else if (off == 0) kloop(std::integral_constant<int, 0>{});
+    else if (off == 2) kloop(std::integral_constant<int, 2>{});
+    else kloop(Off{});   // not reached by the layouts above: full work, still correct
   }
   wait_vm<0>();
   // Keep every MFMA above this point and give the last ones time to write
