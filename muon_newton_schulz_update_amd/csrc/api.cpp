@@ -42,6 +42,7 @@ hipError_t launch_ns_gemm(int ns_t, const DevMat* mats, const TileItem* items, i
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu, int nesterov,
                                  int sgd, hipStream_t st);
 hipError_t launch_check_finite(DevMat* m, LaunchList L, int nblk, int upd, hipStream_t st);
+hipError_t launch_wnorm(const DevMat* m, LaunchList L, int nblk, hipStream_t st);
 hipError_t launch_norms_lines(DevMat* m, LaunchList L, int nblk, float pp_eps, hipStream_t st);
 hipError_t launch_norms_scalars(DevMat* m, LaunchList L, int nblk, float ns_eps, int init_power, hipStream_t st);
 hipError_t launch_prologue(int ns_t, const DevMat* m, LaunchList L, int nblk, int use_xn, hipStream_t st);
@@ -144,9 +145,9 @@ int rect_block(const muon_config& cfg, bool* forced) {
 
 // Fused tail: the matrices of a muon_update call with the bf16 NS type take
 // the tail's sums in the epilogue of their final X' = Q X (||U||^2, <U, X>
-// and the parts of sigma = ||X v||) and in the momentum pass (||W||^2), so
-// the tail reads U, X and W once, in its single pass, and the power
-// iteration ends without its last X v. fp32 matrices keep the tail's
+// and the parts of sigma = ||X v||) and in a read-only pass over W
+// (||W||^2), so the tail reads U, X and W once, in its single pass, and the
+// power iteration ends without its last X v. fp32 matrices keep the tail's
 // reduction pass and the last X v (the fp32 engine's epilogue stages fp32
 // slabs). MUON_FUSED_TAIL=0 (read when a plan is built) turns it off.
 inline bool fused_tail(int kind, int ns_t) {
@@ -212,6 +213,7 @@ struct Plan {
   // lists
   HostList stream, permat, lines, colblk, matvec, ascale;
   HostList stream_r;                      // the tail's reduction pass: streaming tiles of the matrices without the fused tail
+  HostList stream_f;                      // the weight-norm pass: streaming tiles of the fused-tail matrices
   HostList frows;                         // fused tail: sigma's row sums, one block per 256 rows
   HostList fused[2];                      // power rounds: fused X^T X v pass, one list per NS type
   HostList matvec_w, rmatvec_w;           // X v + X^T u for matrices wider than kFusedCols
@@ -513,14 +515,15 @@ std::unique_ptr<Plan> build_plan(int kind, int pp, bool wide_rows, bool fp8, int
   }
   add_list(meta, P->stream, all, blocks);
   {
-    std::vector<int> ms, bl, fm, fb;
+    std::vector<int> ms, bl, fm, fb, ft;
     for (int i = 0; i < nm; ++i) {
       const MatInfo& m = P->mats[i];
       if (!m.ft) { ms.push_back(i); bl.push_back(m.n_rt * m.n_seg); }
-      else { fm.push_back(i); fb.push_back(cdiv(m.rows, 256)); }
+      else { fm.push_back(i); fb.push_back(cdiv(m.rows, 256)); ft.push_back(m.n_rt * m.n_seg); }
     }
     add_list(meta, P->stream_r, ms, bl);
     add_list(meta, P->frows, fm, fb);
+    add_list(meta, P->stream_f, fm, ft);
   }
   for (int i = 0; i < nm; ++i) blocks[i] = 1;
   add_list(meta, P->permat, all, blocks);
@@ -1031,7 +1034,7 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
 
   // algorithmic byte counts for the profile
   double el_mv = 0, el_all = 0, el_fused[2] = {0, 0}, el_wide = 0;
-  double b_mom = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_dup[2] = {0, 0}, b_dfin = 0;
+  double b_mom = 0, b_wn = 0, b_tail_r = 0, b_tail_a = 0, b_pro[2][2] = {{0, 0}, {0, 0}}, b_dup[2] = {0, 0}, b_dfin = 0;
   for (size_t i = 0; i < P->mats.size(); ++i) {
     const MatInfo& m = P->mats[i];
     const double el = (double)m.rows * m.cols;
@@ -1039,7 +1042,8 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     el_all += el;
     if (!m.ft) el_mv += el * esz(m.ns_t);
     (fused_power(m) ? el_fused[m.ns_t] : el_wide) += el * esz(m.ns_t);
-    b_mom += upd ? el * (esz(d.dt_g) + 8 + esz(m.ns_t) + (d.ftw ? esz(d.dt_w) : 0)) : el * esz(d.dt_g);
+    b_mom += upd ? el * (esz(d.dt_g) + 8 + esz(m.ns_t)) : el * esz(d.dt_g);
+    if (d.ftw) b_wn += el * esz(d.dt_w);
     if (!m.ft) b_tail_r += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? esz(d.dt_w) : 0));
     else if (contra) b_tail_r += el * 4.0 / 64;   // sigma's row parts
     b_tail_a += el * (esz(m.ns_t) * (contra ? 2 : 1) + (d.w ? 2 * esz(d.dt_w) : 0) + (d.uo ? esz(d.dt_uo) : 0));
@@ -1079,6 +1083,10 @@ muon_status run(muon_handle* h, const Call& c, bool use_static = false) {
     ProfScope ps(h, 1, b_mom);
     CHECK_LAUNCH(h, launch_momentum_stats(D, dev_list(meta, P->stream), P->stream.nblk, upd ? 1 : 0, cfg.mu,
                                           cfg.nesterov, (cfg.flags & MUON_FLAG_SGD_MOMENTUM) ? 1 : 0, st));
+  }
+  if (upd && c.w && P->stream_f.nblk) {
+    ProfScope ps(h, 1, b_wn);
+    CHECK_LAUNCH(h, launch_wnorm(D, dev_list(meta, P->stream_f), P->stream_f.nblk, st));
   }
   {
     ProfScope ps(h, 1, 0);
@@ -1288,7 +1296,7 @@ std::string check_plan(const Plan& P) {
       {&P.matvec_w, "matvec_w"}, {&P.rmatvec_w, "rmatvec_w"}, {&P.prologue[0][0], "prologue"},
       {&P.prologue[0][1], "prologue"}, {&P.prologue[1][0], "prologue"}, {&P.prologue[1][1], "prologue"},
       {&P.dupdate[0], "dupdate"}, {&P.dupdate[1], "dupdate"}, {&P.dfinish, "dfinish"},
-      {&P.stream_r, "stream_r"}, {&P.frows, "frows"}};
+      {&P.stream_r, "stream_r"}, {&P.frows, "frows"}, {&P.stream_f, "stream_f"}};
   for (const auto& l : lists) {
     std::string e = list_ok(*l.first, l.second);
     if (!e.empty()) return e;

@@ -136,14 +136,14 @@ struct DevMat {
   int32_t* ist;     // IS_COUNT
   // Fused tail (muon_update, bf16 NS type; null otherwise): the epilogue of
   // the matrix's final X' = Q X takes the tail's sums from the values it
-  // stores, and the momentum pass takes ||W||^2, so no kernel reads U, X
-  // and W before the tail's single pass.
+  // stores, and a read-only pass takes ||W||^2, so no kernel reads U and X
+  // before the tail's single pass.
   float* ftail;     // cdiv(rows,64) x cdiv(cols,64) x 2: per 64 x 64 block of the storage frame, ||U||^2 and
                     // <U, X> (X the stored blended update)
   float* frow;      // cdiv(cols,64) x rows: per storage row and 64-column block, the block's part of
                     // (X / ||X||_F) v, v the last power-iteration vector (sigma = ||X v||)
-  float* fwp;       // n_rt x n_seg: ||W||^2 per streaming tile, from the momentum pass (tailpart is
-                    // taken by the D update in between)
+  float* fwp;       // n_rt x n_seg: ||W||^2 per streaming tile, from k_wnorm (tailpart is taken by
+                    // the D update in between)
   int32_t x0n;      // a tall bf16 matrix of muon_update with rows and cols multiples of kTile: X0^T is
                     // scale D o X row by row, so the pass prologue writes only X0 and each pass's first
                     // X' = Q X reads xn (ld = cols = s_pad) and applies scale D_l to output column l
@@ -151,7 +151,7 @@ struct DevMat {
                     // cols multiples of kTile: X0 = scale X, so the pass prologue writes only X0^T and the
                     // pass's first Gram reads xn (ld = cols = L_pad) and scales A by scale^2
   int32_t ftx;      // per call: the epilogue also takes <U, X> and the sigma parts (contra != 0)
-  int32_t ftw;      // per call: the momentum pass takes ||W||^2 (a weight is given)
+  int32_t ftw;      // per call: k_wnorm takes ||W||^2 (a weight is given)
 };
 
 // One output tile of a Newton-Schulz product.

@@ -23,7 +23,6 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
-#include <type_traits>
 
 #include "muon_device.hpp"
 
@@ -224,16 +223,11 @@ __device__ __forceinline__ float strided_sum(const float* p, size_t stride, int 
 // tile's columns) and, for wide matrices, colpart[tile_row][c] (column sums
 // over the tile's rows, the four waves combined in LDS).
 // ---------------------------------------------------------------------------
-// TW (not void): a fused-tail matrix with a weight; the pass also reads W and
-// writes the tile's ||W||^2 to fwp[local] (the tail then reads U, X and W
-// only once, in its single pass).
-template <typename TG, typename TX, bool NP, typename TW = void>
+template <typename TG, typename TX, bool NP>
 __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float mu, int nesterov, int sgd,
-                                              float* cp, float* wred) {
+                                              float* cp) {
   typedef Ty<TG> G;
   typedef Ty<float> F;
-  constexpr bool kW = !std::is_void<TW>::value;
-  typedef std::conditional_t<kW, TW, float> TWx;
   constexpr int R = kWaveRows;
   const int tr = local / M.n_seg, sg = local % M.n_seg;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -243,10 +237,8 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
   const int dg = sizeof(TG) == 2 ? DT_BF16 : DT_F32, dx = sizeof(TX) == 2 ? DT_BF16 : DT_F32;
   const int nv = max(0, min(8, M.cols - c));
   const bool fast = nr == R && nv == 8 && aligned16(M.g, M.ld_g, dg) &&
-                    (!NP || (aligned16(M.m, M.ld_m, DT_F32) && aligned16(M.xn, M.cols, dx))) &&
-                    (!kW || aligned16(M.w, M.ld_w, sizeof(TWx) == 2 ? DT_BF16 : DT_F32));
+                    (!NP || (aligned16(M.m, M.ld_m, DT_F32) && aligned16(M.xn, M.cols, dx)));
   float col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float sw = 0.f;   // this lane's part of the tile's ||W||^2 (kW)
   float rsl[R];   // this lane's part of each row's sum of squares
   // one row: the update (stored through vector or element-wise stores), then
   // this lane's sums of squares; a row's floats die before the next row is
@@ -276,24 +268,18 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
     rsl[k] = rs;
   };
   if (fast) {
-    // fp32 grads load in two batches of R/2 rows, and so do bf16 ones with
-    // a weight (fp32 weights in four of R/4): the kernel's register budget
-    // is set by its largest body
-    constexpr int RB = !kW ? (sizeof(TG) == 2 ? R : R / 2) : (sizeof(TWx) == 2 ? R / 2 : R / 4);
+    // fp32 grads load in two batches of R/2 rows: the kernel's register
+    // budget is set by its largest body
+    constexpr int RB = sizeof(TG) == 2 ? R : R / 2;
 #pragma unroll
     for (int k0 = 0; k0 < R; k0 += RB) {
       typename G::Raw qg[RB];
       typename F::Raw qm[RB];
-      typename Ty<TWx>::Raw qw[kW ? RB : 1];
 #pragma unroll
       for (int k = 0; k < RB; ++k) qg[k] = G::ld(M.g, (size_t)(r + k0 + k) * M.ld_g + c);
       if (NP) {
 #pragma unroll
         for (int k = 0; k < RB; ++k) qm[k] = F::ld(M.m, (size_t)(r + k0 + k) * M.ld_m + c);
-      }
-      if constexpr (kW) {
-#pragma unroll
-        for (int k = 0; k < RB; ++k) qw[k] = Ty<TW>::ld(M.w, (size_t)(r + k0 + k) * M.ld_w + c);
       }
 #pragma unroll
       for (int k = 0; k < RB; ++k) {
@@ -301,12 +287,6 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
         G::cvt(qg[k], x);
         if (NP) F::cvt(qm[k], m);
         row(k0 + k, x, m, true);
-        if constexpr (kW) {
-          float wv[8];
-          Ty<TW>::cvt(qw[k], wv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sw += wv[e] * wv[e];
-        }
       }
     }
   } else {
@@ -317,20 +297,7 @@ __device__ __forceinline__ void momentum_body(const DevMat& M, int local, float 
       ld_part<TG>(M.g, (size_t)(r + k) * M.ld_g + c, n, x);
       if (NP) ld_part<float>(M.m, (size_t)(r + k) * M.ld_m + c, n, m);
       row(k, x, m, false);
-      if constexpr (kW) {
-        float wv[8];
-        ld_part<TW>(M.w, (size_t)(r + k) * M.ld_w + c, n, wv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sw += wv[e] * wv[e];
-      }
     }
-  }
-  if constexpr (kW) {
-    // the four waves' sums in order (block-uniform: every wave gets here)
-    sw = wave_sum(sw);
-    if (lane == 0) wred[w] = sw;
-    __syncthreads();
-    if (threadIdx.x == 0) gst<float>(M.fwp + local, wred[0] + wred[1] + wred[2] + wred[3]);
   }
 #pragma unroll
   for (int k = 0; k < R; ++k) {
@@ -354,24 +321,64 @@ __global__ __launch_bounds__(256) void k_momentum_stats(const DevMat* __restrict
                                                         int nesterov_pass, float mu, int nesterov, int sgd) {
   static_assert(kStreamRows == 4 * kWaveRows, "four waves per streaming tile");
   __shared__ float cp[4 * kSegCols];
-  __shared__ float wred[4];
   int local;
   const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
-  // the grad's type is the NS type (plans are keyed by it); fused-tail
-  // matrices are bf16
+  // the grad's type is the NS type (plans are keyed by it)
   if (M.dt_g == DT_BF16) {
-    if (nesterov_pass && M.ftw) {
-      if (M.dt_w == DT_BF16) momentum_body<__bf16, __bf16, true, __bf16>(M, local, mu, nesterov, sgd, cp, wred);
-      else momentum_body<__bf16, __bf16, true, float>(M, local, mu, nesterov, sgd, cp, wred);
-    } else if (nesterov_pass) {
-      momentum_body<__bf16, __bf16, true>(M, local, mu, nesterov, sgd, cp, wred);
-    } else {
-      momentum_body<__bf16, __bf16, false>(M, local, mu, nesterov, sgd, cp, wred);
+    if (nesterov_pass) momentum_body<__bf16, __bf16, true>(M, local, mu, nesterov, sgd, cp);
+    else momentum_body<__bf16, __bf16, false>(M, local, mu, nesterov, sgd, cp);
+  } else {
+    if (nesterov_pass) momentum_body<float, float, true>(M, local, mu, nesterov, sgd, cp);
+    else momentum_body<float, float, false>(M, local, mu, nesterov, sgd, cp);
+  }
+}
+
+// Fused tail: ||W||^2 per streaming tile of a matrix with a weight (fwp),
+// read once before the tail (its single pass needs the norm first). A
+// lane sums its 8 columns of its wave's 8 rows, loaded in one batch; the
+// four waves' sums are added in order.
+template <typename TW>
+__device__ __forceinline__ void wnorm_body(const DevMat& M, int local, float* red) {
+  constexpr int R = kWaveRows;
+  const int tr = local / M.n_seg, sg = local % M.n_seg;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = sg * kSegCols + lane * 8;
+  const int r = tr * kStreamRows + w * R;
+  const int nr = max(0, min(R, M.rows - r));
+  const int nv = max(0, min(8, M.cols - c));
+  float sw = 0.f;
+  if (nr == R && nv == 8 && aligned16(M.w, M.ld_w, sizeof(TW) == 2 ? DT_BF16 : DT_F32)) {
+    typename Ty<TW>::Raw q[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) q[k] = Ty<TW>::ld(M.w, (size_t)(r + k) * M.ld_w + c);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      float v[8];
+      Ty<TW>::cvt(q[k], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sw += v[e] * v[e];
     }
   } else {
-    if (nesterov_pass) momentum_body<float, float, true>(M, local, mu, nesterov, sgd, cp, wred);
-    else momentum_body<float, float, false>(M, local, mu, nesterov, sgd, cp, wred);
+    for (int k = 0; k < nr; ++k) {
+      float v[8];
+      ld_part<TW>(M.w, (size_t)(r + k) * M.ld_w + c, nv, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sw += v[e] * v[e];
+    }
   }
+  sw = wave_sum(sw);
+  if (lane == 0) red[w] = sw;
+  __syncthreads();
+  if (threadIdx.x == 0) gst<float>(M.fwp + local, red[0] + red[1] + red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void k_wnorm(const DevMat* __restrict__ mats, LaunchList L) {
+  __shared__ float red[4];
+  int local;
+  const DevMat& M = mats[find_job(L, blockIdx.x, &local)];
+  if (!M.ftw) return;   // no weight in this call (uniform over the block)
+  if (M.dt_w == DT_BF16) wnorm_body<__bf16>(M, local, red);
+  else wnorm_body<float>(M, local, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -1453,6 +1460,10 @@ __global__ __launch_bounds__(256) void k_tail_apply(const DevMat* __restrict__ m
 hipError_t launch_momentum_stats(const DevMat* m, LaunchList L, int nblk, int nesterov_pass, float mu,
                                  int nesterov, int sgd, hipStream_t st) {
   LAUNCH(k_momentum_stats, nblk, m, L, nesterov_pass, mu, nesterov, sgd);
+  return hipGetLastError();
+}
+hipError_t launch_wnorm(const DevMat* m, LaunchList L, int nblk, hipStream_t st) {
+  LAUNCH(k_wnorm, nblk, m, L);
   return hipGetLastError();
 }
 hipError_t launch_check_finite(DevMat* m, LaunchList L, int nblk, int upd, hipStream_t st) {
