@@ -8,15 +8,18 @@
 //
 // Sequence of one muon_update (Aurora record page, www.xxmr.cn/news/295280,
 // section 组合优化栈 and the pseudocode in Aurora 的迭代伪代码):
-//   momentum + Nesterov + row partial norms -> norm lines (row and column
-//   norms, rho, D0) -> per-matrix scalars (||X||, prologue scale)
+//   momentum + Nesterov + row partial norms [-> ||W||^2, fused tail]
+//   -> norm lines (row and column norms, rho, D0) -> per-matrix scalars
+//      (||X||, prologue scale)
 //   -> power iteration (power_steps + 1 rounds of w = X^T X v, one read of X
 //      in a fused pass, or X v then X^T u for matrices wider than
-//      kFusedCols; ||w||, v = w/||w||; then X v and sigma)
-//   -> for each Aurora pass: prologue (scale * D o T, both orientations),
-//      ns_steps x {A = XX^T, B' = bA + cA^2 + aI, X = B'X}, D update between
-//      passes
-//   -> tail reduce -> tail finalise (Contra, Frobenius restore, aspect, floor)
+//      kFusedCols; ||w||, v = w/||w||; then X v and sigma, except for the
+//      fused tail, whose final product takes X v)
+//   -> for each Aurora pass: prologue (scale * D o T, one or both
+//      orientations), ns_steps in blocks of iterations {A = XX^T, B' = bA +
+//      cA^2 + aI, ..., X' = Q X}, D update between passes
+//   -> tail reduce (or, fused tail, the final product's sums and sigma's row
+//      sums) -> tail finalise (Contra, Frobenius restore, aspect, floor)
 //   -> tail apply (update_out, W -= lr V).
 #include <hip/hip_runtime.h>
 #include <dlfcn.h>

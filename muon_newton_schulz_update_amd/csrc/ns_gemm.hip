@@ -42,6 +42,11 @@
 // at once held waves in load issue while their step had little matrix work.
 // LDS rows are XOR-swizzled in 16-byte chunks so fragment reads are
 // conflict-free.
+// On a symmetric product's diagonal tile each wave leaves out the 32x32
+// blocks wholly below the diagonal (the stored result is the upper triangle
+// and its mirror). The final X' = Q X of a muon_update matrix with the bf16
+// type also takes the tail's sums (||U||^2, <U, X>, the rows' parts of X v)
+// from the values it stores.
 // bf16 runs v_mfma_f32_32x32x16_bf16 (fp32 accumulation); fp32 runs
 // v_mfma_f32_32x32x2f32 on the same tiles; the optional fp8 first Gram runs
 // v_mfma_scale_f32_32x32x64_f8f6f4 on an e4m3 copy of X0 stored in panels of
