@@ -173,16 +173,19 @@ typedef struct {
   int64_t gemm_launches;      /* Newton-Schulz matrix-core launches */
   double  gemm_ms;            /* event time of those launches */
   double  gemm_counted_flop;  /* 4 s^2 L + 2 s^3 per iteration per matrix (s <= L) */
-  double  gemm_executed_flop; /* flops the tiles actually issue (symmetric tiles skipped; on diagonal tiles the waves wholly below the diagonal issue none) */
+  double  gemm_executed_flop; /* flops the tiles actually issue (symmetric results' lower tiles
+                                 skipped, and on their diagonal tiles the 32x32 blocks wholly
+                                 below the diagonal) */
   double  gemm_algorithmic_flop; /* flops the products need: the upper half of each symmetric
                                     result, no padding (3 s^2 L + (4 r - 3) s^3 per block of r
                                     iterations) */
   int64_t stream_launches;    /* bandwidth-bound launches of the step itself: momentum and
-                                 norms, power iteration, tail (and the latency kernels between) */
+                                 norms, the weight norm, power iteration, tail (and the latency
+                                 kernels between) */
   double  stream_ms;
   double  stream_bytes;       /* algorithmic HBM bytes of those launches */
   int64_t aux_launches;       /* Aurora vector kernels feeding the products: the pass prologue
-                                 (X0 = scale D o T in both orientations) and the D update */
+                                 (X0 = scale D o T in one or both orientations) and the D update */
   double  aux_ms;
   double  aux_bytes;          /* HBM bytes of those launches (source read, iterate pair written;
                                  D update: one read of U) */
@@ -252,8 +255,9 @@ const char* muon_version(void);
  *                          muon_update take the tail's norms in a reduction
  *                          pass over U, X and W (and the operator-norm
  *                          estimate in its own X v launch) instead of in the
- *                          final Newton-Schulz product's epilogue and the
- *                          momentum pass (the same sums in another order).
+ *                          final Newton-Schulz product's epilogue and a
+ *                          read-only pass over W (the same sums in another
+ *                          order).
  *   MUON_TALL_X0=0         read when a plan is built: bf16 matrices of
  *                          muon_update with both sides multiples of 256 get
  *                          both orientations of the pass's first iterate
