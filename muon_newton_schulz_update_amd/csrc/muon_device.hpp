@@ -154,6 +154,42 @@ struct DevMat {
   int32_t ftw;      // per call: k_wnorm takes ||W||^2 (a weight is given)
 };
 
+// Diagonal tiles of the symmetric products (GM_GRAM, GM_SQ, GM_SYM): the
+// stored result is the upper triangle and its mirror, so the 32x32 blocks
+// wholly below the diagonal need no work. Keep<OFF, MI, NI> names the blocks
+// a wave of MI x NI blocks computes, OFF being its row origin less its column
+// origin in 32-row blocks (kDiagFull: every block): block (mi, ni) is left
+// out when ni < mi + OFF. Rows and columns with no block left need no
+// fragments. Plain constexpr code, shared by the engine and a host test.
+constexpr int kDiagFull = -1;
+template <int OFF, int MI, int NI>
+struct Keep {
+  static constexpr bool blk(int mi, int ni) { return !(OFF >= 0 && ni < mi + OFF); }
+  static constexpr bool row(int mi) { return !(OFF >= 0 && mi + OFF >= NI); }
+  static constexpr bool col(int ni) { return !(OFF >= 0 && ni < OFF); }
+  static constexpr int blocks() {
+    int n = 0;
+    for (int mi = 0; mi < MI; ++mi)
+      for (int ni = 0; ni < NI; ++ni) n += blk(mi, ni) ? 1 : 0;
+    return n;
+  }
+  static constexpr int frags() {
+    int n = 0;
+    for (int mi = 0; mi < MI; ++mi) n += row(mi) ? 1 : 0;
+    for (int ni = 0; ni < NI; ++ni) n += col(ni) ? 1 : 0;
+    return n;
+  }
+};
+// The K-loop form a wave (wm, wn) of a diagonal tile runs: its offset from
+// the diagonal where that form is compiled (0 and 2, or NI for a wave wholly
+// below it), kDiagFull otherwise (full work is always correct). The engine's
+// layouts (8 waves of 2 x 4 blocks, 4 of 4 x 4, 4 of 2 x 2) meet offsets
+// below 0, 0, 2 and NI or more.
+constexpr int diag_form(int wm, int wn, int MI, int NI) {
+  const int off = wm * MI - wn * NI;
+  return off < 0 ? kDiagFull : off >= NI ? NI : (off == 0 || off == 2) ? off : kDiagFull;
+}
+
 // One output tile of a Newton-Schulz product.
 struct TileItem {
   uint16_t mat;   // index into the launch's DevMat array

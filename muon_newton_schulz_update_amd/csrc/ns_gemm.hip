@@ -230,30 +230,6 @@ template <> struct Elem<float> {
 };
 
 
-// The 32x32 blocks of a wave's part of a tile that the wave computes. OFF
-// is, on a diagonal tile of a symmetric product, the wave's row origin less
-// its column origin in 32-row blocks (-1 elsewhere): block (mi, ni) lies
-// wholly below the diagonal, and is left out, when ni < mi + OFF. Rows and
-// columns with no block left need no fragments.
-template <int OFF, int MI, int NI>
-struct Keep {
-  static constexpr bool blk(int mi, int ni) { return !(OFF >= 0 && ni < mi + OFF); }
-  static constexpr bool row(int mi) { return !(OFF >= 0 && mi + OFF >= NI); }
-  static constexpr bool col(int ni) { return !(OFF >= 0 && ni < OFF); }
-  static constexpr int blocks() {
-    int n = 0;
-    for (int mi = 0; mi < MI; ++mi)
-      for (int ni = 0; ni < NI; ++ni) n += blk(mi, ni) ? 1 : 0;
-    return n;
-  }
-  static constexpr int frags() {
-    int n = 0;
-    for (int mi = 0; mi < MI; ++mi) n += row(mi) ? 1 : 0;
-    for (int ni = 0; ni < NI; ++ni) n += col(ni) ? 1 : 0;
-    return n;
-  }
-};
-
 }  // namespace
 
 // Launch geometry: grid.x = 8 * per_xcd blocks; the hardware deals
@@ -614,20 +590,18 @@ __global__ __launch_bounds__(WM * WN * 64, TILE == 256 ? 1 : 2) void k_ns_gemm(c
     }
     mf(1);   // KS is even: the last k-step's fragments are in buffer 1
   };
-  using Off = std::integral_constant<int, -1>;
+  using Off = std::integral_constant<int, kDiagFull>;
   if constexpr (mode == GM_BX || sizeof(T) == 4) {
     // (fp32 operands compute whole tiles: the reduced forms spill registers
     // in their second product)
     kloop(Off{});
   } else {
-    // the wave's offset from the diagonal in 32-row blocks; the layouts here
-    // give -NI.., 0, 2 (8 waves of 64 x 128) and NI or more (wholly below)
-    const int off = it.tm == it.tn ? wm * MI - wn * NI : -1;
-    if (off < 0) kloop(Off{});
-    else if (off >= NI) kloop(std::integral_constant<int, NI>{});
-    else if (off == 0) kloop(std::integral_constant<int, 0>{});
-    else if (off == 2) kloop(std::integral_constant<int, 2>{});
-    else kloop(Off{});   // not reached by the layouts above: full work, still correct
+    // the form compiled for the wave's offset from the diagonal (diag_form)
+    const int form = it.tm == it.tn ? diag_form(wm, wn, MI, NI) : kDiagFull;
+    if (form == NI) kloop(std::integral_constant<int, NI>{});
+    else if (form == 0) kloop(std::integral_constant<int, 0>{});
+    else if (form == 2) kloop(std::integral_constant<int, 2>{});
+    else kloop(Off{});
   }
   wait_vm<0>();
   // Keep every MFMA above this point and give the last ones time to write
